@@ -1,0 +1,279 @@
+"""ctypes binding of libmuonadamw.so (include/muon_adamw.h).
+
+Argument marshalling only: tensors are checked for device, dtype and layout, their
+device pointers and the current HIP stream are handed to the C ABI, and a negative
+status is raised as MuonAdamWError with the library's own message.  Every step of
+the optimizer runs in the library's HIP kernels; there is no fallback path.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from dataclasses import dataclass
+from typing import Optional, Sequence
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libmuonadamw.so")
+
+MA_OK = 0
+MA_ERR_INVALID_ARG = -1
+MA_ERR_UNSUPPORTED = -2
+MA_ERR_WORKSPACE = -3
+MA_ERR_HIP = -4
+MA_MAX_NS_STEPS = 64
+
+EXPORTED = (
+    "ma_abi_version", "ma_status_string", "ma_last_error", "ma_muon_route_of",
+    "ma_muon_workspace_bytes", "ma_muon_step", "ma_adamw_step",
+    "ma_newton_schulz_workspace_bytes", "ma_newton_schulz",
+)
+
+
+class MuonAdamWError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(f"[{status}] {message}")
+        self.status = status
+
+
+class _MuonBucket(ctypes.Structure):
+    _fields_ = [("K", ctypes.c_int64), ("A", ctypes.c_int64), ("B", ctypes.c_int64),
+                ("param", ctypes.c_void_p), ("grad", ctypes.c_void_p),
+                ("momentum", ctypes.c_void_p)]
+
+
+class _MuonHParams(ctypes.Structure):
+    _fields_ = [("lr", ctypes.c_float), ("momentum", ctypes.c_float),
+                ("weight_decay", ctypes.c_float), ("ns_eps", ctypes.c_float),
+                ("nesterov", ctypes.c_int32), ("cautious_wd", ctypes.c_int32),
+                ("ns_steps", ctypes.c_int32), ("scale_mode", ctypes.c_int32),
+                ("ns_coeffs", ctypes.POINTER(ctypes.c_float))]
+
+
+class _MuonRoute(ctypes.Structure):
+    _fields_ = [("transposed", ctypes.c_int32), ("m", ctypes.c_int32), ("n", ctypes.c_int32),
+                ("ns_steps_run", ctypes.c_int32), ("m_pad", ctypes.c_int32),
+                ("n_pad", ctypes.c_int32)]
+
+
+class _AdamWHParams(ctypes.Structure):
+    _fields_ = [("lr", ctypes.c_float), ("beta1", ctypes.c_float), ("beta2", ctypes.c_float),
+                ("eps", ctypes.c_float), ("weight_decay", ctypes.c_float),
+                ("step", ctypes.c_int64), ("decoupled", ctypes.c_int32),
+                ("cautious_wd", ctypes.c_int32)]
+
+
+@dataclass(frozen=True)
+class Route:
+    """Routing report of one bucket (see ma_muon_route)."""
+
+    transposed: bool
+    m: int
+    n: int
+    ns_steps_run: int
+    m_pad: int
+    n_pad: int
+
+
+_lib: Optional[ctypes.CDLL] = None
+
+
+def load(path: str = LIB_PATH) -> ctypes.CDLL:
+    """Load the HIP library; raise if it has not been built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise RuntimeError(
+            f"libmuonadamw.so not found at {path}: build it first "
+            "(python -c 'import __graft_entry__ as g; g.build()')")
+    lib = ctypes.CDLL(path)
+    lib.ma_abi_version.restype = ctypes.c_int
+    lib.ma_status_string.restype = ctypes.c_char_p
+    lib.ma_status_string.argtypes = [ctypes.c_int]
+    lib.ma_last_error.restype = ctypes.c_char_p
+    lib.ma_muon_route_of.restype = ctypes.c_int
+    lib.ma_muon_route_of.argtypes = [ctypes.c_int64, ctypes.c_int64, ctypes.POINTER(_MuonHParams),
+                                     ctypes.POINTER(_MuonRoute)]
+    lib.ma_muon_workspace_bytes.restype = ctypes.c_size_t
+    lib.ma_muon_workspace_bytes.argtypes = [ctypes.POINTER(_MuonBucket), ctypes.c_int32,
+                                            ctypes.POINTER(_MuonHParams)]
+    lib.ma_muon_step.restype = ctypes.c_int
+    lib.ma_muon_step.argtypes = [ctypes.POINTER(_MuonBucket), ctypes.c_int32,
+                                 ctypes.POINTER(_MuonHParams), ctypes.c_void_p, ctypes.c_size_t,
+                                 ctypes.c_void_p, ctypes.POINTER(_MuonRoute)]
+    lib.ma_adamw_step.restype = ctypes.c_int
+    lib.ma_adamw_step.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+                                  ctypes.c_void_p, ctypes.c_int64,
+                                  ctypes.POINTER(_AdamWHParams), ctypes.c_void_p]
+    lib.ma_newton_schulz_workspace_bytes.restype = ctypes.c_size_t
+    lib.ma_newton_schulz_workspace_bytes.argtypes = [ctypes.c_int64] * 3
+    lib.ma_newton_schulz.restype = ctypes.c_int
+    lib.ma_newton_schulz.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64,
+                                     ctypes.c_int64, ctypes.c_int64,
+                                     ctypes.POINTER(_MuonHParams), ctypes.c_void_p,
+                                     ctypes.c_size_t, ctypes.c_void_p]
+    _lib = lib
+    return lib
+
+
+def _check(status: int) -> None:
+    if status != MA_OK:
+        lib = load()
+        raise MuonAdamWError(status, lib.ma_last_error().decode() or
+                             lib.ma_status_string(status).decode())
+
+
+def abi_version() -> int:
+    return load().ma_abi_version()
+
+
+# --------------------------------------------------------------------------
+# marshalling helpers
+# --------------------------------------------------------------------------
+def _ptr(t) -> int:
+    return t.data_ptr() if t is not None else 0
+
+
+def _require_f32_cuda(name: str, t) -> None:
+    import torch
+
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must live on the GPU (got {t.device})")
+    if t.dtype != torch.float32:
+        raise ValueError(f"{name} must be float32 (got {t.dtype})")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def _stream_handle(stream, device) -> int:
+    import torch
+
+    if stream is None:
+        stream = torch.cuda.current_stream(device)
+    return int(stream.cuda_stream)
+
+
+def _muon_hparams(lr, momentum, weight_decay, nesterov, ns_steps, ns_coeffs, ns_eps,
+                  cautious_wd, scale_mode):
+    hp = _MuonHParams(lr=lr, momentum=momentum, weight_decay=weight_decay, ns_eps=ns_eps,
+                      nesterov=int(bool(nesterov)), cautious_wd=int(bool(cautious_wd)),
+                      ns_steps=int(ns_steps), scale_mode=int(scale_mode))
+    keep = None
+    if ns_coeffs is not None:
+        flat = [float(x) for row in ns_coeffs for x in (row if hasattr(row, "__len__") else [row])]
+        if len(flat) == 3 and ns_steps != 1:
+            flat = flat * int(ns_steps)  # one triple for every iteration
+        if len(flat) != 3 * int(ns_steps):
+            raise ValueError("ns_coeffs must be one (a, b, c) triple or ns_steps of them")
+        keep = (ctypes.c_float * len(flat))(*flat)
+        hp.ns_coeffs = ctypes.cast(keep, ctypes.POINTER(ctypes.c_float))
+    return hp, keep
+
+
+def _as_stack(t):
+    """(K, A, B) view of a 3-D stack or a single 2-D matrix."""
+    if t.dim() == 3:
+        return t
+    if t.dim() == 2:
+        return t.unsqueeze(0)
+    raise ValueError("Muon parameters are 2-D matrices or 3-D (K, A, B) stacks")
+
+
+# --------------------------------------------------------------------------
+# entry points (names of the C ABI without the ma_ prefix)
+# --------------------------------------------------------------------------
+def muon_route_of(A: int, B: int, ns_steps: int = 5) -> Route:
+    hp = _MuonHParams(ns_steps=int(ns_steps))
+    out = _MuonRoute()
+    _check(load().ma_muon_route_of(int(A), int(B), ctypes.byref(hp), ctypes.byref(out)))
+    return Route(bool(out.transposed), out.m, out.n, out.ns_steps_run, out.m_pad, out.n_pad)
+
+
+def _bucket_array(buckets):
+    arr = (_MuonBucket * max(len(buckets), 1))()
+    for i, (p, g, m) in enumerate(buckets):
+        K, A, B = p.shape
+        arr[i] = _MuonBucket(K, A, B, _ptr(p), _ptr(g), _ptr(m))
+    return arr
+
+
+def muon_workspace_bytes(shapes: Sequence[Sequence[int]]) -> int:
+    """Workspace bytes for buckets of these (K, A, B) shapes."""
+    arr = (_MuonBucket * max(len(shapes), 1))()
+    for i, (K, A, B) in enumerate(shapes):
+        arr[i] = _MuonBucket(int(K), int(A), int(B), 0, 0, 0)
+    return int(load().ma_muon_workspace_bytes(arr, len(shapes), None))
+
+
+def muon_step(buckets, *, lr: float, momentum: float = 0.95, weight_decay: float = 0.0,
+              nesterov: bool = True, ns_steps: int = 5, ns_coeffs=None, ns_eps: float = 1e-7,
+              cautious_wd: bool = False, scale_mode: int = 0, workspace=None, stream=None):
+    """One Muon step (ma_muon_step) on (param, grad, momentum) triples of (K, A, B) or
+    (A, B) fp32 GPU tensors.  Returns the routing report of each bucket."""
+    import torch
+
+    stacks = []
+    for i, (p, g, m) in enumerate(buckets):
+        for name, t in (("param", p), ("grad", g), ("momentum", m)):
+            _require_f32_cuda(f"bucket {i} {name}", t)
+        p3, g3, m3 = _as_stack(p), _as_stack(g), _as_stack(m)
+        if not (p3.shape == g3.shape == m3.shape):
+            raise ValueError(f"bucket {i}: param, grad and momentum shapes differ")
+        stacks.append((p3, g3, m3))
+    lib = load()
+    arr = _bucket_array(stacks)
+    hp, _keep = _muon_hparams(lr, momentum, weight_decay, nesterov, ns_steps, ns_coeffs, ns_eps,
+                              cautious_wd, scale_mode)
+    need = int(lib.ma_muon_workspace_bytes(arr, len(stacks), ctypes.byref(hp)))
+    device = stacks[0][0].device if stacks else None
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=device)
+    routes = (_MuonRoute * max(len(stacks), 1))()
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    _check(lib.ma_muon_step(arr, len(stacks), ctypes.byref(hp), _ptr(workspace), ws_bytes,
+                            _stream_handle(stream, device) if device is not None else 0, routes))
+    return [Route(bool(r.transposed), r.m, r.n, r.ns_steps_run, r.m_pad, r.n_pad)
+            for r in routes[:len(stacks)]]
+
+
+def adamw_step(param, grad, exp_avg, exp_avg_sq, *, step: int, lr: float, beta1: float = 0.9,
+               beta2: float = 0.999, eps: float = 1e-8, weight_decay: float = 0.0,
+               decoupled: bool = True, cautious_wd: bool = False, stream=None) -> None:
+    """One AdamW step (ma_adamw_step) over contiguous fp32 GPU tensors of equal size."""
+    for name, t in (("param", param), ("grad", grad), ("exp_avg", exp_avg),
+                    ("exp_avg_sq", exp_avg_sq)):
+        _require_f32_cuda(name, t)
+    n = param.numel()
+    if not (grad.numel() == exp_avg.numel() == exp_avg_sq.numel() == n):
+        raise ValueError("param, grad, exp_avg and exp_avg_sq differ in size")
+    hp = _AdamWHParams(lr=lr, beta1=beta1, beta2=beta2, eps=eps, weight_decay=weight_decay,
+                       step=int(step), decoupled=int(bool(decoupled)),
+                       cautious_wd=int(bool(cautious_wd)))
+    _check(load().ma_adamw_step(_ptr(param), _ptr(grad), _ptr(exp_avg), _ptr(exp_avg_sq), n,
+                                ctypes.byref(hp), _stream_handle(stream, param.device)))
+
+
+def newton_schulz_workspace_bytes(K: int, A: int, B: int) -> int:
+    return int(load().ma_newton_schulz_workspace_bytes(int(K), int(A), int(B)))
+
+
+def newton_schulz(inp, out, *, ns_steps: int = 5, ns_coeffs=None, ns_eps: float = 1e-7,
+                  workspace=None, stream=None) -> None:
+    """The orthogonalisation alone (ma_newton_schulz): out = NS(inp), (K, A, B) or (A, B)."""
+    import torch
+
+    _require_f32_cuda("inp", inp)
+    _require_f32_cuda("out", out)
+    i3, o3 = _as_stack(inp), _as_stack(out)
+    if i3.shape != o3.shape:
+        raise ValueError("inp and out shapes differ")
+    K, A, B = i3.shape
+    hp, _keep = _muon_hparams(0.0, 0.0, 0.0, True, ns_steps, ns_coeffs, ns_eps, False, 0)
+    need = newton_schulz_workspace_bytes(K, A, B)
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=inp.device)
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    _check(load().ma_newton_schulz(_ptr(i3), _ptr(o3), K, A, B, ctypes.byref(hp), _ptr(workspace),
+                                   ws_bytes, _stream_handle(stream, inp.device)))

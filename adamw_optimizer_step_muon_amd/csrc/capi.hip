@@ -1,0 +1,380 @@
+// Exported C ABI (include/muon_adamw.h): argument checks, routing, workspace layout
+// and the launch sequence of one optimizer step.  Host code only; the arithmetic is
+// in the kernels of adamw.hip, muon_elementwise.hip and ns_gemm.hip.
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <string>
+
+#include "muon_adamw.h"
+#include "ma_internal.h"
+
+namespace ma {
+namespace {
+
+thread_local std::string g_last_error;
+
+ma_status fail(ma_status st, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return st;
+}
+
+ma_status hip_fail(hipError_t e, const char* what) {
+  return fail(MA_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+int64_t round_up(int64_t x, int64_t q) { return (x + q - 1) / q * q; }
+size_t align256(size_t x) { return (x + 255) & ~static_cast<size_t>(255); }
+
+// The quintic of the newton_schulz listing ("Optimizers: AdamW, Muon and the
+// distributed optimizer", section "Muon: orthogonalising the update").
+constexpr NsCoeffs kQuintic{3.4445f, -4.7750f, 2.0315f};
+
+bool finite(float x) { return std::isfinite(x); }
+
+struct Range {
+  uintptr_t lo, hi;
+};
+bool overlap(Range a, Range b) { return a.lo < b.hi && b.lo < a.hi; }
+Range range_of(const void* p, int64_t bytes) {
+  const uintptr_t lo = reinterpret_cast<uintptr_t>(p);
+  return Range{lo, lo + static_cast<uintptr_t>(bytes)};
+}
+
+// Largest sizes the kernels' index arithmetic is written for.
+constexpr int64_t kMaxSide = int64_t(1) << 20;   // m_pad, n_pad
+constexpr int64_t kMaxBlocks = (int64_t(1) << 31) - 1;
+
+ma_status check_hparams(const ma_muon_hparams* hp) {
+  if (!hp) return fail(MA_ERR_INVALID_ARG, "hparams is NULL");
+  if (!finite(hp->lr) || !finite(hp->momentum) || !finite(hp->weight_decay) ||
+      !finite(hp->ns_eps))
+    return fail(MA_ERR_INVALID_ARG, "non-finite Muon hyperparameter");
+  if (hp->ns_steps < 0 || hp->ns_steps > MA_MAX_NS_STEPS)
+    return fail(MA_ERR_INVALID_ARG, "ns_steps %d outside [0, %d]", hp->ns_steps, MA_MAX_NS_STEPS);
+  if (hp->scale_mode != 0 && hp->scale_mode != 1)
+    return fail(MA_ERR_INVALID_ARG, "scale_mode %d is not 0 or 1", hp->scale_mode);
+  if (hp->ns_coeffs) {
+    for (int i = 0; i < 3 * hp->ns_steps; ++i)
+      if (!finite(hp->ns_coeffs[i])) return fail(MA_ERR_INVALID_ARG, "non-finite ns_coeffs[%d]", i);
+  }
+  return MA_OK;
+}
+
+NsCoeffs coeff_at(const ma_muon_hparams* hp, int it) {
+  if (!hp->ns_coeffs) return kQuintic;
+  return NsCoeffs{hp->ns_coeffs[3 * it], hp->ns_coeffs[3 * it + 1], hp->ns_coeffs[3 * it + 2]};
+}
+
+ma_status check_shape(int64_t K, int64_t A, int64_t B) {
+  if (K < 0) return fail(MA_ERR_INVALID_ARG, "K = %lld < 0", (long long)K);
+  if (K == 0) return MA_OK;
+  if (A < 1 || B < 1)
+    return fail(MA_ERR_INVALID_ARG, "matrix shape %lld x %lld", (long long)A, (long long)B);
+  const int64_t m = A < B ? A : B, n = A < B ? B : A;
+  if (round_up(m, kTile) > kMaxSide || round_up(n, kTile) > kMaxSide)
+    return fail(MA_ERR_UNSUPPORTED, "matrix side above %lld", (long long)kMaxSide);
+  // grid limits: (nblk, K) and (Bp/64, Ap/64, K) launches, K x tiles GEMM launches
+  const BucketPlan p = plan_bucket(K, A, B);
+  const int64_t tiles = (p.m_pad / kTile) * (p.n_pad / kTile);
+  if (K > 65535 || p.nblk > kMaxBlocks || K * tiles > kMaxBlocks ||
+      K * A * B / 4 / 256 > kMaxBlocks)
+    return fail(MA_ERR_UNSUPPORTED, "bucket (%lld, %lld, %lld) exceeds the launch grid",
+                (long long)K, (long long)A, (long long)B);
+  return MA_OK;
+}
+
+ma_muon_route route_of(const BucketPlan& p, int ns_steps) {
+  ma_muon_route r;
+  r.transposed = p.transposed ? 1 : 0;
+  r.m = static_cast<int32_t>(p.m);
+  r.n = static_cast<int32_t>(p.n);
+  r.ns_steps_run = ns_steps;
+  r.m_pad = static_cast<int32_t>(p.m_pad);
+  r.n_pad = static_cast<int32_t>(p.n_pad);
+  return r;
+}
+
+// Runs Newton-Schulz on the cast X0/XT0 of a bucket; returns the buffer that holds the
+// result in the matrix's own orientation (and its row stride).
+ma_status run_ns(const BucketPlan& p, const ma_muon_hparams* hp, char* ws, hipStream_t s,
+                 const unsigned short** out, int64_t* ldo) {
+  unsigned short* X[2] = {reinterpret_cast<unsigned short*>(ws + p.off_x[0]),
+                          reinterpret_cast<unsigned short*>(ws + p.off_x[1])};
+  unsigned short* XT[2] = {reinterpret_cast<unsigned short*>(ws + p.off_xt[0]),
+                           reinterpret_cast<unsigned short*>(ws + p.off_xt[1])};
+  unsigned short* R = reinterpret_cast<unsigned short*>(ws + p.off_r);
+  unsigned short* P = reinterpret_cast<unsigned short*>(ws + p.off_p);
+  int cur = 0;
+  for (int it = 0; it < hp->ns_steps; ++it) {
+    const NsCoeffs c = coeff_at(hp, it);
+    hipError_t e = launch_gram(p, X[cur], R, s);
+    if (e != hipSuccess) return hip_fail(e, "gram launch");
+    e = launch_poly(p, R, P, c.b, c.c, s);
+    if (e != hipSuccess) return hip_fail(e, "poly launch");
+    e = launch_combine(p, P, X[cur], XT[cur], c.a, X[cur ^ 1], XT[cur ^ 1], s);
+    if (e != hipSuccess) return hip_fail(e, "combine launch");
+    cur ^= 1;
+  }
+  // Own orientation: X (m_pad x n_pad) when not transposed, X^T (n_pad x m_pad) when it is.
+  *out = p.transposed ? XT[cur] : X[cur];
+  *ldo = p.transposed ? p.m_pad : p.n_pad;
+  return MA_OK;
+}
+
+}  // namespace
+
+BucketPlan plan_bucket(int64_t K, int64_t A, int64_t B) {
+  BucketPlan p{};
+  p.K = K;
+  p.A = A;
+  p.B = B;
+  p.transposed = A > B;
+  p.m = p.transposed ? B : A;
+  p.n = p.transposed ? A : B;
+  p.m_pad = round_up(p.m, kTile);
+  p.n_pad = round_up(p.n, kTile);
+  p.nblk = (A * B + kPrepChunk - 1) / kPrepChunk;
+  if (p.nblk < 1) p.nblk = 1;
+  const size_t xb = static_cast<size_t>(K * p.m_pad * p.n_pad) * 2;
+  const size_t rb = static_cast<size_t>(K * p.m_pad * p.m_pad) * 2;
+  size_t off = 0;
+  for (int i = 0; i < 2; ++i) {
+    p.off_x[i] = off;
+    off = align256(off + xb);
+    p.off_xt[i] = off;
+    off = align256(off + xb);
+  }
+  p.off_r = off;
+  off = align256(off + rb);
+  p.off_p = off;
+  off = align256(off + rb);
+  p.off_part = off;
+  off = align256(off + static_cast<size_t>(K * p.nblk) * 4);
+  p.off_inv = off;
+  off = align256(off + static_cast<size_t>(K) * 4);
+  p.bytes = off;
+  return p;
+}
+
+}  // namespace ma
+
+using namespace ma;
+
+extern "C" {
+
+int ma_abi_version(void) { return MA_ABI_VERSION; }
+
+const char* ma_status_string(int status) {
+  switch (status) {
+    case MA_OK: return "ok";
+    case MA_ERR_INVALID_ARG: return "invalid argument";
+    case MA_ERR_UNSUPPORTED: return "unsupported";
+    case MA_ERR_WORKSPACE: return "workspace missing or too small";
+    case MA_ERR_HIP: return "HIP error";
+    default: return "unknown status";
+  }
+}
+
+const char* ma_last_error(void) { return g_last_error.c_str(); }
+
+ma_status ma_muon_route_of(int64_t A, int64_t B, const ma_muon_hparams* hp, ma_muon_route* out) {
+  g_last_error.clear();
+  if (!out) return fail(MA_ERR_INVALID_ARG, "out is NULL");
+  if (A < 1 || B < 1) return fail(MA_ERR_INVALID_ARG, "matrix shape %lld x %lld", (long long)A, (long long)B);
+  const int steps = hp ? hp->ns_steps : 5;
+  if (steps < 0 || steps > MA_MAX_NS_STEPS) return fail(MA_ERR_INVALID_ARG, "ns_steps %d", steps);
+  *out = route_of(plan_bucket(1, A, B), steps);
+  return MA_OK;
+}
+
+size_t ma_muon_workspace_bytes(const ma_muon_bucket* buckets, int32_t n_buckets,
+                               const ma_muon_hparams* hp) {
+  (void)hp;
+  if (n_buckets <= 0 || !buckets) return 0;
+  size_t need = 0;
+  for (int32_t i = 0; i < n_buckets; ++i) {
+    const ma_muon_bucket& b = buckets[i];
+    if (b.K <= 0 || b.A < 1 || b.B < 1) continue;
+    const size_t bytes = plan_bucket(b.K, b.A, b.B).bytes;
+    if (bytes > need) need = bytes;
+  }
+  return need;
+}
+
+ma_status ma_muon_step(const ma_muon_bucket* buckets, int32_t n_buckets,
+                       const ma_muon_hparams* hp, void* workspace, size_t workspace_bytes,
+                       void* stream, ma_muon_route* route_out) {
+  g_last_error.clear();
+  ma_status st = check_hparams(hp);
+  if (st != MA_OK) return st;
+  if (n_buckets < 0) return fail(MA_ERR_INVALID_ARG, "n_buckets %d < 0", n_buckets);
+  if (n_buckets > 0 && !buckets) return fail(MA_ERR_INVALID_ARG, "buckets is NULL");
+  for (int32_t i = 0; i < n_buckets; ++i) {
+    const ma_muon_bucket& b = buckets[i];
+    st = check_shape(b.K, b.A, b.B);
+    if (st != MA_OK) return fail(st, "bucket %d: %s", i, g_last_error.c_str());
+    if (b.K == 0) continue;
+    if (!b.param || !b.grad || !b.momentum)
+      return fail(MA_ERR_INVALID_ARG, "bucket %d: NULL param, grad or momentum", i);
+    if ((reinterpret_cast<uintptr_t>(b.param) | reinterpret_cast<uintptr_t>(b.grad) |
+         reinterpret_cast<uintptr_t>(b.momentum)) & 3u)
+      return fail(MA_ERR_INVALID_ARG, "bucket %d: pointers must be 4-byte aligned", i);
+    const int64_t bytes = b.K * b.A * b.B * 4;
+    const Range rp = range_of(b.param, bytes), rg = range_of(b.grad, bytes),
+                rm = range_of(b.momentum, bytes);
+    if (overlap(rp, rg) || overlap(rp, rm) || overlap(rg, rm))
+      return fail(MA_ERR_INVALID_ARG, "bucket %d: param, grad and momentum overlap", i);
+    // Across buckets: what one bucket writes (param, momentum) must not overlap
+    // anything another bucket touches; gradients are read only and may alias.
+    for (int32_t j = 0; j < i; ++j) {
+      const ma_muon_bucket& o = buckets[j];
+      if (o.K == 0) continue;
+      const int64_t ob = o.K * o.A * o.B * 4;
+      const Range op = range_of(o.param, ob), og = range_of(o.grad, ob),
+                  om = range_of(o.momentum, ob);
+      if (overlap(rp, op) || overlap(rp, og) || overlap(rp, om) || overlap(rm, op) ||
+          overlap(rm, og) || overlap(rm, om) || overlap(rg, op) || overlap(rg, om))
+        return fail(MA_ERR_INVALID_ARG, "buckets %d and %d overlap", j, i);
+    }
+  }
+  const size_t need = ma_muon_workspace_bytes(buckets, n_buckets, hp);
+  if (need > 0) {
+    if (!workspace) return fail(MA_ERR_WORKSPACE, "workspace is NULL, %zu bytes needed", need);
+    if (reinterpret_cast<uintptr_t>(workspace) & 255u)
+      return fail(MA_ERR_WORKSPACE, "workspace must be 256-byte aligned");
+    if (workspace_bytes < need)
+      return fail(MA_ERR_WORKSPACE, "workspace has %zu bytes, %zu needed", workspace_bytes, need);
+  }
+  if (route_out) {
+    for (int32_t i = 0; i < n_buckets; ++i) {
+      const ma_muon_bucket& b = buckets[i];
+      route_out[i] = b.K > 0 ? route_of(plan_bucket(b.K, b.A, b.B), hp->ns_steps)
+                             : ma_muon_route{0, 0, 0, 0, 0, 0};
+    }
+  }
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  char* ws = static_cast<char*>(workspace);
+  for (int32_t i = 0; i < n_buckets; ++i) {
+    const ma_muon_bucket& b = buckets[i];
+    if (b.K == 0) continue;
+    const BucketPlan p = plan_bucket(b.K, b.A, b.B);
+    float* partials = reinterpret_cast<float*>(ws + p.off_part);
+    float* inv = reinterpret_cast<float*>(ws + p.off_inv);
+    unsigned short* S = reinterpret_cast<unsigned short*>(ws + (p.transposed ? p.off_xt[0] : p.off_x[0]));
+    unsigned short* T = reinterpret_cast<unsigned short*>(ws + (p.transposed ? p.off_x[0] : p.off_xt[0]));
+    hipError_t e = launch_muon_prep(p, b.grad, b.momentum, hp->momentum, hp->nesterov, partials, s);
+    if (e != hipSuccess) return hip_fail(e, "momentum launch");
+    e = launch_norm_finalize(p, partials, hp->ns_eps, inv, s);
+    if (e != hipSuccess) return hip_fail(e, "norm launch");
+    e = launch_norm_cast(p, b.grad, b.momentum, hp->momentum, hp->nesterov, inv, S, T, s);
+    if (e != hipSuccess) return hip_fail(e, "cast launch");
+    const unsigned short* O = nullptr;
+    int64_t ldo = 0;
+    st = run_ns(p, hp, ws, s, &O, &ldo);
+    if (st != MA_OK) return st;
+    const double big = static_cast<double>(b.A > b.B ? b.A : b.B);
+    const double scale = hp->scale_mode == 0
+                             ? 0.2 * std::sqrt(big)
+                             : std::sqrt(std::fmax(1.0, static_cast<double>(b.A) / static_cast<double>(b.B)));
+    e = launch_muon_apply(p, b.param, O, ldo, hp->lr, hp->weight_decay, static_cast<float>(scale),
+                          hp->cautious_wd, s);
+    if (e != hipSuccess) return hip_fail(e, "apply launch");
+  }
+  return MA_OK;
+}
+
+size_t ma_newton_schulz_workspace_bytes(int64_t K, int64_t A, int64_t B) {
+  if (K <= 0 || A < 1 || B < 1) return 0;
+  return plan_bucket(K, A, B).bytes;
+}
+
+ma_status ma_newton_schulz(const float* in, float* out, int64_t K, int64_t A, int64_t B,
+                           const ma_muon_hparams* hp, void* workspace, size_t workspace_bytes,
+                           void* stream) {
+  g_last_error.clear();
+  ma_status st = check_hparams(hp);
+  if (st != MA_OK) return st;
+  st = check_shape(K, A, B);
+  if (st != MA_OK) return st;
+  if (K == 0) return MA_OK;
+  if (!in || !out) return fail(MA_ERR_INVALID_ARG, "NULL in or out");
+  if ((reinterpret_cast<uintptr_t>(in) | reinterpret_cast<uintptr_t>(out)) & 3u)
+    return fail(MA_ERR_INVALID_ARG, "pointers must be 4-byte aligned");
+  const int64_t bytes = K * A * B * 4;
+  if (overlap(range_of(in, bytes), range_of(out, bytes)))
+    return fail(MA_ERR_INVALID_ARG, "in and out overlap");
+  const BucketPlan p = plan_bucket(K, A, B);
+  if (!workspace) return fail(MA_ERR_WORKSPACE, "workspace is NULL, %zu bytes needed", p.bytes);
+  if (reinterpret_cast<uintptr_t>(workspace) & 255u)
+    return fail(MA_ERR_WORKSPACE, "workspace must be 256-byte aligned");
+  if (workspace_bytes < p.bytes)
+    return fail(MA_ERR_WORKSPACE, "workspace has %zu bytes, %zu needed", workspace_bytes, p.bytes);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  char* ws = static_cast<char*>(workspace);
+  float* partials = reinterpret_cast<float*>(ws + p.off_part);
+  float* inv = reinterpret_cast<float*>(ws + p.off_inv);
+  unsigned short* S = reinterpret_cast<unsigned short*>(ws + (p.transposed ? p.off_xt[0] : p.off_x[0]));
+  unsigned short* T = reinterpret_cast<unsigned short*>(ws + (p.transposed ? p.off_x[0] : p.off_xt[0]));
+  hipError_t e = launch_muon_prep(p, in, nullptr, 0.0f, 0, partials, s);
+  if (e != hipSuccess) return hip_fail(e, "norm partials launch");
+  e = launch_norm_finalize(p, partials, hp->ns_eps, inv, s);
+  if (e != hipSuccess) return hip_fail(e, "norm launch");
+  e = launch_norm_cast(p, in, nullptr, 0.0f, 0, inv, S, T, s);
+  if (e != hipSuccess) return hip_fail(e, "cast launch");
+  const unsigned short* O = nullptr;
+  int64_t ldo = 0;
+  st = run_ns(p, hp, ws, s, &O, &ldo);
+  if (st != MA_OK) return st;
+  e = launch_ns_extract(p, out, O, ldo, s);
+  if (e != hipSuccess) return hip_fail(e, "extract launch");
+  return MA_OK;
+}
+
+ma_status ma_adamw_step(float* param, const float* grad, float* exp_avg, float* exp_avg_sq,
+                        int64_t n, const ma_adamw_hparams* hp, void* stream) {
+  g_last_error.clear();
+  if (!hp) return fail(MA_ERR_INVALID_ARG, "hparams is NULL");
+  if (n < 0) return fail(MA_ERR_INVALID_ARG, "n = %lld < 0", (long long)n);
+  if (hp->step < 1) return fail(MA_ERR_INVALID_ARG, "step %lld < 1", (long long)hp->step);
+  if (!finite(hp->lr) || !finite(hp->beta1) || !finite(hp->beta2) || !finite(hp->eps) ||
+      !finite(hp->weight_decay))
+    return fail(MA_ERR_INVALID_ARG, "non-finite AdamW hyperparameter");
+  if (!(hp->beta1 >= 0.0f && hp->beta1 < 1.0f && hp->beta2 >= 0.0f && hp->beta2 < 1.0f))
+    return fail(MA_ERR_INVALID_ARG, "betas must lie in [0, 1)");
+  if (n == 0) return MA_OK;
+  if (!param || !grad || !exp_avg || !exp_avg_sq)
+    return fail(MA_ERR_INVALID_ARG, "NULL param, grad, exp_avg or exp_avg_sq");
+  if ((reinterpret_cast<uintptr_t>(param) | reinterpret_cast<uintptr_t>(grad) |
+       reinterpret_cast<uintptr_t>(exp_avg) | reinterpret_cast<uintptr_t>(exp_avg_sq)) & 3u)
+    return fail(MA_ERR_INVALID_ARG, "pointers must be 4-byte aligned");
+  const Range r[4] = {range_of(param, n * 4), range_of(grad, n * 4), range_of(exp_avg, n * 4),
+                      range_of(exp_avg_sq, n * 4)};
+  for (int i = 0; i < 4; ++i)
+    for (int j = i + 1; j < 4; ++j)
+      if (overlap(r[i], r[j])) return fail(MA_ERR_INVALID_ARG, "param/grad/exp_avg/exp_avg_sq overlap");
+  AdamWConst c;
+  c.lr = hp->lr;
+  c.beta1 = hp->beta1;
+  c.beta2 = hp->beta2;
+  c.one_m_beta1 = static_cast<float>(1.0 - static_cast<double>(hp->beta1));
+  c.one_m_beta2 = static_cast<float>(1.0 - static_cast<double>(hp->beta2));
+  c.eps = hp->eps;
+  c.wd = hp->weight_decay;
+  const double t = static_cast<double>(hp->step);
+  c.inv_bc1 = static_cast<float>(1.0 / (1.0 - std::pow(static_cast<double>(hp->beta1), t)));
+  c.inv_bc2 = static_cast<float>(1.0 / (1.0 - std::pow(static_cast<double>(hp->beta2), t)));
+  c.decoupled = hp->decoupled ? 1 : 0;
+  c.cautious = hp->cautious_wd ? 1 : 0;
+  const hipError_t e = launch_adamw(param, grad, exp_avg, exp_avg_sq, n, c,
+                                    static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "adamw launch");
+  return MA_OK;
+}
+
+}  // extern "C"

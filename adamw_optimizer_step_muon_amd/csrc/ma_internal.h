@@ -1,0 +1,90 @@
+// Internal declarations shared by the library's translation units (not installed).
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <cstddef>
+#include <cstdint>
+
+namespace ma {
+
+// ---------------------------------------------------------------------------
+// Vector types for gfx950 (64-wide wavefronts, MFMA bf16 operands of 8 values)
+// ---------------------------------------------------------------------------
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+
+// fp32 -> bf16, round to nearest even (NaN stays NaN).
+__device__ __forceinline__ unsigned short f2bf(float f) {
+  return __builtin_bit_cast(unsigned short, static_cast<__bf16>(f));
+}
+__device__ __forceinline__ float bf2f(unsigned short h) {
+  return __builtin_bit_cast(float, static_cast<unsigned int>(h) << 16);
+}
+
+// ---------------------------------------------------------------------------
+// Workspace layout of one Muon bucket (bf16 buffers, tile-padded)
+// ---------------------------------------------------------------------------
+constexpr int kTile = 128;        // square GEMM macro-tile; m and n pad to this
+constexpr int kCastTile = 64;     // normalise/cast kernel tile
+constexpr int kPrepChunk = 16384; // elements per momentum/norm block
+
+struct BucketPlan {
+  int64_t K, A, B;
+  bool transposed;
+  int64_t m, n, m_pad, n_pad;
+  int64_t nblk;  // momentum/norm blocks per matrix
+  // byte offsets inside the workspace
+  size_t off_x[2], off_xt[2], off_r, off_p, off_part, off_inv, bytes;
+};
+
+BucketPlan plan_bucket(int64_t K, int64_t A, int64_t B);
+
+// ---------------------------------------------------------------------------
+// Kernel launchers (return hipSuccess or the launch error)
+// ---------------------------------------------------------------------------
+struct NsCoeffs {
+  float a, b, c;
+};
+
+// M <- mu M + G (when M != nullptr), U = G + mu M_new | M_new | G; per-block sum of U^2.
+hipError_t launch_muon_prep(const BucketPlan& p, const float* G, float* M, float mu,
+                            int nesterov, float* partials, hipStream_t s);
+// inv[k] = 1 / (sqrt(sum of partials of matrix k) + eps)
+hipError_t launch_norm_finalize(const BucketPlan& p, const float* partials, float eps,
+                                float* inv, hipStream_t s);
+// X0 = U * inv[k] in bf16: orientation copy S (Ap x Bp) and transposed copy T (Bp x Ap),
+// zero in the padding.
+hipError_t launch_norm_cast(const BucketPlan& p, const float* G, const float* M, float mu,
+                            int nesterov, const float* inv, unsigned short* S,
+                            unsigned short* T, hipStream_t s);
+// R = X X^T (lower-triangle tiles, mirrored)
+hipError_t launch_gram(const BucketPlan& p, const unsigned short* X, unsigned short* R,
+                       hipStream_t s);
+// P = b R + c R R^T (lower-triangle tiles, mirrored)
+hipError_t launch_poly(const BucketPlan& p, const unsigned short* R, unsigned short* P,
+                       float b, float c, hipStream_t s);
+// Xn = a X + P X, written row-major (Xn) and transposed (XTn)
+hipError_t launch_combine(const BucketPlan& p, const unsigned short* P,
+                          const unsigned short* X, const unsigned short* XT, float a,
+                          unsigned short* Xn, unsigned short* XTn, hipStream_t s);
+// param <- param - lr*wd*mask*param - lr*scale*O   (O bf16, row stride ldo)
+hipError_t launch_muon_apply(const BucketPlan& p, float* param, const unsigned short* O,
+                             int64_t ldo, float lr, float wd, float scale, int cautious,
+                             hipStream_t s);
+// out = O as fp32 in the (K, A, B) orientation
+hipError_t launch_ns_extract(const BucketPlan& p, float* out, const unsigned short* O,
+                             int64_t ldo, hipStream_t s);
+
+struct AdamWConst {
+  float lr, beta1, beta2, one_m_beta1, one_m_beta2, eps, wd, inv_bc1, inv_bc2;
+  int decoupled, cautious;
+};
+hipError_t launch_adamw(float* p, const float* g, float* m, float* v, int64_t n,
+                        const AdamWConst& c, hipStream_t s);
+
+}  // namespace ma

@@ -1,0 +1,233 @@
+"""Benchmark of one hybrid Muon + AdamW optimizer step on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload I]
+
+A step is the whole hot path over one batch of synthetic gradients already resident
+in HBM: ma_adamw_step over the flat AdamW buffer, then ma_muon_step over every shape
+bucket (momentum, normalisation, 5 Newton-Schulz iterations, update), all on one
+stream.  Printed: one JSON line with the step time (ms), the Newton-Schulz GEMM
+throughput against the bf16 MFMA peak and the AdamW bandwidth against HBM peak, each
+measured with HIP events on the launch stream, plus the fp64 CPU oracle timed on a
+bounded sample of the same workload.
+
+Default workload: index 1, the 12-layer GPT with hidden 768.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+MFMA_BF16_PEAK_TFLOPS = 2500.0   # MI355X dense bf16
+HBM_PEAK_GBS = 8000.0            # MI355X HBM3E
+ADAMW_BYTES_PER_ELEM = 28        # read p, g, m, v; write p, m, v (fp32)
+
+
+def ns_flops(wl, steps=None, symmetric=True):
+    """Algorithmic Newton-Schulz FLOP of one optimizer step: per matrix and iteration
+    3 m^2 n + m^3 with the symmetric Gram and R R^T on one triangle (dense: 4 m^2 n + 2 m^3)."""
+    total = 0
+    for b in wl.muon:
+        m, n = min(b.A, b.B), max(b.A, b.B)
+        per = (3 * m * m * n + m ** 3) if symmetric else (4 * m * m * n + 2 * m ** 3)
+        total += b.K * per * (wl.muon_hp.ns_steps if steps is None else steps)
+    return total
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=2)
+    ap.add_argument("--workload", type=int, default=1)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-budget-s", type=float, default=20.0)
+    return ap.parse_args()
+
+
+def cpu_baseline(wl, budget_s):
+    """The fp64 oracle as it stands on the host cores, on a bounded sample: one matrix
+    per Muon bucket for one step, and a slice of the AdamW buffer; scaled to one full
+    step (x K per bucket, x n / slice for AdamW)."""
+    import numpy as np
+
+    import oracle
+    from workloads import gen
+
+    try:
+        from threadpoolctl import threadpool_info
+
+        cores = max((i.get("num_threads", 1) for i in threadpool_info()), default=1)
+    except Exception:
+        cores = os.cpu_count() or 1
+    hp = wl.muon_hp
+    muon_s = 0.0
+    parts = []
+    for bi, b in enumerate(wl.muon):
+        p0 = gen.np_param(wl.seed, gen.muon_index(wl, bi, 0), (b.A, b.B))
+        g1 = gen.np_grad(wl.seed, 1, gen.muon_index(wl, bi, 0), (b.A, b.B), wl.muon_grad,
+                         gen.MUON_SIGMA)
+        t0 = time.perf_counter()
+        oracle.muon_step(p0, g1, np.zeros((b.A, b.B)), lr=hp.lr, mu=hp.momentum,
+                         weight_decay=hp.weight_decay, cautious_wd=hp.cautious_wd)
+        dt = time.perf_counter() - t0
+        muon_s += dt * b.K
+        parts.append(f"1 of {b.K} {b.A}x{b.B}")
+        if dt * len(wl.muon) > budget_s:
+            break
+    n = wl.adamw_numel
+    n_s = min(n, 4_000_000)
+    rng = np.random.default_rng(0)
+    p = rng.standard_normal(n_s).astype(np.float32)
+    g = (1e-3 * rng.standard_normal(n_s)).astype(np.float32)
+    ah = wl.adamw_hp
+    t0 = time.perf_counter()
+    oracle.adamw_step(p, g, np.zeros(n_s), np.zeros(n_s), step=1, lr=ah.lr, beta1=ah.beta1,
+                      beta2=ah.beta2, eps=ah.eps, weight_decay=ah.weight_decay)
+    adamw_s = (time.perf_counter() - t0) * (n / n_s)
+    return {"value": round((muon_s + adamw_s) * 1e3, 1), "unit": "ms", "cores": int(cores),
+            "kind": "oracle",
+            "sample": (f"Muon: one step of {', '.join(parts)} matrices, scaled by K; AdamW: "
+                       f"{n_s} of {n} elements, scaled; numpy float64 (BLAS threads={cores}, "
+                       "elementwise single-threaded)")}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported "
+              "(each owner's share runs on its own GPU, see the design notes)", file=sys.stderr)
+        sys.exit(2)
+    import torch
+
+    import adamw_optimizer_step_muon_amd as ma
+    import workloads
+    from workloads import gen
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    wl = workloads.workload(args.workload)
+    mh, ah = wl.muon_hp, wl.adamw_hp
+
+    # ---- inputs resident in HBM ----
+    buckets = []
+    for bi, b in enumerate(wl.muon):
+        p = torch.empty((b.K, b.A, b.B), dtype=torch.float32, device=dev)
+        g = torch.empty_like(p)
+        gen.torch_muon_bucket(torch, wl, bi, 0, p)
+        gen.torch_muon_bucket(torch, wl, bi, 1, g)
+        buckets.append((p, g, torch.zeros_like(p)))
+    n = wl.adamw_numel
+    ap_ = torch.empty(n, dtype=torch.float32, device=dev)
+    ag = torch.empty_like(ap_)
+    gen.torch_adamw_flat(torch, wl, 0, ap_)
+    gen.torch_adamw_flat(torch, wl, 1, ag)
+    am, av = torch.zeros_like(ap_), torch.zeros_like(ap_)
+    ws = torch.empty(max(ma.muon_workspace_bytes([tuple(b[0].shape) for b in buckets]), 1),
+                     dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream(dev)
+    state = {"t": 0}
+
+    def adamw():
+        ma.adamw_step(ap_, ag, am, av, step=state["t"], lr=ah.lr, beta1=ah.beta1, beta2=ah.beta2,
+                      eps=ah.eps, weight_decay=ah.weight_decay, decoupled=ah.decoupled,
+                      cautious_wd=ah.cautious_wd, stream=stream)
+
+    def muon(ns_steps):
+        ma.muon_step(buckets, lr=mh.lr, momentum=mh.momentum, weight_decay=mh.weight_decay,
+                     nesterov=mh.nesterov, ns_steps=ns_steps, ns_eps=mh.ns_eps,
+                     cautious_wd=mh.cautious_wd, scale_mode=mh.scale_mode, workspace=ws,
+                     stream=stream)
+
+    def step():
+        state["t"] += 1
+        adamw()
+        muon(mh.ns_steps)
+
+    def timed(fn, reps):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record(stream)
+        for _ in range(reps):
+            fn()
+        e1.record(stream)
+        e1.synchronize()
+        return e0.elapsed_time(e1) / reps  # ms per call
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    step_ms = timed(step, args.steps)
+    wall_s = time.perf_counter() - wall0
+
+    # ---- per-kernel figures, live, same stream ----
+    reps = max(3, args.steps)
+    muon_ms = timed(lambda: muon(mh.ns_steps), reps)
+    muon0_ms = timed(lambda: muon(0), reps)
+    ns_ms = max(muon_ms - muon0_ms, 1e-9)          # the 3 x ns_steps GEMM launches per bucket
+    launches = 3 * mh.ns_steps * len(wl.muon)
+    flops = ns_flops(wl)
+    ns_tflops = flops / (ns_ms * 1e-3) / 1e12
+    state["t"] = 1
+    adamw_ms = timed(adamw, reps)
+    adamw_gbs = ADAMW_BYTES_PER_ELEM * n / (adamw_ms * 1e-3) / 1e9
+
+    out = {
+        "metric": "optimizer-step ms + NS TFLOP/s (%MFMA peak) + AdamW GB/s (%HBM)",
+        "value": round(step_ms, 4),
+        "unit": "ms",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(step_ms, 4),
+        "higher_is_better": False,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16 MFMA (fp32 accumulate) + fp32 elementwise",
+        "data": "synthetic (seeded device-generated gradients and N(0,1) parameters)",
+        "config": {"workload": wl.name, "muon_buckets": [[b.K, b.A, b.B] for b in wl.muon],
+                   "adamw_elements": n, "ns_steps": mh.ns_steps,
+                   "cautious_wd": mh.cautious_wd},
+        "ns_tflops": round(ns_tflops, 2),
+        "ns_mfma_frac": round(ns_tflops / MFMA_BF16_PEAK_TFLOPS, 4),
+        "ns_ms": round(ns_ms, 4),
+        "adamw_ms": round(adamw_ms, 4),
+        "adamw_gbs": round(adamw_gbs, 1),
+        "adamw_hbm_frac": round(adamw_gbs / HBM_PEAK_GBS, 4),
+        "muon_elementwise_ms": round(muon0_ms, 4),
+        "roofline": {
+            "kernel": "ns_gemm_kernel (gram, poly, combine launches of Newton-Schulz)",
+            "bound": "mfma",
+            "achieved": round(ns_tflops, 2),
+            "peak": MFMA_BF16_PEAK_TFLOPS,
+            "unit": "TFLOP/s",
+            "frac": round(ns_tflops / MFMA_BF16_PEAK_TFLOPS, 4),
+            "traffic": None,
+            "flops_per_launch": flops / launches,
+            "avg_launch_ms": ns_ms / launches,
+        },
+        "adamw_roofline": {
+            "kernel": "adamw_vec_kernel",
+            "bound": "hbm",
+            "achieved": round(adamw_gbs, 1),
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": round(adamw_gbs / HBM_PEAK_GBS, 4),
+            "traffic": None,
+        },
+        "timed_wall_s": round(wall_s, 3),
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(wl, args.cpu_budget_s)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

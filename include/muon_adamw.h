@@ -1,0 +1,167 @@
+/*
+ * muon_adamw.h -- C ABI of the hybrid Muon + AdamW optimizer step on MI355X (gfx950).
+ *
+ * The library (libmuonadamw.so) performs one optimizer step:
+ *
+ *   ma_muon_step   Muon on shape buckets of 2-D hidden matrices: sum-form momentum,
+ *                  Nesterov input, Frobenius normalisation, quintic Newton-Schulz
+ *                  orthogonalisation in bf16 on the matrix cores, shape scale and
+ *                  decoupled (optionally cautious) weight decay.
+ *   ma_adamw_step  the fused elementwise AdamW step over one flat fp32 range
+ *                  (embeddings, LM head, normalisation gains, biases).
+ *
+ * Sources, by page title:
+ *   [HB] "Optimizers: AdamW, Muon and the distributed optimizer" (AI infra handbook):
+ *        section "AdamW: decoupled weight decay" and section "Muon: orthogonalising
+ *        the update" (the update's three steps, the newton_schulz and Muon listings).
+ *   [NC] "MuonAdamW vs DistMuonAdamW: Key Differences for Single and Multi-GPU Training
+ *        in nanochat": one optimizer with "adamw" and "muon" parameter groups, a fused
+ *        AdamW kernel and a fused Muon kernel over same-shape stacks (K, ...).
+ *   [DM] "dtensor-muon" package description, "Features" and "Key options": Nesterov
+ *        switch, ns_steps, cautious weight decay, decoupled vs coupled Adam decay.
+ *   [DMuon] "DMuon: Efficient Distributed Muon Training with Near-Adam Overhead",
+ *        section 2.2: batching same-shape matrices, symmetric (lower-triangle) Gram.
+ *
+ * Conventions shared by every entry point
+ *   - Pointers are DEVICE pointers unless marked "host".  All device memory is owned
+ *     by the caller; the library never allocates, frees or keeps a pointer after the
+ *     work it enqueued has completed.
+ *   - fp32 tensors are contiguous row-major.  Device pointers must be 4-byte aligned;
+ *     16-byte alignment (what allocators return) selects the vectorised kernels,
+ *     other alignments give identical results through scalar kernels.
+ *   - `stream` is a hipStream_t passed as void* (NULL: the null stream).  Calls enqueue
+ *     their kernels on it and return without synchronising.
+ *   - Argument errors are detected on the host before anything is launched; the
+ *     call then returns a negative ma_status and ma_last_error() describes it.
+ *     A failed launch returns MA_ERR_HIP.  Faults inside kernels surface at the
+ *     caller's next synchronisation.  No C++ exception crosses this boundary.
+ *   - Calls are thread-safe with respect to each other as long as they do not share
+ *     buffers; ma_last_error() is per calling thread.
+ */
+#ifndef MUON_ADAMW_H
+#define MUON_ADAMW_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define MA_ABI_VERSION 1
+
+typedef enum {
+  MA_OK = 0,
+  MA_ERR_INVALID_ARG = -1, /* null pointer, bad size, bad hyperparameter, overlap */
+  MA_ERR_UNSUPPORTED = -2, /* valid request outside what this build handles */
+  MA_ERR_WORKSPACE = -3,   /* workspace missing, misaligned or too small */
+  MA_ERR_HIP = -4          /* a HIP runtime call or launch failed */
+} ma_status;
+
+/* One shape bucket of Muon matrices [NC]: K matrices of A x B, stacked (K, A, B).
+ * K == 0 is an empty bucket (skipped).  The three buffers must not overlap. */
+typedef struct {
+  int64_t K, A, B;
+  float* param;       /* device, (K, A, B) fp32, updated in place */
+  const float* grad;  /* device, (K, A, B) fp32, read only */
+  float* momentum;    /* device, (K, A, B) fp32, updated in place; zeros before step 1 */
+} ma_muon_bucket;
+
+/* Muon hyperparameters ([HB] update steps; [DM] "Key options"). */
+typedef struct {
+  float lr;               /* learning rate eta */
+  float momentum;         /* mu; M <- mu M + G */
+  float weight_decay;     /* lambda; P <- P (1 - eta lambda) before the update */
+  float ns_eps;           /* added to ||U||_F before dividing (1e-7 in [HB]) */
+  int32_t nesterov;       /* 1: NS input U = G + mu M (new M); 0: U = M */
+  int32_t cautious_wd;    /* 1: decay only where update * param > 0 [DM] */
+  int32_t ns_steps;       /* Newton-Schulz iterations, 0..MA_MAX_NS_STEPS */
+  int32_t scale_mode;     /* 0: 0.2 sqrt(max(A,B)) [HB]; 1: sqrt(max(1, A/B)) [HB] */
+  const float* ns_coeffs; /* host, ns_steps x 3 (a, b, c) per iteration; NULL selects
+                             the quintic (3.4445, -4.7750, 2.0315) for every iteration */
+} ma_muon_hparams;
+
+#define MA_MAX_NS_STEPS 64
+
+/* Routing report for one bucket (integer, exact).  [HB] newton_schulz listing: a
+ * matrix with more rows than columns (A > B, strict) is orthogonalised transposed,
+ * so that the Gram matrix X X^T is the smaller square.  m = min(A,B), n = max(A,B).
+ * m_pad / n_pad are the tile-padded sizes of the workspace layout. */
+typedef struct {
+  int32_t transposed;
+  int32_t m, n;
+  int32_t ns_steps_run;
+  int32_t m_pad, n_pad;
+} ma_muon_route;
+
+/* AdamW hyperparameters ([HB] "AdamW: decoupled weight decay"; [DM] is_adamw). */
+typedef struct {
+  float lr, beta1, beta2, eps, weight_decay;
+  int64_t step;          /* t >= 1, used for the bias corrections 1 - beta^t */
+  int32_t decoupled;     /* 1: AdamW, decay applied to the weights; 0: Adam + L2 */
+  int32_t cautious_wd;   /* 1 (decoupled only): decay only where update * param > 0 */
+} ma_adamw_hparams;
+
+/* ABI version of the loaded library (MA_ABI_VERSION it was built with). */
+int ma_abi_version(void);
+
+/* Static text for a status code. */
+const char* ma_status_string(int status);
+
+/* Detail of the last failure on the calling thread ("" if none). */
+const char* ma_last_error(void);
+
+/* Host only: the route one A x B matrix takes (see ma_muon_route).  hp may be NULL
+ * (ns_steps 5).  Returns MA_ERR_INVALID_ARG for A < 1, B < 1 or a NULL out. */
+ma_status ma_muon_route_of(int64_t A, int64_t B, const ma_muon_hparams* hp, ma_muon_route* out);
+
+/* Host only: workspace bytes ma_muon_step needs for these buckets (the maximum
+ * over buckets, which run one after another).  0 when there is nothing to do.
+ * Returns 0 as well for invalid arguments; ma_muon_step then reports them. */
+size_t ma_muon_workspace_bytes(const ma_muon_bucket* buckets, int32_t n_buckets,
+                               const ma_muon_hparams* hp);
+
+/* One Muon step on every bucket [HB], in this order per bucket:
+ *   M <- mu M + G;  U <- G + mu M (nesterov) or M;  X0 <- U / (||U||_F + ns_eps)  (bf16,
+ *   transposed when A > B);  ns_steps times: R <- X X^T, P <- b R + c R R,
+ *   X <- a X + P X  (bf16 operands, fp32 accumulation);  O <- X (un-transposed);
+ *   s <- scale(A, B);  P <- P - eta lambda [mask] P - eta s O,
+ *   mask = (s O * P > 0) when cautious_wd, else 1.
+ * buckets:    host array of n_buckets descriptors (n_buckets >= 0).
+ * workspace:  device, 256-byte aligned, at least ma_muon_workspace_bytes(...) bytes;
+ *             may be NULL when that is 0.  Its contents are scratch.
+ * route_out:  host, NULL or an array of n_buckets reports filled before any launch.
+ * Errors: MA_ERR_INVALID_ARG (null/overlapping buffers, K < 0, A or B < 1 with K > 0,
+ * ns_steps out of range, non-finite hyperparameters), MA_ERR_WORKSPACE, MA_ERR_HIP. */
+ma_status ma_muon_step(const ma_muon_bucket* buckets, int32_t n_buckets,
+                       const ma_muon_hparams* hp, void* workspace, size_t workspace_bytes,
+                       void* stream, ma_muon_route* route_out);
+
+/* One AdamW step over n elements [HB]:
+ *   decoupled: p <- p (1 - lr wd)   (cautious: only where update * p > 0)
+ *   coupled:   g <- g + wd p
+ *   m <- b1 m + (1 - b1) g;  v <- b2 v + (1 - b2) g^2
+ *   p <- p - lr mhat / (sqrt(vhat) + eps),  mhat = m / (1 - b1^t),  vhat = v / (1 - b2^t)
+ * param, exp_avg, exp_avg_sq are updated in place; grad is read only.  n == 0 is a
+ * no-op.  The four ranges must not overlap.
+ * Errors: MA_ERR_INVALID_ARG (null pointers with n > 0, n < 0, step < 1, overlap,
+ * non-finite hyperparameters), MA_ERR_HIP. */
+ma_status ma_adamw_step(float* param, const float* grad, float* exp_avg, float* exp_avg_sq,
+                        int64_t n, const ma_adamw_hparams* hp, void* stream);
+
+/* Host only: workspace bytes ma_newton_schulz needs for a (K, A, B) stack. */
+size_t ma_newton_schulz_workspace_bytes(int64_t K, int64_t A, int64_t B);
+
+/* The orthogonalisation alone ([HB] newton_schulz): for each of K matrices,
+ * out = NS(in) in the input's own orientation, fp32, using hp->ns_eps, hp->ns_steps
+ * and hp->ns_coeffs (other fields ignored).  in and out must not overlap.
+ * Errors: as ma_muon_step. */
+ma_status ma_newton_schulz(const float* in, float* out, int64_t K, int64_t A, int64_t B,
+                           const ma_muon_hparams* hp, void* workspace, size_t workspace_bytes,
+                           void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MUON_ADAMW_H */

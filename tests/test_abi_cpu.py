@@ -1,0 +1,186 @@
+"""The C ABI on the host: the library loads, exports every symbol the header
+declares, routes shapes like the oracle, sizes workspaces, and rejects bad
+arguments before launching anything (no GPU needed: nothing here reaches a kernel).
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+import oracle
+from conftest import ROOT
+
+ma = pytest.importorskip("adamw_optimizer_step_muon_amd")
+from adamw_optimizer_step_muon_amd import _lib  # noqa: E402
+
+HEADER = os.path.join(ROOT, "include", "muon_adamw.h")
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(_lib.LIB_PATH):
+        pytest.skip("libmuonadamw.so not built")
+    return _lib.load()
+
+
+def _declared():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(ma_[a-z_]+)\s*\(", text)))
+
+
+def test_exports_every_declared_symbol(lib):
+    declared = _declared()
+    assert set(declared) == set(_lib.EXPORTED)
+    for name in declared:
+        assert hasattr(lib, name), name
+
+
+def test_abi_version_matches_header(lib):
+    m = re.search(r"#define MA_ABI_VERSION (\d+)", open(HEADER).read())
+    assert lib.ma_abi_version() == int(m.group(1))
+    assert lib.ma_status_string(0) == b"ok"
+    assert lib.ma_status_string(-3).startswith(b"workspace")
+
+
+@pytest.mark.parametrize("A,B", [(64, 128), (128, 64), (768, 768), (768, 3072), (3072, 768),
+                                 (2048, 512), (512, 2048), (8192, 28672), (28672, 8192),
+                                 (1, 1), (1, 5), (5, 1), (257, 129), (129, 257)])
+@pytest.mark.parametrize("steps", [0, 5, 7])
+def test_routing_matches_oracle(lib, A, B, steps):
+    r = ma.muon_route_of(A, B, steps)
+    o = oracle.route(A, B, steps)
+    assert (r.transposed, r.m, r.n, r.ns_steps_run) == (o.transposed, o.m, o.n, o.ns_steps)
+    assert r.m_pad % 128 == 0 and r.n_pad % 128 == 0
+    assert r.m <= r.m_pad < r.m + 128 and r.n <= r.n_pad < r.n + 128
+
+
+def test_workspace_bytes(lib):
+    assert ma.muon_workspace_bytes([]) == 0
+    one = ma.muon_workspace_bytes([(1, 768, 3072)])
+    # X, X^T twice (bf16, m x n) plus R and P (bf16, m x m), plus norm scratch
+    assert one >= 4 * 768 * 3072 * 2 + 2 * 768 * 768 * 2
+    assert ma.muon_workspace_bytes([(2, 768, 3072)]) > one
+    # buckets run one after another: the maximum, not the sum
+    both = ma.muon_workspace_bytes([(1, 768, 3072), (1, 3072, 768)])
+    assert both == max(one, ma.muon_workspace_bytes([(1, 3072, 768)]))
+    assert ma.muon_workspace_bytes([(0, 10, 10)]) == 0
+
+
+def _hp(**kw):
+    base = dict(lr=0.02, momentum=0.95, weight_decay=0.1, ns_eps=1e-7, nesterov=1,
+                cautious_wd=0, ns_steps=5, scale_mode=0)
+    base.update(kw)
+    return _lib._MuonHParams(**base)
+
+
+FAKE = 0x10000000  # never dereferenced: every call below fails validation first
+
+
+@pytest.mark.parametrize("case,status", [
+    ("null_hp", _lib.MA_ERR_INVALID_ARG),
+    ("neg_steps", _lib.MA_ERR_INVALID_ARG),
+    ("big_steps", _lib.MA_ERR_INVALID_ARG),
+    ("bad_scale", _lib.MA_ERR_INVALID_ARG),
+    ("nan_lr", _lib.MA_ERR_INVALID_ARG),
+    ("neg_K", _lib.MA_ERR_INVALID_ARG),
+    ("zero_A", _lib.MA_ERR_INVALID_ARG),
+    ("null_param", _lib.MA_ERR_INVALID_ARG),
+    ("misaligned", _lib.MA_ERR_INVALID_ARG),
+    ("overlap", _lib.MA_ERR_INVALID_ARG),
+    ("no_workspace", _lib.MA_ERR_WORKSPACE),
+    ("small_workspace", _lib.MA_ERR_WORKSPACE),
+    ("unaligned_workspace", _lib.MA_ERR_WORKSPACE),
+])
+def test_muon_step_rejects_before_launch(lib, case, status):
+    K, A, B = 2, 64, 96
+    size = K * A * B * 4
+    bucket = _lib._MuonBucket(K, A, B, FAKE, FAKE + 2 * size, FAKE + 4 * size)
+    hp = _hp()
+    hp_ptr = ctypes.byref(hp)
+    need = lib.ma_muon_workspace_bytes(ctypes.byref(bucket), 1, hp_ptr)
+    ws, ws_bytes = FAKE + 8 * size, need
+    if case == "null_hp":
+        hp_ptr = None
+    elif case == "neg_steps":
+        hp.ns_steps = -1
+    elif case == "big_steps":
+        hp.ns_steps = _lib.MA_MAX_NS_STEPS + 1
+    elif case == "bad_scale":
+        hp.scale_mode = 2
+    elif case == "nan_lr":
+        hp.lr = float("nan")
+    elif case == "neg_K":
+        bucket.K = -1
+    elif case == "zero_A":
+        bucket.A = 0
+    elif case == "null_param":
+        bucket.param = None
+    elif case == "misaligned":
+        bucket.grad = FAKE + 2 * size + 2
+    elif case == "overlap":
+        bucket.grad = FAKE + size // 2
+    elif case == "no_workspace":
+        ws = None
+    elif case == "small_workspace":
+        ws_bytes = need - 1
+    elif case == "unaligned_workspace":
+        ws = FAKE + 8 * size + 16
+    got = lib.ma_muon_step(ctypes.byref(bucket), 1, hp_ptr, ws, ws_bytes, None, None)
+    assert got == status, (case, lib.ma_last_error())
+    assert lib.ma_last_error()
+
+
+@pytest.mark.parametrize("case", ["null_hp", "step0", "neg_n", "null_ptr", "overlap",
+                                  "misaligned", "beta_one", "inf_eps"])
+def test_adamw_step_rejects_before_launch(lib, case):
+    n = 1000
+    p, g, m, v = FAKE, FAKE + 4 * n, FAKE + 8 * n, FAKE + 12 * n
+    hp = _lib._AdamWHParams(lr=1e-3, beta1=0.9, beta2=0.95, eps=1e-8, weight_decay=0.1, step=1,
+                            decoupled=1, cautious_wd=0)
+    hp_ptr = ctypes.byref(hp)
+    if case == "null_hp":
+        hp_ptr = None
+    elif case == "step0":
+        hp.step = 0
+    elif case == "neg_n":
+        n = -1
+    elif case == "null_ptr":
+        g = None
+    elif case == "overlap":
+        m = FAKE + 4 * n + 40
+    elif case == "misaligned":
+        v = FAKE + 12 * n + 1
+    elif case == "beta_one":
+        hp.beta2 = 1.0
+    elif case == "inf_eps":
+        hp.eps = float("inf")
+    got = lib.ma_adamw_step(p, g, m, v, n, hp_ptr, None)
+    assert got == _lib.MA_ERR_INVALID_ARG, (case, lib.ma_last_error())
+
+
+def test_empty_calls_are_no_ops(lib):
+    hp = _lib._AdamWHParams(lr=1e-3, beta1=0.9, beta2=0.95, eps=1e-8, weight_decay=0.1, step=1,
+                            decoupled=1, cautious_wd=0)
+    assert lib.ma_adamw_step(None, None, None, None, 0, ctypes.byref(hp), None) == 0
+    mhp = _hp()
+    assert lib.ma_muon_step(None, 0, ctypes.byref(mhp), None, 0, None, None) == 0
+    empty = _lib._MuonBucket(0, 64, 64, None, None, None)
+    route = _lib._MuonRoute()
+    assert lib.ma_muon_step(ctypes.byref(empty), 1, ctypes.byref(mhp), None, 0, None,
+                            ctypes.byref(route)) == 0
+    assert route.m == 0
+
+
+def test_optimizer_state_bytes_match_printed(golden):
+    # Printed in the handbook's "The optimizer's memory budget" section: 8 bytes of
+    # state per AdamW parameter, 4 per Muon parameter (4096x1024 + 1024x4096).
+    torch = pytest.importorskip("torch")
+    g = golden("state_bytes.txt")
+    w1 = torch.zeros(4096, 1024)
+    w2 = torch.zeros(1024, 4096)
+    opt = ma.MuonAdamW([{"params": [w1], "kind": "muon"}, {"params": [w2], "kind": "adamw"}])
+    assert (w1.numel() + w2.numel()) / 1e6 == pytest.approx(float(g["params_millions"][0]), abs=0.05)
+    assert opt.state_bytes_per_param("adamw") == float(g["adamw_state_bytes_per_param"][0])
+    assert opt.state_bytes_per_param("muon") == float(g["muon_state_bytes_per_param"][0])

@@ -1,0 +1,150 @@
+"""AdamW through the C ABI on the GPU against the fp64 oracle, element by element."""
+import numpy as np
+import pytest
+
+import oracle
+import workloads
+from parity import ADAMW_RTOL, f32, rel_err_floor
+from workloads import gen
+
+torch = pytest.importorskip("torch")
+ma = pytest.importorskip("adamw_optimizer_step_muon_amd")
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda:0"
+
+
+def _hp(**kw):
+    base = dict(lr=3e-3, beta1=0.9, beta2=0.95, eps=1e-8, weight_decay=0.1, decoupled=True,
+                cautious_wd=False)
+    base.update(kw)
+    return base
+
+
+def _oracle_hp(hp):
+    return {k: (f32(v) if isinstance(v, float) else v) for k, v in hp.items()}
+
+
+def _run(p0, grads, hp, offset=0):
+    """Run len(grads) steps on the GPU; return (param, exp_avg, exp_avg_sq) per step."""
+    n = p0.size
+    buf = torch.zeros(4, n + offset, dtype=torch.float32, device=DEV)
+    gbuf = torch.zeros(n + offset, dtype=torch.float32, device=DEV)
+    p, m, v = buf[0, offset:], buf[1, offset:], buf[2, offset:]
+    g = gbuf[offset:]
+    p.copy_(torch.from_numpy(p0))
+    out = []
+    for t, gr in enumerate(grads, start=1):
+        g.copy_(torch.from_numpy(gr))
+        ma.adamw_step(p, g, m, v, step=t, **hp)
+        torch.cuda.synchronize()
+        out.append((p.cpu().numpy().copy(), m.cpu().numpy().copy(), v.cpu().numpy().copy()))
+    return out
+
+
+def _oracle(p0, grads, hp):
+    p, m, v = p0.astype(np.float64), np.zeros(p0.size), np.zeros(p0.size)
+    out = []
+    for t, gr in enumerate(grads, start=1):
+        r = oracle.adamw_step(p, gr, m, v, step=t, **_oracle_hp(hp))
+        p, m, v = r.param, r.exp_avg, r.exp_avg_sq
+        out.append((p, m, v))
+    return out
+
+
+def _check(got, ref):
+    for step, ((gp, gm, gv), (rp, rm, rv)) in enumerate(zip(got, ref), start=1):
+        for name, a, b in (("param", gp, rp), ("exp_avg", gm, rm), ("exp_avg_sq", gv, rv)):
+            err = rel_err_floor(a, b)
+            assert err <= ADAMW_RTOL, f"step {step} {name}: {err:.3e}"
+
+
+@pytest.mark.parametrize("n", [1, 3, 4, 5, 255, 1023, 4096, 262147])
+@pytest.mark.parametrize("offset", [0, 1])
+def test_adamw_ragged_and_misaligned(n, offset):
+    rng = np.random.default_rng(n * 7 + offset)
+    p0 = rng.standard_normal(n).astype(np.float32)
+    grads = [(1e-3 * rng.standard_normal(n)).astype(np.float32) for _ in range(3)]
+    hp = _hp()
+    _check(_run(p0, grads, hp, offset), _oracle(p0, grads, hp))
+
+
+@pytest.mark.parametrize("variant", [dict(decoupled=False), dict(cautious_wd=True),
+                                     dict(weight_decay=0.0), dict(beta2=0.999, lr=1e-2)])
+def test_adamw_variants(variant):
+    rng = np.random.default_rng(5)
+    n = 100003
+    p0 = rng.standard_normal(n).astype(np.float32)
+    grads = [(1e-3 * rng.standard_normal(n)).astype(np.float32) for _ in range(4)]
+    hp = _hp(**variant)
+    _check(_run(p0, grads, hp), _oracle(p0, grads, hp))
+
+
+def test_adamw_decay_experiment_on_gpu(golden):
+    # the handbook's decay experiment (gradients 1000x apart, 1000 steps) through the kernel
+    g = golden("adamw_decay_experiment.txt")
+    scale = np.array([0.01, 10.0], dtype=np.float32)
+    hp = dict(lr=1e-2, beta1=0.9, beta2=0.999, eps=1e-8, weight_decay=0.1)
+    out = {}
+    for decoupled in (False, True):
+        p = torch.ones(2, device=DEV)
+        gr = torch.zeros(2, device=DEV)
+        m, v = torch.zeros(2, device=DEV), torch.zeros(2, device=DEV)
+        for t in range(1000):
+            gr.copy_(torch.from_numpy(scale * (-1.0) ** t))
+            ma.adamw_step(p, gr, m, v, step=t + 1, decoupled=decoupled, **hp)
+        out[decoupled] = p.cpu().numpy()
+    assert f"{out[False][0]:.3f}" == g["coupled_small"][0]
+    assert f"{out[False][1]:.3f}" == g["coupled_large"][0]
+    assert f"{out[True][0]:.3f}" == g["decoupled_small"][0]
+    assert f"{out[True][1]:.3f}" == g["decoupled_large"][0]
+
+
+def test_adamw_tiny_workload_all_steps():
+    wl = workloads.workload(0)
+    p0 = gen.np_adamw_flat_params(wl)
+    grads = [gen.np_adamw_flat_grads(wl, t) for t in range(1, wl.steps + 1)]
+    ah = wl.adamw_hp
+    hp = _hp(lr=ah.lr, beta1=ah.beta1, beta2=ah.beta2, eps=ah.eps, weight_decay=ah.weight_decay)
+    _check(_run(p0, grads, hp), _oracle(p0, grads, hp))
+
+
+def test_adamw_zero_length_and_determinism():
+    rng = np.random.default_rng(9)
+    n = 65537
+    p0 = rng.standard_normal(n).astype(np.float32)
+    grads = [(1e-3 * rng.standard_normal(n)).astype(np.float32) for _ in range(2)]
+    a = _run(p0, grads, _hp())
+    b = _run(p0, grads, _hp())
+    for x, y in zip(a, b):
+        for u, w in zip(x, y):
+            assert np.array_equal(u, w)
+    e = torch.empty(0, device=DEV)
+    ma.adamw_step(e, e, e, e, step=1, lr=1e-3)
+
+
+@pytest.mark.parametrize("index", [1, 2, 3, 4])
+def test_adamw_full_size_sampled(index):
+    """Full flat AdamW buffer of the workload, in the launch configuration the
+    benchmark times; 200k sampled elements re-computed by the oracle one by one."""
+    wl = workloads.workload(index)
+    n = wl.adamw_numel
+    ah = wl.adamw_hp
+    hp = _hp(lr=ah.lr, beta1=ah.beta1, beta2=ah.beta2, eps=ah.eps, weight_decay=ah.weight_decay)
+    steps = 2
+    p = torch.empty(n, dtype=torch.float32, device=DEV)
+    gen.torch_adamw_flat(torch, wl, 0, p)
+    m, v = torch.zeros_like(p), torch.zeros_like(p)
+    idx = np.sort(np.random.default_rng(index).choice(n, size=200_000, replace=False))
+    tidx = torch.from_numpy(idx).to(DEV)
+    p0 = p[tidx].cpu().numpy()
+    g = torch.empty_like(p)
+    gs = []
+    for t in range(1, steps + 1):
+        gen.torch_adamw_flat(torch, wl, t, g)
+        gs.append(g[tidx].cpu().numpy())
+        ma.adamw_step(p, g, m, v, step=t, **hp)
+    torch.cuda.synchronize()
+    got = [(p[tidx].cpu().numpy(), m[tidx].cpu().numpy(), v[tidx].cpu().numpy())]
+    ref = _oracle(p0, gs, hp)[-1:]
+    _check(got, ref)
