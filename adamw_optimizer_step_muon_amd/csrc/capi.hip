@@ -4,6 +4,7 @@
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
+#include <cstdlib>
 #include <string>
 
 #include "muon_adamw.h"
@@ -77,11 +78,11 @@ ma_status check_shape(int64_t K, int64_t A, int64_t B) {
   if (A < 1 || B < 1)
     return fail(MA_ERR_INVALID_ARG, "matrix shape %lld x %lld", (long long)A, (long long)B);
   const int64_t m = A < B ? A : B, n = A < B ? B : A;
-  if (round_up(m, kTile) > kMaxSide || round_up(n, kTile) > kMaxSide)
+  if (round_up(m, 256) > kMaxSide || round_up(n, 256) > kMaxSide)
     return fail(MA_ERR_UNSUPPORTED, "matrix side above %lld", (long long)kMaxSide);
   // grid limits: (nblk, K) and (Bp/64, Ap/64, K) launches, K x tiles GEMM launches
   const BucketPlan p = plan_bucket(K, A, B);
-  const int64_t tiles = (p.m_pad / kTile) * (p.n_pad / kTile);
+  const int64_t tiles = (p.m_pad / p.tile) * (p.n_pad / p.tile);
   if (K > 65535 || p.nblk > kMaxBlocks || K * tiles > kMaxBlocks ||
       K * A * B / 4 / 256 > kMaxBlocks)
     return fail(MA_ERR_UNSUPPORTED, "bucket (%lld, %lld, %lld) exceeds the launch grid",
@@ -137,8 +138,13 @@ BucketPlan plan_bucket(int64_t K, int64_t A, int64_t B) {
   p.transposed = A > B;
   p.m = p.transposed ? B : A;
   p.n = p.transposed ? A : B;
-  p.m_pad = round_up(p.m, kTile);
-  p.n_pad = round_up(p.n, kTile);
+  p.tile = pick_tile(K, p.m, p.n);
+  if (const char* env = std::getenv("MA_NS_TILE")) {  // tuning override: 128 or 256
+    const int t = std::atoi(env);
+    if (t == 128 || t == 256) p.tile = t;
+  }
+  p.m_pad = round_up(p.m, p.tile);
+  p.n_pad = round_up(p.n, p.tile);
   p.nblk = (A * B + kPrepChunk - 1) / kPrepChunk;
   if (p.nblk < 1) p.nblk = 1;
   const size_t xb = static_cast<size_t>(K * p.m_pad * p.n_pad) * 2;

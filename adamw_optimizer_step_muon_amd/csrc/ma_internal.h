@@ -29,13 +29,13 @@ __device__ __forceinline__ float bf2f(unsigned short h) {
 // ---------------------------------------------------------------------------
 // Workspace layout of one Muon bucket (bf16 buffers, tile-padded)
 // ---------------------------------------------------------------------------
-constexpr int kTile = 128;        // square GEMM macro-tile; m and n pad to this
 constexpr int kCastTile = 64;     // normalise/cast kernel tile
 constexpr int kPrepChunk = 16384; // elements per momentum/norm block
 
 struct BucketPlan {
   int64_t K, A, B;
   bool transposed;
+  int tile;  // square GEMM tile (128 or 256); m and n are padded to it
   int64_t m, n, m_pad, n_pad;
   int64_t nblk;  // momentum/norm blocks per matrix
   // byte offsets inside the workspace
@@ -43,6 +43,8 @@ struct BucketPlan {
 };
 
 BucketPlan plan_bucket(int64_t K, int64_t A, int64_t B);
+// GEMM tile for a bucket of K matrices with Gram side m and long side n
+int pick_tile(int64_t K, int64_t m, int64_t n);
 
 // ---------------------------------------------------------------------------
 // Kernel launchers (return hipSuccess or the launch error)

@@ -9,7 +9,7 @@
 //   combine:  X' = a X + P X           m x n
 //
 // Every product is C = A B^T with both operands stored row-major along the
-// contraction index, which is what the MFMA operand layout wants:
+// contraction index, which is the layout the MFMA operands want:
 //   gram     A = B = X  (contraction over n)
 //   poly     A = B = R  (contraction over m)
 //   combine  A = P, B = X^T (the library keeps X in both orientations; contraction m)
@@ -18,25 +18,25 @@
 // with Near-Adam Overhead", section 2.2, symmetry exploitation); same-shape matrices
 // are batched in one launch (same section, batching).
 //
-// Tiling: 128 x 128 output tile per 256-thread block (2 x 2 waves of 64 x 64), k-steps
-// of 64, operands staged through LDS (double-buffered, XOR-swizzled 16-byte chunks so
-// the 32 rows an MFMA fragment reads hit distinct banks), v_mfma_f32_32x32x16_bf16.
-// All sizes are padded to the tile by the caller (zero padding is preserved by the
-// iteration), so there are no bounds checks inside.
+// Kernel structure (one template, two tile shapes):
+//   * BM x BN output tile per block, WM x WN waves, v_mfma_f32_32x32x16_bf16;
+//   * operands stream HBM/L2 -> LDS with global_load_lds_dwordx4 (no register
+//     staging) into STAGES ring buffers; each 16-byte chunk of an operand row is
+//     XOR-swizzled so the 32 rows one MFMA fragment reads fall on distinct banks;
+//     the swizzle is applied on the global side, since LDS-DMA writes each wave's
+//     64 chunks contiguously;
+//   * blocks are renumbered so each XCD (blocks go round-robin to the 8 XCDs) works
+//     on a contiguous run of tiles, and those runs are grouped by row panels, so
+//     the blocks resident on one XCD share operand panels in its L2;
+//   * epilogue in registers (a/b/c terms in fp32, round to bf16), row-major stores
+//     straight from the accumulator layout, the transposed / mirrored copy through
+//     an XOR-swizzled LDS tile with 16-byte stores.
+// Sizes are padded to the tile by the caller and the padding is zero (preserved by
+// the iteration), so there are no bounds checks inside.
 #include "ma_internal.h"
 
 namespace ma {
 namespace {
-
-constexpr int BM = kTile;  // 128
-constexpr int BN = kTile;
-constexpr int BK = 64;
-constexpr int kThreads = 256;
-constexpr int WTM = 2;     // 32x32 MFMA tiles per wave along M
-constexpr int WTN = 2;     // along N
-constexpr int kChunksPerRow = BK / 8;  // 16-byte chunks per LDS row
-constexpr int kLoadIters = (BM * kChunksPerRow) / kThreads;  // 4
-constexpr int kTPad = 8;   // epilogue transpose tile padding (bf16 elements)
 
 enum Epi { kGram = 0, kPoly = 1, kCombine = 2 };
 
@@ -48,33 +48,88 @@ struct GemmArgs {
   unsigned short* C;    // row-major target
   unsigned short* C2;   // transposed target (combine) or mirror target (gram/poly)
   int64_t ldc, ldc2, strideC, strideC2;
-  const unsigned short* aux;  // poly: R; combine: X
+  const unsigned short* aux;  // transposed a/b-term source: poly R (symmetric), combine X^T
   int64_t ldaux, strideAux;
   float alpha, beta;    // poly: b, c; combine: a, 1
   int tiles_m, tiles_n; // tile grid (triangular for gram/poly)
   int tiles_per_batch;
 };
 
-__device__ __forceinline__ int swz(int row, int chunk) { return chunk ^ (row & 7); }
+template <int BM_, int BN_, int BK_, int WM_, int WN_, int STAGES_>
+struct Cfg {
+  static constexpr int BM = BM_, BN = BN_, BK = BK_, WM = WM_, WN = WN_, STAGES = STAGES_;
+  static constexpr int kWaves = WM * WN;
+  static constexpr int kThreads = 64 * kWaves;
+  static constexpr int WTM = BM / (WM * 32);  // 32x32 MFMA tiles per wave along M
+  static constexpr int WTN = BN / (WN * 32);
+  static constexpr int kChunks = BK / 8;              // 16-byte chunks per operand row
+  static constexpr int kRowsPerDma = 64 / kChunks;    // rows one wave-wide LDS-DMA fills
+  static constexpr int kDmaA = BM / kRowsPerDma / kWaves;  // per wave per stage
+  static constexpr int kDmaB = BN / kRowsPerDma / kWaves;
+  static constexpr int kDmaPerStage = kDmaA + kDmaB;
+  static constexpr int kStageElems = (BM + BN) * BK;
+  static constexpr int kMainElems = STAGES * kStageElems;
+  static constexpr int kEpiElems = BM * BN;
+  static constexpr int kLdsElems = kMainElems > kEpiElems ? kMainElems : kEpiElems;
+  static constexpr int kGroupM = 4;  // row panels per L2 group (combine)
+  static_assert(BM % (WM * 32) == 0 && BN % (WN * 32) == 0, "wave tiling");
+  static_assert(BM % (kRowsPerDma * kWaves) == 0 && BN % (kRowsPerDma * kWaves) == 0, "dma");
+  static_assert(BK == 32 || BK == 64, "swizzle defined for BK 32 and 64");
+  static_assert(kLdsElems * 2 <= 160 * 1024, "LDS");
+};
 
-template <int kEpi>
-__global__ __launch_bounds__(kThreads, 2) void ns_gemm_kernel(GemmArgs args) {
-  __shared__ __attribute__((aligned(16))) unsigned short smem[2 * 2 * BM * BK];
-  unsigned short* As = smem;                 // [2][BM][BK]
-  unsigned short* Bs = smem + 2 * BM * BK;   // [2][BN][BK]
+// 16-byte chunk swizzle inside an operand row (an involution in c).
+template <int BK>
+__device__ __forceinline__ int swz(int r, int c) {
+  if constexpr (BK == 64) return c ^ (r & 7);         // 8 chunks: 8 rows -> 8 slots
+  else return c ^ ((r >> 1) & 3);                     // 4 chunks: row pairs fill the banks
+}
+
+// wait until at most n vector-memory operations of this wave are outstanding
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt");
+  // gfx9 s_waitcnt: vmcnt[3:0] | expcnt[6:4] | lgkmcnt[11:8] | vmcnt[5:4] at [15:14]
+  __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
+}
+
+__device__ __forceinline__ void dma16(const unsigned short* g, unsigned short* l) {
+  // address-space casts (generic -> global / LDS) need C-style casts
+  __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)(g),
+                                   (__attribute__((address_space(3))) void*)(l), 16, 0, 0);
+}
+
+// Block id -> logical id so that each XCD's blocks (bid % 8) are a contiguous run.
+__device__ __forceinline__ int xcd_linear(int bid, int nblocks) {
+  constexpr int kXcd = 8;
+  const int q = nblocks / kXcd, r = nblocks % kXcd;
+  const int xcd = bid % kXcd, local = bid / kXcd;
+  return xcd < r ? xcd * (q + 1) + local : r * (q + 1) + (xcd - r) * q + local;
+}
+
+template <class C, int kEpi>
+__global__ __launch_bounds__(C::kThreads) void ns_gemm_kernel(GemmArgs args) {
+  __shared__ __attribute__((aligned(16))) unsigned short smem[C::kLdsElems];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
-  const int wm = wave >> 1;
-  const int wn = wave & 1;
+  const int wm = wave / C::WN;
+  const int wn = wave % C::WN;
 
-  const int64_t batch = blockIdx.x / args.tiles_per_batch;
-  const int tile = blockIdx.x - static_cast<int>(batch) * args.tiles_per_batch;
+  const int lid = xcd_linear(blockIdx.x, gridDim.x);
+  const int64_t batch = lid / args.tiles_per_batch;
+  const int tile = lid - static_cast<int>(batch) * args.tiles_per_batch;
   int ti, tj;
   if (kEpi == kCombine) {
-    ti = tile / args.tiles_n;
-    tj = tile - ti * args.tiles_n;
+    // groups of kGroupM row panels; inside a group, column-major over tiles
+    const int per_group = C::kGroupM * args.tiles_n;
+    const int g = tile / per_group;
+    const int first = g * C::kGroupM;
+    const int rows = min(args.tiles_m - first, C::kGroupM);
+    const int in = tile - g * per_group;
+    ti = first + in % rows;
+    tj = in / rows;
   } else {
     // lower-triangle enumeration: tile = ti (ti + 1) / 2 + tj, tj <= ti
     ti = static_cast<int>((__builtin_sqrtf(8.0f * tile + 1.0f) - 1.0f) * 0.5f);
@@ -82,122 +137,149 @@ __global__ __launch_bounds__(kThreads, 2) void ns_gemm_kernel(GemmArgs args) {
     while (ti * (ti + 1) / 2 > tile) --ti;
     tj = tile - ti * (ti + 1) / 2;
   }
-  const int64_t m0 = static_cast<int64_t>(ti) * BM;
-  const int64_t n0 = static_cast<int64_t>(tj) * BN;
+  const int64_t m0 = static_cast<int64_t>(ti) * C::BM;
+  const int64_t n0 = static_cast<int64_t>(tj) * C::BN;
 
   const unsigned short* gA = args.A + batch * args.strideA + m0 * args.lda;
   const unsigned short* gB = args.B + batch * args.strideB + n0 * args.ldb;
 
-  // global -> register prefetch mapping: thread covers rows (tid>>3)+32*i, chunk tid&7
-  const int lrow = tid >> 3;
-  const int lch = tid & 7;
-  u32x4 ra[kLoadIters], rb[kLoadIters];
-
-  auto load_global = [&](int kt) {
+  // LDS-DMA source pointers for this lane (k offset added per stage)
+  const int drow = lane / C::kChunks;  // row inside one DMA
+  const int dpc = lane % C::kChunks;   // physical chunk this lane fills
+  auto issue_stage = [&](int kt, int slot) {
+    unsigned short* as = smem + slot * C::kStageElems;
+    unsigned short* bs = as + C::BM * C::BK;
+    const int k0 = kt * C::BK;
 #pragma unroll
-    for (int i = 0; i < kLoadIters; ++i) {
-      const int r = lrow + 32 * i;
-      ra[i] = *reinterpret_cast<const u32x4*>(gA + r * args.lda + kt * BK + lch * 8);
-      rb[i] = *reinterpret_cast<const u32x4*>(gB + r * args.ldb + kt * BK + lch * 8);
+    for (int i = 0; i < C::kDmaA; ++i) {
+      const int r0 = (i * C::kWaves + wave) * C::kRowsPerDma;
+      const int r = r0 + drow;
+      dma16(gA + r * args.lda + k0 + swz<C::BK>(r, dpc) * 8, as + r0 * C::BK);
     }
-  };
-  auto store_lds = [&](int buf) {
-    unsigned short* as = As + buf * BM * BK;
-    unsigned short* bs = Bs + buf * BN * BK;
 #pragma unroll
-    for (int i = 0; i < kLoadIters; ++i) {
-      const int r = lrow + 32 * i;
-      *reinterpret_cast<u32x4*>(as + r * BK + swz(r, lch) * 8) = ra[i];
-      *reinterpret_cast<u32x4*>(bs + r * BK + swz(r, lch) * 8) = rb[i];
+    for (int i = 0; i < C::kDmaB; ++i) {
+      const int r0 = (i * C::kWaves + wave) * C::kRowsPerDma;
+      const int r = r0 + drow;
+      dma16(gB + r * args.ldb + k0 + swz<C::BK>(r, dpc) * 8, bs + r0 * C::BK);
     }
   };
 
-  f32x16 acc[WTM][WTN];
+  f32x16 acc[C::WTM][C::WTN];
 #pragma unroll
-  for (int i = 0; i < WTM; ++i)
+  for (int i = 0; i < C::WTM; ++i)
 #pragma unroll
-    for (int j = 0; j < WTN; ++j)
+    for (int j = 0; j < C::WTN; ++j)
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
 
-  const int nk = args.kdim / BK;
-  load_global(0);
-  store_lds(0);
-  __syncthreads();
+  const int nk = args.kdim / C::BK;
+#pragma unroll
+  for (int s = 0; s < C::STAGES - 1; ++s)
+    if (s < nk) issue_stage(s, s);
 
-  const int frow = lane & 31;   // fragment row (A) / column (B)
-  const int fkh = lane >> 5;    // which 8-wide half of the 16-wide k slice
+  const int frow = lane & 31;  // fragment row (A) / column (B)
+  const int fkh = lane >> 5;   // which 8-wide half of a 16-wide k slice
 
   for (int kt = 0; kt < nk; ++kt) {
-    const int buf = kt & 1;
-    if (kt + 1 < nk) load_global(kt + 1);
-    const unsigned short* as = As + buf * BM * BK;
-    const unsigned short* bs = Bs + buf * BN * BK;
+    // stage kt must have landed; later stages may still be in flight
+    const int pending = min(C::STAGES - 2, nk - 1 - kt);
+    if constexpr (C::STAGES == 2) {
+      wait_vmcnt<0>();
+    } else {
+      if (pending >= 2) wait_vmcnt<2 * C::kDmaPerStage>();
+      else if (pending == 1) wait_vmcnt<C::kDmaPerStage>();
+      else wait_vmcnt<0>();
+    }
+    // Every wave's DMA for stage kt has landed (each waited on its own above) and every
+    // wave has finished reading slot (kt - 1).  A bare s_barrier: the release fence of
+    // __syncthreads() would also wait for the DMA of the later stages still in flight.
+    __builtin_amdgcn_s_barrier();
+    if (kt + C::STAGES - 1 < nk) issue_stage(kt + C::STAGES - 1, (kt + C::STAGES - 1) % C::STAGES);
+    const unsigned short* as = smem + (kt % C::STAGES) * C::kStageElems;
+    const unsigned short* bs = as + C::BM * C::BK;
 #pragma unroll
-    for (int kk = 0; kk < BK / 16; ++kk) {
-      bf16x8 af[WTM], bfr[WTN];
+    for (int kk = 0; kk < C::BK / 16; ++kk) {
+      bf16x8 af[C::WTM], bfr[C::WTN];
       const int ch = kk * 2 + fkh;
 #pragma unroll
-      for (int i = 0; i < WTM; ++i) {
-        const int r = wm * (WTM * 32) + i * 32 + frow;
-        af[i] = *reinterpret_cast<const bf16x8*>(as + r * BK + swz(r, ch) * 8);
+      for (int i = 0; i < C::WTM; ++i) {
+        const int r = wm * (C::WTM * 32) + i * 32 + frow;
+        af[i] = *reinterpret_cast<const bf16x8*>(as + r * C::BK + swz<C::BK>(r, ch) * 8);
       }
 #pragma unroll
-      for (int j = 0; j < WTN; ++j) {
-        const int r = wn * (WTN * 32) + j * 32 + frow;
-        bfr[j] = *reinterpret_cast<const bf16x8*>(bs + r * BK + swz(r, ch) * 8);
+      for (int j = 0; j < C::WTN; ++j) {
+        const int r = wn * (C::WTN * 32) + j * 32 + frow;
+        bfr[j] = *reinterpret_cast<const bf16x8*>(bs + r * C::BK + swz<C::BK>(r, ch) * 8);
       }
 #pragma unroll
-      for (int i = 0; i < WTM; ++i)
+      for (int i = 0; i < C::WTM; ++i)
 #pragma unroll
-        for (int j = 0; j < WTN; ++j)
+        for (int j = 0; j < C::WTN; ++j)
           acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
     }
-    if (kt + 1 < nk) store_lds(buf ^ 1);
-    __syncthreads();
   }
 
   // ---------------- epilogue ----------------
-  // MFMA 32x32 accumulator layout: lane holds column (lane & 31) of the tile and rows
-  // 8*(r/4) + 4*(lane/32) + r%4 for r = 0..15.
+  // MFMA 32x32 accumulator layout: lane holds column (lane & 31) of the 32x32 tile and
+  // rows 8*(r/4) + 4*(lane/32) + r%4 for r = 0..15, i.e. four runs of 4 rows.
+  // The a X / b R term is read from the transposed copy (X^T for combine; R is
+  // symmetric), where a lane's 4 consecutive rows are 8 contiguous bytes.
   const bool mirror = (kEpi != kCombine) && (ti != tj);
   const bool need_t = (kEpi == kCombine) || mirror;
-  unsigned short* Ts = smem;  // [BN][BM + kTPad], reused after the main loop
-  unsigned short* C = args.C + batch * args.strideC;
-  const unsigned short* aux =
+  constexpr int kTChunks = C::BM / 8;  // 16-byte chunks per row of the transposed tile
+  unsigned short* Ts = smem;           // [BN][BM], chunk c of row j at c ^ (j % kTChunks)
+  unsigned short* Cp = args.C + batch * args.strideC;
+  const unsigned short* auxT =
       (kEpi == kGram) ? nullptr : args.aux + batch * args.strideAux;
+  if (need_t) __syncthreads();  // every wave is done reading the operand stages
 
+  constexpr int kHalves = C::WTM >= 2 ? 2 : 1;  // aux loads in two batches (registers)
 #pragma unroll
-  for (int i = 0; i < WTM; ++i) {
+  for (int hh = 0; hh < kHalves; ++hh) {
+    constexpr int kI = C::WTM / kHalves;
+    u32x2 ax[kI][C::WTN][4];
+    if (kEpi != kGram) {
 #pragma unroll
-    for (int j = 0; j < WTN; ++j) {
-      const int jl = wn * (WTN * 32) + j * 32 + (lane & 31);
+      for (int ii = 0; ii < kI; ++ii)
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        unsigned short h[4];
+        for (int j = 0; j < C::WTN; ++j)
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int r = q * 4 + e;
-          const int il = wm * (WTM * 32) + i * 32 + 8 * q + 4 * fkh + e;
-          float v = acc[i][j][r];
-          const int64_t gi = m0 + il;
-          const int64_t gj = n0 + jl;
-          if (kEpi == kPoly) {
-            v = args.alpha * bf2f(aux[gi * args.ldaux + gj]) + args.beta * v;
-          } else if (kEpi == kCombine) {
-            v = args.alpha * bf2f(aux[gi * args.ldaux + gj]) + v;
+          for (int q = 0; q < 4; ++q) {
+            const int i = hh * kI + ii;
+            const int64_t gj = n0 + wn * (C::WTN * 32) + j * 32 + (lane & 31);
+            const int64_t gi0 = m0 + wm * (C::WTM * 32) + i * 32 + 8 * q + 4 * fkh;
+            ax[ii][j][q] = *reinterpret_cast<const u32x2*>(auxT + gj * args.ldaux + gi0);
           }
-          h[e] = f2bf(v);
-          C[gi * args.ldc + gj] = h[e];
-        }
-        if (need_t) {
-          const int il0 = wm * (WTM * 32) + i * 32 + 8 * q + 4 * fkh;
-          u32x2 packed;
-          packed[0] = static_cast<unsigned>(h[0]) | (static_cast<unsigned>(h[1]) << 16);
-          packed[1] = static_cast<unsigned>(h[2]) | (static_cast<unsigned>(h[3]) << 16);
-          // Ts is written only after every wave has left the main loop (the loop ends
-          // with a barrier), so reusing the operand buffers is safe.
-          *reinterpret_cast<u32x2*>(Ts + jl * (BM + kTPad) + il0) = packed;
+    }
+#pragma unroll
+    for (int ii = 0; ii < kI; ++ii) {
+      const int i = hh * kI + ii;
+#pragma unroll
+      for (int j = 0; j < C::WTN; ++j) {
+        const int jl = wn * (C::WTN * 32) + j * 32 + (lane & 31);
+        const int64_t gj = n0 + jl;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int il0 = wm * (C::WTM * 32) + i * 32 + 8 * q + 4 * fkh;
+          unsigned short h[4];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            float v = acc[i][j][q * 4 + e];
+            if (kEpi != kGram) {
+              const unsigned int w = ax[ii][j][q][e >> 1];
+              const float t = bf2f(static_cast<unsigned short>((e & 1) ? (w >> 16) : (w & 0xffffu)));
+              v = (kEpi == kPoly) ? args.alpha * t + args.beta * v : args.alpha * t + v;
+            }
+            h[e] = f2bf(v);
+            Cp[(m0 + il0 + e) * args.ldc + gj] = h[e];
+          }
+          if (need_t) {
+            u32x2 packed;
+            packed[0] = static_cast<unsigned>(h[0]) | (static_cast<unsigned>(h[1]) << 16);
+            packed[1] = static_cast<unsigned>(h[2]) | (static_cast<unsigned>(h[3]) << 16);
+            const int c = il0 >> 3, half = (il0 >> 2) & 1;
+            *reinterpret_cast<u32x2*>(Ts + jl * C::BM + ((c ^ (jl % kTChunks)) * 8) + half * 4) = packed;
+          }
         }
       }
     }
@@ -205,38 +287,63 @@ __global__ __launch_bounds__(kThreads, 2) void ns_gemm_kernel(GemmArgs args) {
   if (!need_t) return;
   __syncthreads();
   unsigned short* C2 = args.C2 + batch * args.strideC2;
-  constexpr int kChunks = BN * (BM / 8);  // 16-byte chunks in the transposed tile
+  constexpr int kAll = C::BN * kTChunks;
+  static_assert(kAll % C::kThreads == 0, "epilogue copy");
 #pragma unroll
-  for (int it = 0; it < kChunks / kThreads; ++it) {
-    const int idx = tid + it * kThreads;
-    const int row = idx / (BM / 8);  // local column j of the product
-    const int ch = idx - row * (BM / 8);
-    const u32x4 v = *reinterpret_cast<const u32x4*>(Ts + row * (BM + kTPad) + ch * 8);
-    *reinterpret_cast<u32x4*>(C2 + (n0 + row) * args.ldc2 + m0 + ch * 8) = v;
+  for (int it = 0; it < kAll / C::kThreads; ++it) {
+    const int idx = tid + it * C::kThreads;
+    const int row = idx / kTChunks;  // local column j of the product
+    const int c = idx - row * kTChunks;
+    const u32x4 v = *reinterpret_cast<const u32x4*>(Ts + row * C::BM + ((c ^ (row % kTChunks)) * 8));
+    *reinterpret_cast<u32x4*>(C2 + (n0 + row) * args.ldc2 + m0 + c * 8) = v;
   }
 }
 
-static_assert(2 * 2 * BM * BK >= BN * (BM + kTPad), "epilogue tile must fit the operand buffers");
-static_assert(((BM + kTPad) * 2) % 16 == 0, "transpose tile rows must stay 16-byte aligned");
+// Tile shapes.  Big: 256 x 256 per block, 8 waves of 128 x 64, 4 stages of k = 32
+// (128 KiB LDS, one block per CU).  Small: 128 x 128, 4 waves of 64 x 64, 2 stages of
+// k = 64 (64 KiB, two blocks per CU) for Gram sides too short to fill the chip.
+using BigCfg = Cfg<256, 256, 32, 2, 4, 4>;
+using SmallCfg = Cfg<128, 128, 64, 2, 2, 2>;
 
-hipError_t launch(int epi, const GemmArgs& a, int64_t K, hipStream_t s) {
+template <class C>
+hipError_t launch_cfg(int epi, const GemmArgs& a, int64_t K, hipStream_t s) {
   const int64_t blocks = K * a.tiles_per_batch;
   if (blocks <= 0) return hipSuccess;
   const dim3 grid(static_cast<unsigned>(blocks));
   switch (epi) {
-    case kGram: hipLaunchKernelGGL((ns_gemm_kernel<kGram>), grid, dim3(kThreads), 0, s, a); break;
-    case kPoly: hipLaunchKernelGGL((ns_gemm_kernel<kPoly>), grid, dim3(kThreads), 0, s, a); break;
-    default: hipLaunchKernelGGL((ns_gemm_kernel<kCombine>), grid, dim3(kThreads), 0, s, a); break;
+    case kGram: hipLaunchKernelGGL((ns_gemm_kernel<C, kGram>), grid, dim3(C::kThreads), 0, s, a); break;
+    case kPoly: hipLaunchKernelGGL((ns_gemm_kernel<C, kPoly>), grid, dim3(C::kThreads), 0, s, a); break;
+    default: hipLaunchKernelGGL((ns_gemm_kernel<C, kCombine>), grid, dim3(C::kThreads), 0, s, a); break;
   }
   return hipGetLastError();
 }
 
+hipError_t launch(int epi, GemmArgs a, const BucketPlan& p, hipStream_t s) {
+  const int T = p.tile;
+  if (epi == kCombine) {
+    a.tiles_m = static_cast<int>(p.m_pad / T);
+    a.tiles_n = static_cast<int>(p.n_pad / T);
+    a.tiles_per_batch = a.tiles_m * a.tiles_n;
+  } else {
+    a.tiles_m = a.tiles_n = static_cast<int>(p.m_pad / T);
+    a.tiles_per_batch = a.tiles_m * (a.tiles_m + 1) / 2;
+  }
+  if (T == BigCfg::BM) return launch_cfg<BigCfg>(epi, a, p.K, s);
+  return launch_cfg<SmallCfg>(epi, a, p.K, s);
+}
+
 }  // namespace
+
+int pick_tile(int64_t K, int64_t m, int64_t n) {
+  // 256-tiles once the batch of combine tiles fills the chip twice over at one block
+  // per CU; smaller problems keep 128-tiles (two blocks per CU, 4x the blocks).
+  const int64_t m256 = (m + 255) / 256, n256 = (n + 255) / 256;
+  return (K * m256 * n256 >= 512 && m >= 512) ? BigCfg::BM : SmallCfg::BM;
+}
 
 hipError_t launch_gram(const BucketPlan& p, const unsigned short* X, unsigned short* R,
                        hipStream_t s) {
   GemmArgs a{};
-  const int T = static_cast<int>(p.m_pad / BM);
   a.A = X; a.B = X;
   a.lda = a.ldb = p.n_pad;
   a.strideA = a.strideB = p.m_pad * p.n_pad;
@@ -244,15 +351,12 @@ hipError_t launch_gram(const BucketPlan& p, const unsigned short* X, unsigned sh
   a.C = R; a.C2 = R;
   a.ldc = a.ldc2 = p.m_pad;
   a.strideC = a.strideC2 = p.m_pad * p.m_pad;
-  a.tiles_m = a.tiles_n = T;
-  a.tiles_per_batch = T * (T + 1) / 2;
-  return launch(kGram, a, p.K, s);
+  return launch(kGram, a, p, s);
 }
 
 hipError_t launch_poly(const BucketPlan& p, const unsigned short* R, unsigned short* P,
                        float b, float c, hipStream_t s) {
   GemmArgs a{};
-  const int T = static_cast<int>(p.m_pad / BM);
   a.A = R; a.B = R;
   a.lda = a.ldb = p.m_pad;
   a.strideA = a.strideB = p.m_pad * p.m_pad;
@@ -264,9 +368,7 @@ hipError_t launch_poly(const BucketPlan& p, const unsigned short* R, unsigned sh
   a.ldaux = p.m_pad;
   a.strideAux = p.m_pad * p.m_pad;
   a.alpha = b; a.beta = c;
-  a.tiles_m = a.tiles_n = T;
-  a.tiles_per_batch = T * (T + 1) / 2;
-  return launch(kPoly, a, p.K, s);
+  return launch(kPoly, a, p, s);
 }
 
 hipError_t launch_combine(const BucketPlan& p, const unsigned short* P,
@@ -281,14 +383,11 @@ hipError_t launch_combine(const BucketPlan& p, const unsigned short* P,
   a.C = Xn; a.C2 = XTn;
   a.ldc = p.n_pad; a.ldc2 = p.m_pad;
   a.strideC = a.strideC2 = p.m_pad * p.n_pad;
-  a.aux = X;
-  a.ldaux = p.n_pad;
+  a.aux = XT;  // X[i][j] read as X^T[j][i]
+  a.ldaux = p.m_pad;
   a.strideAux = p.m_pad * p.n_pad;
   a.alpha = alpha; a.beta = 1.0f;
-  a.tiles_m = static_cast<int>(p.m_pad / BM);
-  a.tiles_n = static_cast<int>(p.n_pad / BN);
-  a.tiles_per_batch = a.tiles_m * a.tiles_n;
-  return launch(kCombine, a, p.K, s);
+  return launch(kCombine, a, p, s);
 }
 
 }  // namespace ma
