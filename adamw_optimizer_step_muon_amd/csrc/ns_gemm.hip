@@ -33,6 +33,8 @@
 //     an XOR-swizzled LDS tile with 16-byte stores.
 // Sizes are padded to the tile by the caller and the padding is zero (preserved by
 // the iteration), so there are no bounds checks inside.
+#include <cstdlib>
+
 #include "ma_internal.h"
 
 namespace ma {
@@ -78,11 +80,14 @@ struct Cfg {
   static_assert(kLdsElems * 2 <= 160 * 1024, "LDS");
 };
 
-// 16-byte chunk swizzle inside an operand row (an involution in c).
+// 16-byte chunk swizzle inside an operand row (an involution in c).  A fragment read
+// has 32 lanes on 32 consecutive rows at one logical chunk; the swizzle spreads every
+// 16 lanes over 16 distinct 16-byte slots of a 256-byte bank row (and every 8 lanes
+// over the 8 slots of 128 bytes), so the b128 reads are free of bank conflicts.
 template <int BK>
 __device__ __forceinline__ int swz(int r, int c) {
-  if constexpr (BK == 64) return c ^ (r & 7);         // 8 chunks: 8 rows -> 8 slots
-  else return c ^ ((r >> 1) & 3);                     // 4 chunks: row pairs fill the banks
+  if constexpr (BK == 64) return c ^ ((r ^ (r >> 3)) & 7);         // 8 chunks per row
+  else return c ^ (((r >> 1) ^ (r >> 3)) & 3);                     // 4 chunks per row
 }
 
 // wait until at most n vector-memory operations of this wave are outstanding
@@ -173,6 +178,8 @@ __global__ __launch_bounds__(C::kThreads) void ns_gemm_kernel(GemmArgs args) {
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
 
   const int nk = args.kdim / C::BK;
+  constexpr int KK = C::BK / 16;  // MFMA k-slices per stage
+  constexpr int L = C::kDmaPerStage;
 #pragma unroll
   for (int s = 0; s < C::STAGES - 1; ++s)
     if (s < nk) issue_stage(s, s);
@@ -180,42 +187,69 @@ __global__ __launch_bounds__(C::kThreads) void ns_gemm_kernel(GemmArgs args) {
   const int frow = lane & 31;  // fragment row (A) / column (B)
   const int fkh = lane >> 5;   // which 8-wide half of a 16-wide k slice
 
-  for (int kt = 0; kt < nk; ++kt) {
-    // stage kt must have landed; later stages may still be in flight
-    const int pending = min(C::STAGES - 2, nk - 1 - kt);
-    if constexpr (C::STAGES == 2) {
-      wait_vmcnt<0>();
-    } else {
-      if (pending >= 2) wait_vmcnt<2 * C::kDmaPerStage>();
-      else if (pending == 1) wait_vmcnt<C::kDmaPerStage>();
-      else wait_vmcnt<0>();
+  // wait until stage `st` has landed: the stages issued after it may stay in flight
+  auto wait_stage = [&](int st) {
+    const int pending = min(C::STAGES - 2, nk - 1 - st);
+    if constexpr (C::STAGES >= 4) {
+      if (pending >= 2) { wait_vmcnt<2 * L>(); return; }
     }
-    // Every wave's DMA for stage kt has landed (each waited on its own above) and every
-    // wave has finished reading slot (kt - 1).  A bare s_barrier: the release fence of
-    // __syncthreads() would also wait for the DMA of the later stages still in flight.
-    __builtin_amdgcn_s_barrier();
-    if (kt + C::STAGES - 1 < nk) issue_stage(kt + C::STAGES - 1, (kt + C::STAGES - 1) % C::STAGES);
-    const unsigned short* as = smem + (kt % C::STAGES) * C::kStageElems;
+    if constexpr (C::STAGES >= 3) {
+      if (pending >= 1) { wait_vmcnt<L>(); return; }
+    }
+    wait_vmcnt<0>();
+  };
+  auto load_frags = [&](int slot, int kk, bf16x8 (&af)[C::WTM], bf16x8 (&bfr)[C::WTN]) {
+    const unsigned short* as = smem + slot * C::kStageElems;
     const unsigned short* bs = as + C::BM * C::BK;
+    const int ch = kk * 2 + fkh;
 #pragma unroll
-    for (int kk = 0; kk < C::BK / 16; ++kk) {
-      bf16x8 af[C::WTM], bfr[C::WTN];
-      const int ch = kk * 2 + fkh;
+    for (int i = 0; i < C::WTM; ++i) {
+      const int r = wm * (C::WTM * 32) + i * 32 + frow;
+      af[i] = *reinterpret_cast<const bf16x8*>(as + r * C::BK + swz<C::BK>(r, ch) * 8);
+    }
 #pragma unroll
-      for (int i = 0; i < C::WTM; ++i) {
-        const int r = wm * (C::WTM * 32) + i * 32 + frow;
-        af[i] = *reinterpret_cast<const bf16x8*>(as + r * C::BK + swz<C::BK>(r, ch) * 8);
-      }
+    for (int j = 0; j < C::WTN; ++j) {
+      const int r = wn * (C::WTN * 32) + j * 32 + frow;
+      bfr[j] = *reinterpret_cast<const bf16x8*>(bs + r * C::BK + swz<C::BK>(r, ch) * 8);
+    }
+  };
+
+  // Fragments are double-buffered: the LDS reads of k-slice kk+1 are issued before the
+  // MFMAs of slice kk, and across a stage boundary the barrier wait and the first
+  // reads of the next stage sit before the MFMAs of the last slice, so the matrix
+  // cores keep working while the block synchronises.
+  bf16x8 fa[2][C::WTM], fb[2][C::WTN];
+  wait_stage(0);
+  __builtin_amdgcn_s_barrier();
+  load_frags(0, 0, fa[0], fb[0]);
+  for (int kt = 0; kt < nk; ++kt) {
+    const int slot = kt % C::STAGES;
+    // slot (kt - 1) % STAGES was last read before the barrier that preceded this stage
+    if (kt + C::STAGES - 1 < nk) issue_stage(kt + C::STAGES - 1, (kt + C::STAGES - 1) % C::STAGES);
 #pragma unroll
-      for (int j = 0; j < C::WTN; ++j) {
-        const int r = wn * (C::WTN * 32) + j * 32 + frow;
-        bfr[j] = *reinterpret_cast<const bf16x8*>(bs + r * C::BK + swz<C::BK>(r, ch) * 8);
+    for (int kk = 0; kk < KK; ++kk) {
+      const int cur = kk & 1;
+      if (kk + 1 < KK) {
+        load_frags(slot, kk + 1, fa[cur ^ 1], fb[cur ^ 1]);
+      } else if (kt + 1 < nk) {
+        // every wave's reads of this stage are done and stage kt+1 has landed
+        __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0), vmcnt and expcnt untouched
+        wait_stage(kt + 1);
+        __builtin_amdgcn_s_barrier();
+        load_frags((kt + 1) % C::STAGES, 0, fa[cur ^ 1], fb[cur ^ 1]);
       }
 #pragma unroll
       for (int i = 0; i < C::WTM; ++i)
 #pragma unroll
         for (int j = 0; j < C::WTN; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[cur][i], fb[cur][j], acc[i][j], 0, 0, 0);
+    }
+    if constexpr ((KK & 1) == 1) {
+      // odd slice count: the next stage's first fragments landed in buffer 1
+#pragma unroll
+      for (int i = 0; i < C::WTM; ++i) fa[0][i] = fa[1][i];
+#pragma unroll
+      for (int j = 0; j < C::WTN; ++j) fb[0][j] = fb[1][j];
     }
   }
 
@@ -299,10 +333,15 @@ __global__ __launch_bounds__(C::kThreads) void ns_gemm_kernel(GemmArgs args) {
   }
 }
 
-// Tile shapes.  Big: 256 x 256 per block, 8 waves of 128 x 64, 4 stages of k = 32
-// (128 KiB LDS, one block per CU).  Small: 128 x 128, 4 waves of 64 x 64, 2 stages of
-// k = 64 (64 KiB, two blocks per CU) for Gram sides too short to fill the chip.
-using BigCfg = Cfg<256, 256, 32, 2, 4, 4>;
+// Tile shapes.  Big: 256 x 256 per block (128 KiB LDS, one block per CU); the default
+// runs 8 waves of 128 x 64 over 2 stages of k = 64 (one barrier per 64 of k).  Small:
+// 128 x 128, 4 waves of 64 x 64, 2 stages of k = 64 (64 KiB, two blocks per CU) for
+// Gram sides too short to fill the chip.  Other big variants stay compiled for tuning
+// (MA_NS_BIG=1: 4 waves k=32 x 4 stages, 2: 4 waves k=64 x 2, 3: 8 waves k=32 x 4).
+using Big8K64 = Cfg<256, 256, 64, 2, 4, 2>;
+using Big4 = Cfg<256, 256, 32, 2, 2, 4>;
+using Big4K64 = Cfg<256, 256, 64, 2, 2, 2>;
+using Big8 = Cfg<256, 256, 32, 2, 4, 4>;
 using SmallCfg = Cfg<128, 128, 64, 2, 2, 2>;
 
 template <class C>
@@ -318,6 +357,14 @@ hipError_t launch_cfg(int epi, const GemmArgs& a, int64_t K, hipStream_t s) {
   return hipGetLastError();
 }
 
+int big_variant() {
+  static const int v = [] {
+    const char* e = std::getenv("MA_NS_BIG");
+    return e ? std::atoi(e) : 0;
+  }();
+  return v;
+}
+
 hipError_t launch(int epi, GemmArgs a, const BucketPlan& p, hipStream_t s) {
   const int T = p.tile;
   if (epi == kCombine) {
@@ -328,7 +375,14 @@ hipError_t launch(int epi, GemmArgs a, const BucketPlan& p, hipStream_t s) {
     a.tiles_m = a.tiles_n = static_cast<int>(p.m_pad / T);
     a.tiles_per_batch = a.tiles_m * (a.tiles_m + 1) / 2;
   }
-  if (T == BigCfg::BM) return launch_cfg<BigCfg>(epi, a, p.K, s);
+  if (T == 256) {
+    switch (big_variant()) {
+      case 1: return launch_cfg<Big4>(epi, a, p.K, s);
+      case 2: return launch_cfg<Big4K64>(epi, a, p.K, s);
+      case 3: return launch_cfg<Big8>(epi, a, p.K, s);
+      default: return launch_cfg<Big8K64>(epi, a, p.K, s);
+    }
+  }
   return launch_cfg<SmallCfg>(epi, a, p.K, s);
 }
 
@@ -338,7 +392,7 @@ int pick_tile(int64_t K, int64_t m, int64_t n) {
   // 256-tiles once the batch of combine tiles fills the chip twice over at one block
   // per CU; smaller problems keep 128-tiles (two blocks per CU, 4x the blocks).
   const int64_t m256 = (m + 255) / 256, n256 = (n + 255) / 256;
-  return (K * m256 * n256 >= 512 && m >= 512) ? BigCfg::BM : SmallCfg::BM;
+  return (K * m256 * n256 >= 512 && m >= 512) ? 256 : SmallCfg::BM;
 }
 
 hipError_t launch_gram(const BucketPlan& p, const unsigned short* X, unsigned short* R,
