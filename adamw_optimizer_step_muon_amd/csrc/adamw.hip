@@ -10,13 +10,14 @@
 // One pass: 16 bytes read and 12 written per element (p, g, m, v in; p, m, v out),
 // no other traffic.  Each thread moves kUnroll float4 groups with all loads issued
 // before any arithmetic, so a wave keeps 4 x kUnroll x 1 KiB in flight.
+#include <cstdlib>
+
 #include "ma_internal.h"
 
 namespace ma {
 namespace {
 
 constexpr int kThreads = 256;
-constexpr int kUnroll = 4;
 
 __device__ __forceinline__ void adamw_elem(float& p, float g, float& m, float& v,
                                            const AdamWConst& c) {
@@ -33,37 +34,55 @@ __device__ __forceinline__ void adamw_elem(float& p, float g, float& m, float& v
   p = p - c.lr * upd;
 }
 
+template <typename T>
+__device__ __forceinline__ T ld(const T* q, bool nt) {
+  return nt ? __builtin_nontemporal_load(q) : *q;
+}
+template <typename T>
+__device__ __forceinline__ void st(T* q, T v, bool nt) {
+  if (nt) __builtin_nontemporal_store(v, q);
+  else *q = v;
+}
+
+// kU float4 groups per thread, all loads issued before any arithmetic; kNt: streaming
+// (non-temporal) loads and stores for every array; kPersistent: a grid-stride loop
+// over a grid sized to the chip instead of one block per kThreads * kU groups.
+template <int kU, bool kNt, bool kPersistent>
 __global__ __launch_bounds__(kThreads) void adamw_vec_kernel(
     f32x4* __restrict__ p, const f32x4* __restrict__ g, f32x4* __restrict__ m,
     f32x4* __restrict__ v, int64_t n4, AdamWConst c) {
-  const int64_t base = static_cast<int64_t>(blockIdx.x) * (kThreads * kUnroll) + threadIdx.x;
-  f32x4 P[kUnroll], G[kUnroll], M[kUnroll], V[kUnroll];
+  const int64_t stride = kPersistent ? static_cast<int64_t>(gridDim.x) * (kThreads * kU) : 0;
+  for (int64_t base = static_cast<int64_t>(blockIdx.x) * (kThreads * kU) + threadIdx.x;
+       base < n4; base += stride) {
+    f32x4 P[kU], G[kU], M[kU], V[kU];
 #pragma unroll
-  for (int u = 0; u < kUnroll; ++u) {
-    const int64_t i = base + static_cast<int64_t>(u) * kThreads;
-    if (i < n4) {
-      P[u] = p[i];
-      G[u] = __builtin_nontemporal_load(&g[i]);
-      M[u] = m[i];
-      V[u] = v[i];
-    }
-  }
-#pragma unroll
-  for (int u = 0; u < kUnroll; ++u) {
-    const int64_t i = base + static_cast<int64_t>(u) * kThreads;
-    if (i < n4) {
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        float pe = P[u][e], me = M[u][e], ve = V[u][e];
-        adamw_elem(pe, G[u][e], me, ve, c);
-        P[u][e] = pe;
-        M[u][e] = me;
-        V[u][e] = ve;
+    for (int u = 0; u < kU; ++u) {
+      const int64_t i = base + static_cast<int64_t>(u) * kThreads;
+      if (i < n4) {
+        P[u] = ld(&p[i], kNt);
+        G[u] = ld(&g[i], true);
+        M[u] = ld(&m[i], kNt);
+        V[u] = ld(&v[i], kNt);
       }
-      p[i] = P[u];
-      m[i] = M[u];
-      v[i] = V[u];
     }
+#pragma unroll
+    for (int u = 0; u < kU; ++u) {
+      const int64_t i = base + static_cast<int64_t>(u) * kThreads;
+      if (i < n4) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          float pe = P[u][e], me = M[u][e], ve = V[u][e];
+          adamw_elem(pe, G[u][e], me, ve, c);
+          P[u][e] = pe;
+          M[u][e] = me;
+          V[u][e] = ve;
+        }
+        st(&p[i], P[u], kNt);
+        st(&m[i], M[u], kNt);
+        st(&v[i], V[u], kNt);
+      }
+    }
+    if (!kPersistent) break;
   }
 }
 
@@ -81,6 +100,28 @@ __global__ __launch_bounds__(kThreads) void adamw_scalar_kernel(
 
 bool aligned16(const void* q) { return (reinterpret_cast<uintptr_t>(q) & 15u) == 0; }
 
+
+template <int kU, bool kNt, bool kPersistent>
+hipError_t launch_vec(float* p, const float* g, float* m, float* v, int64_t n4,
+                      const AdamWConst& c, hipStream_t s) {
+  const int64_t per_block = static_cast<int64_t>(kThreads) * kU;
+  int64_t blocks = (n4 + per_block - 1) / per_block;
+  if (kPersistent && blocks > 256 * 16) blocks = 256 * 16;
+  hipLaunchKernelGGL((adamw_vec_kernel<kU, kNt, kPersistent>), dim3(static_cast<unsigned>(blocks)),
+                     dim3(kThreads), 0, s, reinterpret_cast<f32x4*>(p),
+                     reinterpret_cast<const f32x4*>(g), reinterpret_cast<f32x4*>(m),
+                     reinterpret_cast<f32x4*>(v), n4, c);
+  return hipGetLastError();
+}
+
+int adamw_variant() {
+  static const int v = [] {
+    const char* e = std::getenv("MA_ADAMW_VARIANT");  // tuning override
+    return e ? std::atoi(e) : 0;
+  }();
+  return v;
+}
+
 }  // namespace
 
 hipError_t launch_adamw(float* p, const float* g, float* m, float* v, int64_t n,
@@ -90,12 +131,14 @@ hipError_t launch_adamw(float* p, const float* g, float* m, float* v, int64_t n,
   if (aligned16(p) && aligned16(g) && aligned16(m) && aligned16(v)) {
     const int64_t n4 = n / 4;
     if (n4 > 0) {
-      const int64_t per_block = static_cast<int64_t>(kThreads) * kUnroll;
-      const int64_t blocks = (n4 + per_block - 1) / per_block;
-      hipLaunchKernelGGL(adamw_vec_kernel, dim3(static_cast<unsigned>(blocks)), dim3(kThreads),
-                         0, s, reinterpret_cast<f32x4*>(p), reinterpret_cast<const f32x4*>(g),
-                         reinterpret_cast<f32x4*>(m), reinterpret_cast<f32x4*>(v), n4, c);
-      hipError_t e = hipGetLastError();
+      hipError_t e;
+      switch (adamw_variant()) {
+        // default: 4 groups per thread, streaming loads and stores (at the copy ceiling)
+        case 1: e = launch_vec<4, false, false>(p, g, m, v, n4, c, s); break;
+        case 2: e = launch_vec<2, true, false>(p, g, m, v, n4, c, s); break;
+        case 3: e = launch_vec<4, true, true>(p, g, m, v, n4, c, s); break;
+        default: e = launch_vec<4, true, false>(p, g, m, v, n4, c, s); break;
+      }
       if (e != hipSuccess) return e;
       done = n4 * 4;
     }

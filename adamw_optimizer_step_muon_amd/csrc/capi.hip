@@ -83,7 +83,7 @@ ma_status check_shape(int64_t K, int64_t A, int64_t B) {
   // grid limits: (nblk, K) and (Bp/64, Ap/64, K) launches, K x tiles GEMM launches
   const BucketPlan p = plan_bucket(K, A, B);
   const int64_t tiles = (p.m_pad / p.tile) * (p.n_pad / p.tile);
-  if (K > 65535 || p.nblk > kMaxBlocks || K * tiles > kMaxBlocks ||
+  if (K > 65535 || K * p.nblk > kMaxBlocks || K * tiles > kMaxBlocks ||
       K * A * B / 4 / 256 > kMaxBlocks)
     return fail(MA_ERR_UNSUPPORTED, "bucket (%lld, %lld, %lld) exceeds the launch grid",
                 (long long)K, (long long)A, (long long)B);
@@ -101,30 +101,36 @@ ma_muon_route route_of(const BucketPlan& p, int ns_steps) {
   return r;
 }
 
-// Runs Newton-Schulz on the cast X0/XT0 of a bucket; returns the buffer that holds the
-// result in the matrix's own orientation (and its row stride).
+// Runs Newton-Schulz on a bucket whose unnormalised bf16 U sits in X[0] / XT[0] and
+// whose normalisers inv[k] = 1 / (||U_k|| + eps) are in the workspace; returns the
+// buffer holding the result in the matrix's own orientation, its row stride, and the
+// per-matrix factor still to apply to it (inv when no iteration ran, else none).
 ma_status run_ns(const BucketPlan& p, const ma_muon_hparams* hp, char* ws, hipStream_t s,
-                 const unsigned short** out, int64_t* ldo) {
+                 const unsigned short** out, int64_t* ldo, const float** oscale) {
   unsigned short* X[2] = {reinterpret_cast<unsigned short*>(ws + p.off_x[0]),
                           reinterpret_cast<unsigned short*>(ws + p.off_x[1])};
   unsigned short* XT[2] = {reinterpret_cast<unsigned short*>(ws + p.off_xt[0]),
                            reinterpret_cast<unsigned short*>(ws + p.off_xt[1])};
   unsigned short* R = reinterpret_cast<unsigned short*>(ws + p.off_r);
   unsigned short* P = reinterpret_cast<unsigned short*>(ws + p.off_p);
+  const float* inv = reinterpret_cast<const float*>(ws + p.off_inv);
   int cur = 0;
   for (int it = 0; it < hp->ns_steps; ++it) {
     const NsCoeffs c = coeff_at(hp, it);
-    hipError_t e = launch_gram(p, X[cur], R, s);
+    // the first iteration applies the normalisation X0 = inv U inside its products
+    const float* sc = it == 0 ? inv : nullptr;
+    hipError_t e = launch_gram(p, X[cur], R, sc, s);
     if (e != hipSuccess) return hip_fail(e, "gram launch");
     e = launch_poly(p, R, P, c.b, c.c, s);
     if (e != hipSuccess) return hip_fail(e, "poly launch");
-    e = launch_combine(p, P, X[cur], XT[cur], c.a, X[cur ^ 1], XT[cur ^ 1], s);
+    e = launch_combine(p, P, X[cur], XT[cur], c.a, X[cur ^ 1], XT[cur ^ 1], sc, s);
     if (e != hipSuccess) return hip_fail(e, "combine launch");
     cur ^= 1;
   }
   // Own orientation: X (m_pad x n_pad) when not transposed, X^T (n_pad x m_pad) when it is.
   *out = p.transposed ? XT[cur] : X[cur];
   *ldo = p.transposed ? p.m_pad : p.n_pad;
+  *oscale = hp->ns_steps == 0 ? inv : nullptr;
   return MA_OK;
 }
 
@@ -145,8 +151,7 @@ BucketPlan plan_bucket(int64_t K, int64_t A, int64_t B) {
   }
   p.m_pad = round_up(p.m, p.tile);
   p.n_pad = round_up(p.n, p.tile);
-  p.nblk = (A * B + kPrepChunk - 1) / kPrepChunk;
-  if (p.nblk < 1) p.nblk = 1;
+  p.nblk = (p.m_pad / kCastTile) * (p.n_pad / kCastTile);
   const size_t xb = static_cast<size_t>(K * p.m_pad * p.n_pad) * 2;
   const size_t rb = static_cast<size_t>(K * p.m_pad * p.m_pad) * 2;
   size_t off = 0;
@@ -274,22 +279,22 @@ ma_status ma_muon_step(const ma_muon_bucket* buckets, int32_t n_buckets,
     float* inv = reinterpret_cast<float*>(ws + p.off_inv);
     unsigned short* S = reinterpret_cast<unsigned short*>(ws + (p.transposed ? p.off_xt[0] : p.off_x[0]));
     unsigned short* T = reinterpret_cast<unsigned short*>(ws + (p.transposed ? p.off_x[0] : p.off_xt[0]));
-    hipError_t e = launch_muon_prep(p, b.grad, b.momentum, hp->momentum, hp->nesterov, partials, s);
+    hipError_t e = launch_muon_prep(p, b.grad, b.momentum, hp->momentum, hp->nesterov, partials,
+                                    S, T, s);
     if (e != hipSuccess) return hip_fail(e, "momentum launch");
     e = launch_norm_finalize(p, partials, hp->ns_eps, inv, s);
     if (e != hipSuccess) return hip_fail(e, "norm launch");
-    e = launch_norm_cast(p, b.grad, b.momentum, hp->momentum, hp->nesterov, inv, S, T, s);
-    if (e != hipSuccess) return hip_fail(e, "cast launch");
     const unsigned short* O = nullptr;
+    const float* oscale = nullptr;
     int64_t ldo = 0;
-    st = run_ns(p, hp, ws, s, &O, &ldo);
+    st = run_ns(p, hp, ws, s, &O, &ldo, &oscale);
     if (st != MA_OK) return st;
     const double big = static_cast<double>(b.A > b.B ? b.A : b.B);
     const double scale = hp->scale_mode == 0
                              ? 0.2 * std::sqrt(big)
                              : std::sqrt(std::fmax(1.0, static_cast<double>(b.A) / static_cast<double>(b.B)));
-    e = launch_muon_apply(p, b.param, O, ldo, hp->lr, hp->weight_decay, static_cast<float>(scale),
-                          hp->cautious_wd, s);
+    e = launch_muon_apply(p, b.param, O, oscale, ldo, hp->lr, hp->weight_decay,
+                          static_cast<float>(scale), hp->cautious_wd, s);
     if (e != hipSuccess) return hip_fail(e, "apply launch");
   }
   return MA_OK;
@@ -327,17 +332,16 @@ ma_status ma_newton_schulz(const float* in, float* out, int64_t K, int64_t A, in
   float* inv = reinterpret_cast<float*>(ws + p.off_inv);
   unsigned short* S = reinterpret_cast<unsigned short*>(ws + (p.transposed ? p.off_xt[0] : p.off_x[0]));
   unsigned short* T = reinterpret_cast<unsigned short*>(ws + (p.transposed ? p.off_x[0] : p.off_xt[0]));
-  hipError_t e = launch_muon_prep(p, in, nullptr, 0.0f, 0, partials, s);
-  if (e != hipSuccess) return hip_fail(e, "norm partials launch");
+  hipError_t e = launch_muon_prep(p, in, nullptr, 0.0f, 0, partials, S, T, s);
+  if (e != hipSuccess) return hip_fail(e, "cast launch");
   e = launch_norm_finalize(p, partials, hp->ns_eps, inv, s);
   if (e != hipSuccess) return hip_fail(e, "norm launch");
-  e = launch_norm_cast(p, in, nullptr, 0.0f, 0, inv, S, T, s);
-  if (e != hipSuccess) return hip_fail(e, "cast launch");
   const unsigned short* O = nullptr;
+  const float* oscale = nullptr;
   int64_t ldo = 0;
-  st = run_ns(p, hp, ws, s, &O, &ldo);
+  st = run_ns(p, hp, ws, s, &O, &ldo, &oscale);
   if (st != MA_OK) return st;
-  e = launch_ns_extract(p, out, O, ldo, s);
+  e = launch_ns_extract(p, out, O, oscale, ldo, s);
   if (e != hipSuccess) return hip_fail(e, "extract launch");
   return MA_OK;
 }

@@ -29,15 +29,14 @@ __device__ __forceinline__ float bf2f(unsigned short h) {
 // ---------------------------------------------------------------------------
 // Workspace layout of one Muon bucket (bf16 buffers, tile-padded)
 // ---------------------------------------------------------------------------
-constexpr int kCastTile = 64;     // normalise/cast kernel tile
-constexpr int kPrepChunk = 16384; // elements per momentum/norm block
+constexpr int kCastTile = 64;     // momentum/cast kernel tile
 
 struct BucketPlan {
   int64_t K, A, B;
   bool transposed;
   int tile;  // square GEMM tile (128 or 256); m and n are padded to it
   int64_t m, n, m_pad, n_pad;
-  int64_t nblk;  // momentum/norm blocks per matrix
+  int64_t nblk;  // momentum/cast tiles per matrix (one partial sum of U^2 each)
   // byte offsets inside the workspace
   size_t off_x[2], off_xt[2], off_r, off_p, off_part, off_inv, bytes;
 };
@@ -53,34 +52,35 @@ struct NsCoeffs {
   float a, b, c;
 };
 
-// M <- mu M + G (when M != nullptr), U = G + mu M_new | M_new | G; per-block sum of U^2.
+// M <- mu M + G (when M != nullptr), U = G + mu M_new | M_new | G, cast to bf16 as the
+// orientation copy S (Ap x Bp) and transposed copy T (Bp x Ap), zero in the padding;
+// per-tile sums of U^2.
 hipError_t launch_muon_prep(const BucketPlan& p, const float* G, float* M, float mu,
-                            int nesterov, float* partials, hipStream_t s);
+                            int nesterov, float* partials, unsigned short* S,
+                            unsigned short* T, hipStream_t s);
 // inv[k] = 1 / (sqrt(sum of partials of matrix k) + eps)
 hipError_t launch_norm_finalize(const BucketPlan& p, const float* partials, float eps,
                                 float* inv, hipStream_t s);
-// X0 = U * inv[k] in bf16: orientation copy S (Ap x Bp) and transposed copy T (Bp x Ap),
-// zero in the padding.
-hipError_t launch_norm_cast(const BucketPlan& p, const float* G, const float* M, float mu,
-                            int nesterov, const float* inv, unsigned short* S,
-                            unsigned short* T, hipStream_t s);
-// R = X X^T (lower-triangle tiles, mirrored)
+// R = X X^T (lower-triangle tiles, mirrored); R *= scale[k]^2 when scale is given
 hipError_t launch_gram(const BucketPlan& p, const unsigned short* X, unsigned short* R,
-                       hipStream_t s);
+                       const float* scale, hipStream_t s);
 // P = b R + c R R^T (lower-triangle tiles, mirrored)
 hipError_t launch_poly(const BucketPlan& p, const unsigned short* R, unsigned short* P,
                        float b, float c, hipStream_t s);
-// Xn = a X + P X, written row-major (Xn) and transposed (XTn)
+// Xn = a X + P X (times scale[k] when scale is given), written row-major (Xn) and
+// transposed (XTn)
 hipError_t launch_combine(const BucketPlan& p, const unsigned short* P,
                           const unsigned short* X, const unsigned short* XT, float a,
-                          unsigned short* Xn, unsigned short* XTn, hipStream_t s);
-// param <- param - lr*wd*mask*param - lr*scale*O   (O bf16, row stride ldo)
+                          unsigned short* Xn, unsigned short* XTn, const float* scale,
+                          hipStream_t s);
+// param <- param - lr*wd*mask*param - lr*scale*O with O = oscale[k] * (bf16 O) (oscale
+// may be null: 1), row stride ldo
 hipError_t launch_muon_apply(const BucketPlan& p, float* param, const unsigned short* O,
-                             int64_t ldo, float lr, float wd, float scale, int cautious,
-                             hipStream_t s);
-// out = O as fp32 in the (K, A, B) orientation
+                             const float* oscale, int64_t ldo, float lr, float wd, float scale,
+                             int cautious, hipStream_t s);
+// out = oscale[k] * O as fp32 in the (K, A, B) orientation
 hipError_t launch_ns_extract(const BucketPlan& p, float* out, const unsigned short* O,
-                             int64_t ldo, hipStream_t s);
+                             const float* oscale, int64_t ldo, hipStream_t s);
 
 struct AdamWConst {
   float lr, beta1, beta2, one_m_beta1, one_m_beta2, eps, wd, inv_bc1, inv_bc2;

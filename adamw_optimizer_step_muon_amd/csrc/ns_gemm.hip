@@ -53,6 +53,7 @@ struct GemmArgs {
   const unsigned short* aux;  // transposed a/b-term source: poly R (symmetric), combine X^T
   int64_t ldaux, strideAux;
   float alpha, beta;    // poly: b, c; combine: a, 1
+  const float* scale;   // per-matrix factor or null: gram R *= scale^2, combine X' *= scale
   int tiles_m, tiles_n; // tile grid (triangular for gram/poly)
   int tiles_per_batch;
 };
@@ -266,6 +267,8 @@ __global__ __launch_bounds__(C::kThreads) void ns_gemm_kernel(GemmArgs args) {
   const unsigned short* auxT =
       (kEpi == kGram) ? nullptr : args.aux + batch * args.strideAux;
   if (need_t) __syncthreads();  // every wave is done reading the operand stages
+  float sc = 1.0f;
+  if (kEpi != kPoly && args.scale) sc = args.scale[batch];
 
   constexpr int kHalves = C::WTM >= 2 ? 2 : 1;  // aux loads in two batches (registers)
 #pragma unroll
@@ -302,7 +305,9 @@ __global__ __launch_bounds__(C::kThreads) void ns_gemm_kernel(GemmArgs args) {
             if (kEpi != kGram) {
               const unsigned int w = ax[ii][j][q][e >> 1];
               const float t = bf2f(static_cast<unsigned short>((e & 1) ? (w >> 16) : (w & 0xffffu)));
-              v = (kEpi == kPoly) ? args.alpha * t + args.beta * v : args.alpha * t + v;
+              v = (kEpi == kPoly) ? args.alpha * t + args.beta * v : sc * (args.alpha * t + v);
+            } else {
+              v = (sc * sc) * v;
             }
             h[e] = f2bf(v);
             Cp[(m0 + il0 + e) * args.ldc + gj] = h[e];
@@ -396,8 +401,9 @@ int pick_tile(int64_t K, int64_t m, int64_t n) {
 }
 
 hipError_t launch_gram(const BucketPlan& p, const unsigned short* X, unsigned short* R,
-                       hipStream_t s) {
+                       const float* scale, hipStream_t s) {
   GemmArgs a{};
+  a.scale = scale;
   a.A = X; a.B = X;
   a.lda = a.ldb = p.n_pad;
   a.strideA = a.strideB = p.m_pad * p.n_pad;
@@ -427,8 +433,11 @@ hipError_t launch_poly(const BucketPlan& p, const unsigned short* R, unsigned sh
 
 hipError_t launch_combine(const BucketPlan& p, const unsigned short* P,
                           const unsigned short* X, const unsigned short* XT, float alpha,
-                          unsigned short* Xn, unsigned short* XTn, hipStream_t s) {
+                          unsigned short* Xn, unsigned short* XTn, const float* scale,
+                          hipStream_t s) {
+  (void)X;  // a X is read from the transposed copy
   GemmArgs a{};
+  a.scale = scale;
   a.A = P; a.B = XT;
   a.lda = p.m_pad; a.ldb = p.m_pad;
   a.strideA = p.m_pad * p.m_pad;
