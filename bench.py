@@ -15,8 +15,8 @@ Default workload: index 1, the 12-layer GPT with hidden 768.
 from __future__ import annotations
 
 import argparse
+import hashlib
 import json
-import math
 import os
 import sys
 import time
@@ -48,7 +48,39 @@ def parse():
     ap.add_argument("--workload", type=int, default=1)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget-s", type=float, default=20.0)
+    ap.add_argument("--calibration-copy-mib", type=int, default=0,
+                    help="after timing, copy this many MiB device-to-device once (a plain "
+                         "copy of known size for calibrating HBM byte counters)")
     return ap.parse_args()
+
+
+CSRC = os.path.join(ROOT, "adamw_optimizer_step_muon_amd", "csrc")
+PROFILES = os.path.join(ROOT, "profiles")
+
+
+def source_hash(name):
+    with open(os.path.join(CSRC, name), "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def counted_traffic(summary, source):
+    """HBM bytes per launch from a committed rocprofv3 FETCH_SIZE/WRITE_SIZE summary,
+    or None when the summary is missing or the kernel source changed since."""
+    path = os.path.join(PROFILES, summary)
+    if not os.path.exists(path):
+        return None
+    vals = {}
+    with open(path) as f:
+        for line in f:
+            parts = line.split()
+            if len(parts) == 2 and not line.startswith("#"):
+                vals[parts[0]] = parts[1]
+    if vals.get("source_sha256") != source_hash(source):
+        return None
+    try:
+        return float(vals["traffic_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
 
 
 def cpu_baseline(wl, budget_s):
@@ -209,7 +241,7 @@ def main():
             "peak": MFMA_BF16_PEAK_TFLOPS,
             "unit": "TFLOP/s",
             "frac": round(ns_tflops / MFMA_BF16_PEAK_TFLOPS, 4),
-            "traffic": None,
+            "traffic": counted_traffic(f"ns_gemm_traffic_workload{args.workload}.txt", "ns_gemm.hip"),
             "flops_per_launch": flops / launches,
             "avg_launch_ms": ns_ms / launches,
         },
@@ -220,10 +252,18 @@ def main():
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
             "frac": round(adamw_gbs / HBM_PEAK_GBS, 4),
-            "traffic": None,
+            "traffic": counted_traffic(f"adamw_traffic_workload{args.workload}.txt", "adamw.hip"),
+            "bytes_per_launch": ADAMW_BYTES_PER_ELEM * n,
         },
         "timed_wall_s": round(wall_s, 3),
     }
+    if args.calibration_copy_mib > 0:
+        nbytes = args.calibration_copy_mib << 20
+        src = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        out["calibration_copy_bytes"] = nbytes
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(wl, args.cpu_budget_s)
     print(json.dumps(out), flush=True)
