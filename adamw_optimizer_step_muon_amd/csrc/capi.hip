@@ -101,36 +101,113 @@ ma_muon_route route_of(const BucketPlan& p, int ns_steps) {
   return r;
 }
 
-// Runs Newton-Schulz on a bucket whose unnormalised bf16 U sits in X[0] / XT[0] and
-// whose normalisers inv[k] = 1 / (||U_k|| + eps) are in the workspace; returns the
-// buffer holding the result in the matrix's own orientation, its row stride, and the
-// per-matrix factor still to apply to it (inv when no iteration ran, else none).
-ma_status run_ns(const BucketPlan& p, const ma_muon_hparams* hp, char* ws, hipStream_t s,
+// Buckets run in phases: consecutive buckets with the same GEMM tile, at most
+// kMaxGemmGroups of them and kPhaseBytes of workspace together, share each Newton-Schulz
+// launch (short Gram sides fill the chip together); each has its own workspace region.
+constexpr size_t kPhaseBytes = size_t(4) << 30;
+
+struct Phase {
+  int n = 0;
+  int tile = 0;
+  size_t bytes = 0;
+  BucketPlan plan[kMaxGemmGroups];
+  size_t base[kMaxGemmGroups];
+  int bucket[kMaxGemmGroups];
+};
+
+bool phase_accepts(const Phase& ph, const BucketPlan& p) {
+  return ph.n > 0 && ph.n < kMaxGemmGroups && ph.tile == p.tile &&
+         ph.bytes + p.bytes <= kPhaseBytes;
+}
+
+void phase_add(Phase& ph, const BucketPlan& p, int bucket) {
+  ph.plan[ph.n] = p;
+  ph.base[ph.n] = ph.bytes;
+  ph.bucket[ph.n] = bucket;
+  ph.tile = p.tile;
+  ph.bytes += p.bytes;  // plan sizes are multiples of 256
+  ++ph.n;
+}
+
+// Calls fn(phase) for each phase of the bucket list, in order.
+template <class Fn>
+ma_status for_each_phase(const ma_muon_bucket* buckets, int32_t n_buckets, Fn&& fn) {
+  Phase ph;
+  for (int32_t i = 0; i < n_buckets; ++i) {
+    if (buckets[i].K <= 0) continue;
+    const BucketPlan p = plan_bucket(buckets[i].K, buckets[i].A, buckets[i].B);
+    if (ph.n > 0 && !phase_accepts(ph, p)) {
+      const ma_status st = fn(ph);
+      if (st != MA_OK) return st;
+      ph = Phase();
+    }
+    phase_add(ph, p, i);
+  }
+  if (ph.n > 0) return fn(ph);
+  return MA_OK;
+}
+
+template <class T>
+T* at(char* ws, size_t off) {
+  return reinterpret_cast<T*>(ws + off);
+}
+
+// Newton-Schulz for every bucket of a phase whose unnormalised bf16 U sits in its X[0] /
+// XT[0] and whose normalisers inv[k] = 1 / (||U_k|| + eps) are in its workspace.  On
+// return out[j] holds bucket j's result in the matrix's own orientation (row stride
+// ldo[j]) and oscale[j] the per-matrix factor still to apply (inv when no iteration ran).
+ma_status run_ns(const Phase& ph, const ma_muon_hparams* hp, char* ws, hipStream_t s,
                  const unsigned short** out, int64_t* ldo, const float** oscale) {
-  unsigned short* X[2] = {reinterpret_cast<unsigned short*>(ws + p.off_x[0]),
-                          reinterpret_cast<unsigned short*>(ws + p.off_x[1])};
-  unsigned short* XT[2] = {reinterpret_cast<unsigned short*>(ws + p.off_xt[0]),
-                           reinterpret_cast<unsigned short*>(ws + p.off_xt[1])};
-  unsigned short* R = reinterpret_cast<unsigned short*>(ws + p.off_r);
-  unsigned short* P = reinterpret_cast<unsigned short*>(ws + p.off_p);
-  const float* inv = reinterpret_cast<const float*>(ws + p.off_inv);
+  NsGroup g[kMaxGemmGroups];
+  const float* inv[kMaxGemmGroups];
+  for (int j = 0; j < ph.n; ++j) inv[j] = at<const float>(ws, ph.base[j] + ph.plan[j].off_inv);
   int cur = 0;
   for (int it = 0; it < hp->ns_steps; ++it) {
+    for (int j = 0; j < ph.n; ++j) {
+      const BucketPlan& p = ph.plan[j];
+      char* w = ws + ph.base[j];
+      g[j].plan = &p;
+      g[j].X = at<unsigned short>(w, p.off_x[cur]);
+      g[j].XT = at<unsigned short>(w, p.off_xt[cur]);
+      g[j].Xn = at<unsigned short>(w, p.off_x[cur ^ 1]);
+      g[j].XTn = at<unsigned short>(w, p.off_xt[cur ^ 1]);
+      g[j].R = at<unsigned short>(w, p.off_r);
+      g[j].P = at<unsigned short>(w, p.off_p);
+    }
     const NsCoeffs c = coeff_at(hp, it);
     // the first iteration applies the normalisation X0 = inv U inside its products
-    const float* sc = it == 0 ? inv : nullptr;
-    hipError_t e = launch_gram(p, X[cur], R, sc, s);
+    const float* const* sc = it == 0 ? inv : nullptr;
+    hipError_t e = launch_gram(g, ph.n, sc, s);
     if (e != hipSuccess) return hip_fail(e, "gram launch");
-    e = launch_poly(p, R, P, c.b, c.c, s);
+    e = launch_poly(g, ph.n, c.b, c.c, s);
     if (e != hipSuccess) return hip_fail(e, "poly launch");
-    e = launch_combine(p, P, X[cur], XT[cur], c.a, X[cur ^ 1], XT[cur ^ 1], sc, s);
+    e = launch_combine(g, ph.n, c.a, sc, s);
     if (e != hipSuccess) return hip_fail(e, "combine launch");
     cur ^= 1;
   }
-  // Own orientation: X (m_pad x n_pad) when not transposed, X^T (n_pad x m_pad) when it is.
-  *out = p.transposed ? XT[cur] : X[cur];
-  *ldo = p.transposed ? p.m_pad : p.n_pad;
-  *oscale = hp->ns_steps == 0 ? inv : nullptr;
+  for (int j = 0; j < ph.n; ++j) {
+    const BucketPlan& p = ph.plan[j];
+    char* w = ws + ph.base[j];
+    // own orientation: X (m_pad x n_pad) if not transposed, X^T (n_pad x m_pad) if it is
+    out[j] = at<unsigned short>(w, p.transposed ? p.off_xt[cur] : p.off_x[cur]);
+    ldo[j] = p.transposed ? p.m_pad : p.n_pad;
+    oscale[j] = hp->ns_steps == 0 ? inv[j] : nullptr;
+  }
+  return MA_OK;
+}
+
+// momentum update + bf16 cast + norm of one bucket into its workspace region
+ma_status prep_bucket(const BucketPlan& p, const float* grad, float* momentum,
+                      const ma_muon_hparams* hp, char* w, hipStream_t s) {
+  unsigned short* S = at<unsigned short>(w, p.transposed ? p.off_xt[0] : p.off_x[0]);
+  unsigned short* T = at<unsigned short>(w, p.transposed ? p.off_x[0] : p.off_xt[0]);
+  float* partials = at<float>(w, p.off_part);
+  float* inv = at<float>(w, p.off_inv);
+  hipError_t e = launch_muon_prep(p, grad, momentum, momentum ? hp->momentum : 0.0f,
+                                  momentum ? hp->nesterov : 0, partials, S, T, s);
+  if (e != hipSuccess) return hip_fail(e, "momentum/cast launch");
+  e = launch_norm_finalize(p, partials, hp->ns_eps, inv, s);
+  if (e != hipSuccess) return hip_fail(e, "norm launch");
   return MA_OK;
 }
 
@@ -208,13 +285,13 @@ size_t ma_muon_workspace_bytes(const ma_muon_bucket* buckets, int32_t n_buckets,
                                const ma_muon_hparams* hp) {
   (void)hp;
   if (n_buckets <= 0 || !buckets) return 0;
+  for (int32_t i = 0; i < n_buckets; ++i)
+    if (buckets[i].K > 0 && (buckets[i].A < 1 || buckets[i].B < 1)) return 0;
   size_t need = 0;
-  for (int32_t i = 0; i < n_buckets; ++i) {
-    const ma_muon_bucket& b = buckets[i];
-    if (b.K <= 0 || b.A < 1 || b.B < 1) continue;
-    const size_t bytes = plan_bucket(b.K, b.A, b.B).bytes;
-    if (bytes > need) need = bytes;
-  }
+  for_each_phase(buckets, n_buckets, [&](const Phase& ph) {
+    if (ph.bytes > need) need = ph.bytes;
+    return MA_OK;
+  });
   return need;
 }
 
@@ -271,33 +348,31 @@ ma_status ma_muon_step(const ma_muon_bucket* buckets, int32_t n_buckets,
   }
   hipStream_t s = static_cast<hipStream_t>(stream);
   char* ws = static_cast<char*>(workspace);
-  for (int32_t i = 0; i < n_buckets; ++i) {
-    const ma_muon_bucket& b = buckets[i];
-    if (b.K == 0) continue;
-    const BucketPlan p = plan_bucket(b.K, b.A, b.B);
-    float* partials = reinterpret_cast<float*>(ws + p.off_part);
-    float* inv = reinterpret_cast<float*>(ws + p.off_inv);
-    unsigned short* S = reinterpret_cast<unsigned short*>(ws + (p.transposed ? p.off_xt[0] : p.off_x[0]));
-    unsigned short* T = reinterpret_cast<unsigned short*>(ws + (p.transposed ? p.off_x[0] : p.off_xt[0]));
-    hipError_t e = launch_muon_prep(p, b.grad, b.momentum, hp->momentum, hp->nesterov, partials,
-                                    S, T, s);
-    if (e != hipSuccess) return hip_fail(e, "momentum launch");
-    e = launch_norm_finalize(p, partials, hp->ns_eps, inv, s);
-    if (e != hipSuccess) return hip_fail(e, "norm launch");
-    const unsigned short* O = nullptr;
-    const float* oscale = nullptr;
-    int64_t ldo = 0;
-    st = run_ns(p, hp, ws, s, &O, &ldo, &oscale);
-    if (st != MA_OK) return st;
-    const double big = static_cast<double>(b.A > b.B ? b.A : b.B);
-    const double scale = hp->scale_mode == 0
-                             ? 0.2 * std::sqrt(big)
-                             : std::sqrt(std::fmax(1.0, static_cast<double>(b.A) / static_cast<double>(b.B)));
-    e = launch_muon_apply(p, b.param, O, oscale, ldo, hp->lr, hp->weight_decay,
-                          static_cast<float>(scale), hp->cautious_wd, s);
-    if (e != hipSuccess) return hip_fail(e, "apply launch");
-  }
-  return MA_OK;
+  return for_each_phase(buckets, n_buckets, [&](const Phase& ph) -> ma_status {
+    for (int j = 0; j < ph.n; ++j) {
+      const ma_muon_bucket& b = buckets[ph.bucket[j]];
+      const ma_status st2 = prep_bucket(ph.plan[j], b.grad, b.momentum, hp, ws + ph.base[j], s);
+      if (st2 != MA_OK) return st2;
+    }
+    const unsigned short* O[kMaxGemmGroups];
+    int64_t ldo[kMaxGemmGroups];
+    const float* oscale[kMaxGemmGroups];
+    const ma_status st2 = run_ns(ph, hp, ws, s, O, ldo, oscale);
+    if (st2 != MA_OK) return st2;
+    for (int j = 0; j < ph.n; ++j) {
+      const ma_muon_bucket& b = buckets[ph.bucket[j]];
+      const double big = static_cast<double>(b.A > b.B ? b.A : b.B);
+      const double scale =
+          hp->scale_mode == 0
+              ? 0.2 * std::sqrt(big)
+              : std::sqrt(std::fmax(1.0, static_cast<double>(b.A) / static_cast<double>(b.B)));
+      const hipError_t e = launch_muon_apply(ph.plan[j], b.param, O[j], oscale[j], ldo[j], hp->lr,
+                                             hp->weight_decay, static_cast<float>(scale),
+                                             hp->cautious_wd, s);
+      if (e != hipSuccess) return hip_fail(e, "apply launch");
+    }
+    return MA_OK;
+  });
 }
 
 size_t ma_newton_schulz_workspace_bytes(int64_t K, int64_t A, int64_t B) {
@@ -328,20 +403,16 @@ ma_status ma_newton_schulz(const float* in, float* out, int64_t K, int64_t A, in
     return fail(MA_ERR_WORKSPACE, "workspace has %zu bytes, %zu needed", workspace_bytes, p.bytes);
   hipStream_t s = static_cast<hipStream_t>(stream);
   char* ws = static_cast<char*>(workspace);
-  float* partials = reinterpret_cast<float*>(ws + p.off_part);
-  float* inv = reinterpret_cast<float*>(ws + p.off_inv);
-  unsigned short* S = reinterpret_cast<unsigned short*>(ws + (p.transposed ? p.off_xt[0] : p.off_x[0]));
-  unsigned short* T = reinterpret_cast<unsigned short*>(ws + (p.transposed ? p.off_x[0] : p.off_xt[0]));
-  hipError_t e = launch_muon_prep(p, in, nullptr, 0.0f, 0, partials, S, T, s);
-  if (e != hipSuccess) return hip_fail(e, "cast launch");
-  e = launch_norm_finalize(p, partials, hp->ns_eps, inv, s);
-  if (e != hipSuccess) return hip_fail(e, "norm launch");
-  const unsigned short* O = nullptr;
-  const float* oscale = nullptr;
-  int64_t ldo = 0;
-  st = run_ns(p, hp, ws, s, &O, &ldo, &oscale);
+  Phase ph;
+  phase_add(ph, p, 0);
+  st = prep_bucket(p, in, nullptr, hp, ws, s);
   if (st != MA_OK) return st;
-  e = launch_ns_extract(p, out, O, oscale, ldo, s);
+  const unsigned short* O[kMaxGemmGroups];
+  int64_t ldo[kMaxGemmGroups];
+  const float* oscale[kMaxGemmGroups];
+  st = run_ns(ph, hp, ws, s, O, ldo, oscale);
+  if (st != MA_OK) return st;
+  const hipError_t e = launch_ns_extract(p, out, O[0], oscale[0], ldo[0], s);
   if (e != hipSuccess) return hip_fail(e, "extract launch");
   return MA_OK;
 }

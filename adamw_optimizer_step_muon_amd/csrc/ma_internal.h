@@ -61,17 +61,24 @@ hipError_t launch_muon_prep(const BucketPlan& p, const float* G, float* M, float
 // inv[k] = 1 / (sqrt(sum of partials of matrix k) + eps)
 hipError_t launch_norm_finalize(const BucketPlan& p, const float* partials, float eps,
                                 float* inv, hipStream_t s);
-// R = X X^T (lower-triangle tiles, mirrored); R *= scale[k]^2 when scale is given
-hipError_t launch_gram(const BucketPlan& p, const unsigned short* X, unsigned short* R,
-                       const float* scale, hipStream_t s);
+// Newton-Schulz products over a group of up to kMaxGemmGroups buckets with the same
+// tile, one launch per product for the whole group.
+constexpr int kMaxGemmGroups = 4;
+struct NsGroup {
+  const BucketPlan* plan;
+  unsigned short* X;    // current iterate, m_pad x n_pad per matrix
+  unsigned short* XT;   // its transpose, n_pad x m_pad
+  unsigned short* Xn;   // next iterate and its transpose
+  unsigned short* XTn;
+  unsigned short* R;    // m_pad x m_pad
+  unsigned short* P;
+};
+// R = X X^T (lower-triangle tiles, mirrored); R *= scale[i][k]^2 where scale[i] is given
+hipError_t launch_gram(const NsGroup* g, int n, const float* const* scale, hipStream_t s);
 // P = b R + c R R^T (lower-triangle tiles, mirrored)
-hipError_t launch_poly(const BucketPlan& p, const unsigned short* R, unsigned short* P,
-                       float b, float c, hipStream_t s);
-// Xn = a X + P X (times scale[k] when scale is given), written row-major (Xn) and
-// transposed (XTn)
-hipError_t launch_combine(const BucketPlan& p, const unsigned short* P,
-                          const unsigned short* X, const unsigned short* XT, float a,
-                          unsigned short* Xn, unsigned short* XTn, const float* scale,
+hipError_t launch_poly(const NsGroup* g, int n, float b, float c, hipStream_t s);
+// Xn = a X + P X (times scale[i][k] where given), written row-major and transposed
+hipError_t launch_combine(const NsGroup* g, int n, float a, const float* const* scale,
                           hipStream_t s);
 // param <- param - lr*wd*mask*param - lr*scale*O with O = oscale[k] * (bf16 O) (oscale
 // may be null: 1), row stride ldo

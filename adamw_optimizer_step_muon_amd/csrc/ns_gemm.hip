@@ -56,6 +56,15 @@ struct GemmArgs {
   const float* scale;   // per-matrix factor or null: gram R *= scale^2, combine X' *= scale
   int tiles_m, tiles_n; // tile grid (triangular for gram/poly)
   int tiles_per_batch;
+  int tiles_k;          // matrices in the group (host side: block count = tiles_k x tiles_per_batch)
+};
+
+// Up to kMaxGroups buckets (same tile shape) share one launch: block b belongs to the
+// group g with start[g] <= b' < start[g+1], b' the XCD-remapped block id.
+struct GemmTable {
+  GemmArgs g[kMaxGemmGroups];
+  int start[kMaxGemmGroups + 1];
+  int ngroups;
 };
 
 template <int BM_, int BN_, int BK_, int WM_, int WN_, int STAGES_>
@@ -114,8 +123,12 @@ __device__ __forceinline__ int xcd_linear(int bid, int nblocks) {
 }
 
 template <class C, int kEpi>
-__global__ __launch_bounds__(C::kThreads) void ns_gemm_kernel(GemmArgs args) {
+__global__ __launch_bounds__(C::kThreads) void ns_gemm_kernel(GemmTable table) {
   __shared__ __attribute__((aligned(16))) unsigned short smem[C::kLdsElems];
+  // The table is read in place from the kernel-argument segment with the (uniform)
+  // group index (the compiler turns these into scalar loads), not copied privately.
+  const GemmTable* kt = (const GemmTable*)__builtin_amdgcn_kernarg_segment_ptr();
+  (void)table;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -123,7 +136,18 @@ __global__ __launch_bounds__(C::kThreads) void ns_gemm_kernel(GemmArgs args) {
   const int wm = wave / C::WN;
   const int wn = wave % C::WN;
 
-  const int lid = xcd_linear(blockIdx.x, gridDim.x);
+  // Group by raw block id (group starts are multiples of 8, so a group's blocks keep
+  // the round-robin XCD pattern), then renumber inside the group so each XCD owns a
+  // contiguous run of that group's tiles; padding blocks exit at once.
+  int gi = 0;
+#pragma unroll
+  for (int i = 1; i < kMaxGemmGroups; ++i)
+    if (i < kt->ngroups && static_cast<int>(blockIdx.x) >= kt->start[i]) gi = i;
+  const GemmArgs args = kt->g[gi];
+  const int g0 = kt->start[gi];
+  const int gcount = args.tiles_per_batch * args.tiles_k;
+  const int lid = xcd_linear(static_cast<int>(blockIdx.x) - g0, (gcount + 7) & ~7);
+  if (lid >= gcount) return;
   const int64_t batch = lid / args.tiles_per_batch;
   const int tile = lid - static_cast<int>(batch) * args.tiles_per_batch;
   int ti, tj;
@@ -350,14 +374,14 @@ using Big8 = Cfg<256, 256, 32, 2, 4, 4>;
 using SmallCfg = Cfg<128, 128, 64, 2, 2, 2>;
 
 template <class C>
-hipError_t launch_cfg(int epi, const GemmArgs& a, int64_t K, hipStream_t s) {
-  const int64_t blocks = K * a.tiles_per_batch;
+hipError_t launch_cfg(int epi, const GemmTable& t, hipStream_t s) {
+  const int blocks = t.start[t.ngroups];
   if (blocks <= 0) return hipSuccess;
   const dim3 grid(static_cast<unsigned>(blocks));
   switch (epi) {
-    case kGram: hipLaunchKernelGGL((ns_gemm_kernel<C, kGram>), grid, dim3(C::kThreads), 0, s, a); break;
-    case kPoly: hipLaunchKernelGGL((ns_gemm_kernel<C, kPoly>), grid, dim3(C::kThreads), 0, s, a); break;
-    default: hipLaunchKernelGGL((ns_gemm_kernel<C, kCombine>), grid, dim3(C::kThreads), 0, s, a); break;
+    case kGram: hipLaunchKernelGGL((ns_gemm_kernel<C, kGram>), grid, dim3(C::kThreads), 0, s, t); break;
+    case kPoly: hipLaunchKernelGGL((ns_gemm_kernel<C, kPoly>), grid, dim3(C::kThreads), 0, s, t); break;
+    default: hipLaunchKernelGGL((ns_gemm_kernel<C, kCombine>), grid, dim3(C::kThreads), 0, s, t); break;
   }
   return hipGetLastError();
 }
@@ -370,7 +394,8 @@ int big_variant() {
   return v;
 }
 
-hipError_t launch(int epi, GemmArgs a, const BucketPlan& p, hipStream_t s) {
+// Fill the tile-grid fields of one group's arguments.
+void set_tiles(int epi, GemmArgs& a, const BucketPlan& p) {
   const int T = p.tile;
   if (epi == kCombine) {
     a.tiles_m = static_cast<int>(p.m_pad / T);
@@ -380,15 +405,29 @@ hipError_t launch(int epi, GemmArgs a, const BucketPlan& p, hipStream_t s) {
     a.tiles_m = a.tiles_n = static_cast<int>(p.m_pad / T);
     a.tiles_per_batch = a.tiles_m * (a.tiles_m + 1) / 2;
   }
-  if (T == 256) {
+}
+
+hipError_t launch_table(int epi, GemmTable& t, int tile, hipStream_t s) {
+  // longest contraction first, so the blocks with the most work are dispatched first
+  for (int i = 1; i < t.ngroups; ++i)
+    for (int j = i; j > 0 && t.g[j].kdim > t.g[j - 1].kdim; --j) {
+      const GemmArgs tmp = t.g[j];
+      t.g[j] = t.g[j - 1];
+      t.g[j - 1] = tmp;
+    }
+  t.start[0] = 0;
+  for (int i = 0; i < t.ngroups; ++i)
+    t.start[i + 1] = t.start[i] + ((t.g[i].tiles_per_batch * t.g[i].tiles_k + 7) & ~7);
+  for (int i = t.ngroups + 1; i <= kMaxGemmGroups; ++i) t.start[i] = t.start[t.ngroups];
+  if (tile == 256) {
     switch (big_variant()) {
-      case 1: return launch_cfg<Big4>(epi, a, p.K, s);
-      case 2: return launch_cfg<Big4K64>(epi, a, p.K, s);
-      case 3: return launch_cfg<Big8>(epi, a, p.K, s);
-      default: return launch_cfg<Big8K64>(epi, a, p.K, s);
+      case 1: return launch_cfg<Big4>(epi, t, s);
+      case 2: return launch_cfg<Big4K64>(epi, t, s);
+      case 3: return launch_cfg<Big8>(epi, t, s);
+      default: return launch_cfg<Big8K64>(epi, t, s);
     }
   }
-  return launch_cfg<SmallCfg>(epi, a, p.K, s);
+  return launch_cfg<SmallCfg>(epi, t, s);
 }
 
 }  // namespace
@@ -400,57 +439,73 @@ int pick_tile(int64_t K, int64_t m, int64_t n) {
   return (K * m256 * n256 >= 512 && m >= 512) ? 256 : SmallCfg::BM;
 }
 
-hipError_t launch_gram(const BucketPlan& p, const unsigned short* X, unsigned short* R,
-                       const float* scale, hipStream_t s) {
-  GemmArgs a{};
-  a.scale = scale;
-  a.A = X; a.B = X;
-  a.lda = a.ldb = p.n_pad;
-  a.strideA = a.strideB = p.m_pad * p.n_pad;
-  a.kdim = static_cast<int>(p.n_pad);
-  a.C = R; a.C2 = R;
-  a.ldc = a.ldc2 = p.m_pad;
-  a.strideC = a.strideC2 = p.m_pad * p.m_pad;
-  return launch(kGram, a, p, s);
+hipError_t launch_gram(const NsGroup* g, int n, const float* const* scale, hipStream_t s) {
+  GemmTable t{};
+  t.ngroups = n;
+  for (int i = 0; i < n; ++i) {
+    const BucketPlan& p = *g[i].plan;
+    GemmArgs& a = t.g[i];
+    a.A = g[i].X; a.B = g[i].X;
+    a.lda = a.ldb = p.n_pad;
+    a.strideA = a.strideB = p.m_pad * p.n_pad;
+    a.kdim = static_cast<int>(p.n_pad);
+    a.C = g[i].R; a.C2 = g[i].R;
+    a.ldc = a.ldc2 = p.m_pad;
+    a.strideC = a.strideC2 = p.m_pad * p.m_pad;
+    a.scale = scale ? scale[i] : nullptr;
+    a.tiles_k = static_cast<int>(p.K);
+    set_tiles(kGram, a, p);
+  }
+  return launch_table(kGram, t, g[0].plan->tile, s);
 }
 
-hipError_t launch_poly(const BucketPlan& p, const unsigned short* R, unsigned short* P,
-                       float b, float c, hipStream_t s) {
-  GemmArgs a{};
-  a.A = R; a.B = R;
-  a.lda = a.ldb = p.m_pad;
-  a.strideA = a.strideB = p.m_pad * p.m_pad;
-  a.kdim = static_cast<int>(p.m_pad);
-  a.C = P; a.C2 = P;
-  a.ldc = a.ldc2 = p.m_pad;
-  a.strideC = a.strideC2 = p.m_pad * p.m_pad;
-  a.aux = R;
-  a.ldaux = p.m_pad;
-  a.strideAux = p.m_pad * p.m_pad;
-  a.alpha = b; a.beta = c;
-  return launch(kPoly, a, p, s);
+hipError_t launch_poly(const NsGroup* g, int n, float b, float c, hipStream_t s) {
+  GemmTable t{};
+  t.ngroups = n;
+  for (int i = 0; i < n; ++i) {
+    const BucketPlan& p = *g[i].plan;
+    GemmArgs& a = t.g[i];
+    a.A = g[i].R; a.B = g[i].R;
+    a.lda = a.ldb = p.m_pad;
+    a.strideA = a.strideB = p.m_pad * p.m_pad;
+    a.kdim = static_cast<int>(p.m_pad);
+    a.C = g[i].P; a.C2 = g[i].P;
+    a.ldc = a.ldc2 = p.m_pad;
+    a.strideC = a.strideC2 = p.m_pad * p.m_pad;
+    a.aux = g[i].R;
+    a.ldaux = p.m_pad;
+    a.strideAux = p.m_pad * p.m_pad;
+    a.alpha = b; a.beta = c;
+    a.tiles_k = static_cast<int>(p.K);
+    set_tiles(kPoly, a, p);
+  }
+  return launch_table(kPoly, t, g[0].plan->tile, s);
 }
 
-hipError_t launch_combine(const BucketPlan& p, const unsigned short* P,
-                          const unsigned short* X, const unsigned short* XT, float alpha,
-                          unsigned short* Xn, unsigned short* XTn, const float* scale,
+hipError_t launch_combine(const NsGroup* g, int n, float alpha, const float* const* scale,
                           hipStream_t s) {
-  (void)X;  // a X is read from the transposed copy
-  GemmArgs a{};
-  a.scale = scale;
-  a.A = P; a.B = XT;
-  a.lda = p.m_pad; a.ldb = p.m_pad;
-  a.strideA = p.m_pad * p.m_pad;
-  a.strideB = p.m_pad * p.n_pad;
-  a.kdim = static_cast<int>(p.m_pad);
-  a.C = Xn; a.C2 = XTn;
-  a.ldc = p.n_pad; a.ldc2 = p.m_pad;
-  a.strideC = a.strideC2 = p.m_pad * p.n_pad;
-  a.aux = XT;  // X[i][j] read as X^T[j][i]
-  a.ldaux = p.m_pad;
-  a.strideAux = p.m_pad * p.n_pad;
-  a.alpha = alpha; a.beta = 1.0f;
-  return launch(kCombine, a, p, s);
+  GemmTable t{};
+  t.ngroups = n;
+  for (int i = 0; i < n; ++i) {
+    const BucketPlan& p = *g[i].plan;
+    GemmArgs& a = t.g[i];
+    a.A = g[i].P; a.B = g[i].XT;
+    a.lda = p.m_pad; a.ldb = p.m_pad;
+    a.strideA = p.m_pad * p.m_pad;
+    a.strideB = p.m_pad * p.n_pad;
+    a.kdim = static_cast<int>(p.m_pad);
+    a.C = g[i].Xn; a.C2 = g[i].XTn;
+    a.ldc = p.n_pad; a.ldc2 = p.m_pad;
+    a.strideC = a.strideC2 = p.m_pad * p.n_pad;
+    a.aux = g[i].XT;  // X[i][j] read as X^T[j][i]
+    a.ldaux = p.m_pad;
+    a.strideAux = p.m_pad * p.n_pad;
+    a.alpha = alpha; a.beta = 1.0f;
+    a.scale = scale ? scale[i] : nullptr;
+    a.tiles_k = static_cast<int>(p.K);
+    set_tiles(kCombine, a, p);
+  }
+  return launch_table(kCombine, t, g[0].plan->tile, s);
 }
 
 }  // namespace ma

@@ -115,9 +115,11 @@ const char* ma_last_error(void);
  * (ns_steps 5).  Returns MA_ERR_INVALID_ARG for A < 1, B < 1 or a NULL out. */
 ma_status ma_muon_route_of(int64_t A, int64_t B, const ma_muon_hparams* hp, ma_muon_route* out);
 
-/* Host only: workspace bytes ma_muon_step needs for these buckets (the maximum
- * over buckets, which run one after another).  0 when there is nothing to do.
- * Returns 0 as well for invalid arguments; ma_muon_step then reports them. */
+/* Host only: workspace bytes ma_muon_step needs for these buckets.  Buckets run in
+ * phases: consecutive buckets with the same GEMM tile, at most 4 of them and 4 GiB of
+ * workspace together, share each Newton-Schulz launch; the result is the maximum over
+ * phases of the phase's summed need.  0 when there is nothing to do, and for invalid
+ * arguments (ma_muon_step then reports them). */
 size_t ma_muon_workspace_bytes(const ma_muon_bucket* buckets, int32_t n_buckets,
                                const ma_muon_hparams* hp);
 

@@ -62,9 +62,15 @@ def test_workspace_bytes(lib):
     # X, X^T twice (bf16, m x n) plus R and P (bf16, m x m), plus norm scratch
     assert one >= 4 * 768 * 3072 * 2 + 2 * 768 * 768 * 2
     assert ma.muon_workspace_bytes([(2, 768, 3072)]) > one
-    # buckets run one after another: the maximum, not the sum
-    both = ma.muon_workspace_bytes([(1, 768, 3072), (1, 3072, 768)])
-    assert both == max(one, ma.muon_workspace_bytes([(1, 3072, 768)]))
+    # small buckets with the same tile share a phase: their needs add up
+    other = ma.muon_workspace_bytes([(1, 3072, 768)])
+    assert ma.muon_workspace_bytes([(1, 768, 3072), (1, 3072, 768)]) == one + other
+    # large buckets run in phases of their own: the maximum, not the sum
+    big = [(8, 8192, 28672), (16, 8192, 8192)]
+    assert ma.muon_workspace_bytes(big) == max(ma.muon_workspace_bytes([s]) for s in big)
+    # at most four buckets per phase
+    five = ma.muon_workspace_bytes([(1, 64, 64)] * 5)
+    assert five == 4 * ma.muon_workspace_bytes([(1, 64, 64)])
     assert ma.muon_workspace_bytes([(0, 10, 10)]) == 0
 
 
