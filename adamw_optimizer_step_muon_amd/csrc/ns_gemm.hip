@@ -84,6 +84,10 @@ struct Cfg {
   static constexpr int kEpiElems = BM * BN;
   static constexpr int kLdsElems = kMainElems > kEpiElems ? kMainElems : kEpiElems;
   static constexpr int kGroupM = 4;  // row panels per L2 group (combine)
+  // Take the a X / b R term of the epilogue from the B operand stage that covers the
+  // tile's rows (X[i][j] = X^T[j][i], R[i][j] = R[j][i]) instead of reading it again
+  // from memory; held in registers, so only where the wave tile is small.
+  static constexpr bool kCaptureAux = (WTM * WTN) <= 4;
   static_assert(BM % (WM * 32) == 0 && BN % (WN * 32) == 0, "wave tiling");
   static_assert(BM % (kRowsPerDma * kWaves) == 0 && BN % (kRowsPerDma * kWaves) == 0, "dma");
   static_assert(BK == 32 || BK == 64, "swizzle defined for BK 32 and 64");
@@ -243,10 +247,35 @@ __global__ __launch_bounds__(C::kThreads) void ns_gemm_kernel(GemmTable table) {
   // MFMAs of slice kk, and across a stage boundary the barrier wait and the first
   // reads of the next stage sit before the MFMAs of the last slice, so the matrix
   // cores keep working while the block synchronises.
+  // a X / b R epilogue term captured from the B stage (see Cfg::kCaptureAux)
+  u32x2 cap[C::kCaptureAux ? C::WTM : 1][C::WTN][4];
+  auto capture = [&](int kt_stage) {
+    if constexpr (C::kCaptureAux && kEpi != kGram) {
+      const unsigned short* bs = smem + (kt_stage % C::STAGES) * C::kStageElems + C::BM * C::BK;
+      const int k0 = kt_stage * C::BK;
+#pragma unroll
+      for (int i = 0; i < C::WTM; ++i) {
+        const int rbase = static_cast<int>(m0) + wm * (C::WTM * 32) + i * 32;  // 32 rows of i
+        if (rbase >= k0 && rbase < k0 + C::BK) {
+#pragma unroll
+          for (int j = 0; j < C::WTN; ++j) {
+            const int jl = wn * (C::WTN * 32) + j * 32 + (lane & 31);
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+              const int kl = rbase - k0 + 8 * q + 4 * fkh;  // local k of rows gi0..gi0+3
+              cap[i][j][q] = *reinterpret_cast<const u32x2*>(
+                  bs + jl * C::BK + swz<C::BK>(jl, kl >> 3) * 8 + (kl & 4));
+            }
+          }
+        }
+      }
+    }
+  };
   bf16x8 fa[2][C::WTM], fb[2][C::WTN];
   wait_stage(0);
   __builtin_amdgcn_s_barrier();
   load_frags(0, 0, fa[0], fb[0]);
+  capture(0);
   for (int kt = 0; kt < nk; ++kt) {
     const int slot = kt % C::STAGES;
     // slot (kt - 1) % STAGES was last read before the barrier that preceded this stage
@@ -262,6 +291,7 @@ __global__ __launch_bounds__(C::kThreads) void ns_gemm_kernel(GemmTable table) {
         wait_stage(kt + 1);
         __builtin_amdgcn_s_barrier();
         load_frags((kt + 1) % C::STAGES, 0, fa[cur ^ 1], fb[cur ^ 1]);
+        capture(kt + 1);
       }
 #pragma unroll
       for (int i = 0; i < C::WTM; ++i)
@@ -299,7 +329,14 @@ __global__ __launch_bounds__(C::kThreads) void ns_gemm_kernel(GemmTable table) {
   for (int hh = 0; hh < kHalves; ++hh) {
     constexpr int kI = C::WTM / kHalves;
     u32x2 ax[kI][C::WTN][4];
-    if (kEpi != kGram) {
+    if (kEpi != kGram && C::kCaptureAux) {
+#pragma unroll
+      for (int ii = 0; ii < kI; ++ii)
+#pragma unroll
+        for (int j = 0; j < C::WTN; ++j)
+#pragma unroll
+          for (int q = 0; q < 4; ++q) ax[ii][j][q] = cap[hh * kI + ii][j][q];
+    } else if (kEpi != kGram) {
 #pragma unroll
       for (int ii = 0; ii < kI; ++ii)
 #pragma unroll
