@@ -57,6 +57,9 @@ struct GemmArgs {
   int tiles_m, tiles_n; // tile grid (triangular for gram/poly)
   int tiles_per_batch;
   int tiles_k;          // matrices in the group (host side: block count = tiles_k x tiles_per_batch)
+  int band;             // tile rows per L2 band (tile order; 0: plain row-major triangle)
+  int xcd_remap;        // 1: renumber blocks XCD by XCD
+  int spread;           // 1: spread the next stage's DMAs over the first half-stage
 };
 
 // Up to kMaxGroups buckets (same tile shape) share one launch: block b belongs to the
@@ -83,7 +86,6 @@ struct Cfg {
   static constexpr int kMainElems = STAGES * kStageElems;
   static constexpr int kEpiElems = BM * BN;
   static constexpr int kLdsElems = kMainElems > kEpiElems ? kMainElems : kEpiElems;
-  static constexpr int kGroupM = 4;  // row panels per L2 group (combine)
   // Take the a X / b R term of the epilogue from the B operand stage that covers the
   // tile's rows (X[i][j] = X^T[j][i], R[i][j] = R[j][i]) instead of reading it again
   // from memory; held in registers, so only where the wave tile is small.
@@ -150,20 +152,46 @@ __global__ __launch_bounds__(C::kThreads) void ns_gemm_kernel(GemmTable table) {
   const GemmArgs args = kt->g[gi];
   const int g0 = kt->start[gi];
   const int gcount = args.tiles_per_batch * args.tiles_k;
-  const int lid = xcd_linear(static_cast<int>(blockIdx.x) - g0, (gcount + 7) & ~7);
+  const int raw = static_cast<int>(blockIdx.x) - g0;
+  const int lid = args.xcd_remap ? xcd_linear(raw, (gcount + 7) & ~7) : raw;
   if (lid >= gcount) return;
   const int64_t batch = lid / args.tiles_per_batch;
   const int tile = lid - static_cast<int>(batch) * args.tiles_per_batch;
   int ti, tj;
   if (kEpi == kCombine) {
-    // groups of kGroupM row panels; inside a group, column-major over tiles
-    const int per_group = C::kGroupM * args.tiles_n;
-    const int g = tile / per_group;
-    const int first = g * C::kGroupM;
-    const int rows = min(args.tiles_m - first, C::kGroupM);
-    const int in = tile - g * per_group;
+    // bands of `band` row panels; inside a band, column-major over tiles
+    const int G = args.band;
+    const int per_band = G * args.tiles_n;
+    const int b = tile / per_band;
+    const int first = b * G;
+    const int rows = min(args.tiles_m - first, G);
+    const int in = tile - b * per_band;
     ti = first + in % rows;
     tj = in / rows;
+  } else if (args.band > 0) {
+    // lower triangle in bands of G tile rows [r0, r1); inside a band, column by column
+    // (the r0 full-height columns, then the band's own triangle), so the blocks that
+    // run together share G row panels and a few column panels
+    const int G = args.band, T = args.tiles_m;
+    int r0 = 0, u = tile;
+    for (;;) {
+      const int r1 = min(r0 + G, T), h = r1 - r0;
+      const int cnt = r0 * h + h * (h + 1) / 2;
+      if (u < cnt) {
+        if (u < r0 * h) {
+          tj = u / h;
+          ti = r0 + (u - tj * h);
+        } else {
+          int v = u - r0 * h, c = 0;
+          while (v >= h - c) { v -= h - c; ++c; }
+          tj = r0 + c;
+          ti = tj + v;
+        }
+        break;
+      }
+      u -= cnt;
+      r0 = r1;
+    }
   } else {
     // lower-triangle enumeration: tile = ti (ti + 1) / 2 + tj, tj <= ti
     ti = static_cast<int>((__builtin_sqrtf(8.0f * tile + 1.0f) - 1.0f) * 0.5f);
@@ -180,22 +208,21 @@ __global__ __launch_bounds__(C::kThreads) void ns_gemm_kernel(GemmTable table) {
   // LDS-DMA source pointers for this lane (k offset added per stage)
   const int drow = lane / C::kChunks;  // row inside one DMA
   const int dpc = lane % C::kChunks;   // physical chunk this lane fills
-  auto issue_stage = [&](int kt, int slot) {
+  // DMA number d of this wave's stage load: d < kDmaA fills A rows, the rest B rows
+  auto issue_one = [&](int kt, int slot, int d) {
     unsigned short* as = smem + slot * C::kStageElems;
     unsigned short* bs = as + C::BM * C::BK;
     const int k0 = kt * C::BK;
+    const bool isA = d < C::kDmaA;
+    const int i = isA ? d : d - C::kDmaA;
+    const int r0 = (i * C::kWaves + wave) * C::kRowsPerDma;
+    const int r = r0 + drow;
+    if (isA) dma16(gA + r * args.lda + k0 + swz<C::BK>(r, dpc) * 8, as + r0 * C::BK);
+    else dma16(gB + r * args.ldb + k0 + swz<C::BK>(r, dpc) * 8, bs + r0 * C::BK);
+  };
+  auto issue_stage = [&](int kt, int slot) {
 #pragma unroll
-    for (int i = 0; i < C::kDmaA; ++i) {
-      const int r0 = (i * C::kWaves + wave) * C::kRowsPerDma;
-      const int r = r0 + drow;
-      dma16(gA + r * args.lda + k0 + swz<C::BK>(r, dpc) * 8, as + r0 * C::BK);
-    }
-#pragma unroll
-    for (int i = 0; i < C::kDmaB; ++i) {
-      const int r0 = (i * C::kWaves + wave) * C::kRowsPerDma;
-      const int r = r0 + drow;
-      dma16(gB + r * args.ldb + k0 + swz<C::BK>(r, dpc) * 8, bs + r0 * C::BK);
-    }
+    for (int d = 0; d < C::kDmaPerStage; ++d) issue_one(kt, slot, d);
   };
 
   f32x16 acc[C::WTM][C::WTN];
@@ -279,10 +306,21 @@ __global__ __launch_bounds__(C::kThreads) void ns_gemm_kernel(GemmTable table) {
   for (int kt = 0; kt < nk; ++kt) {
     const int slot = kt % C::STAGES;
     // slot (kt - 1) % STAGES was last read before the barrier that preceded this stage
-    if (kt + C::STAGES - 1 < nk) issue_stage(kt + C::STAGES - 1, (kt + C::STAGES - 1) % C::STAGES);
+    const int nxt = kt + C::STAGES - 1;
+    const bool load_next = nxt < nk;
+    if (load_next && !args.spread) issue_stage(nxt, nxt % C::STAGES);
 #pragma unroll
     for (int kk = 0; kk < KK; ++kk) {
       const int cur = kk & 1;
+      // spread: the next stage's DMAs go out over the first half of this stage's
+      // k-slices, between MFMA groups, instead of as one burst after the barrier
+      constexpr int kHalf = KK / 2 > 0 ? KK / 2 : 1;
+      constexpr int kPer = (C::kDmaPerStage + kHalf - 1) / kHalf;
+      if (load_next && args.spread && kk < kHalf) {
+#pragma unroll
+        for (int e = 0; e < kPer; ++e)
+          if (kk * kPer + e < C::kDmaPerStage) issue_one(nxt, nxt % C::STAGES, kk * kPer + e);
+      }
       if (kk + 1 < KK) {
         load_frags(slot, kk + 1, fa[cur ^ 1], fb[cur ^ 1]);
       } else if (kt + 1 < nk) {
@@ -431,8 +469,22 @@ int big_variant() {
   return v;
 }
 
-// Fill the tile-grid fields of one group's arguments.
+int env_int(const char* name, int dflt) {
+  const char* e = std::getenv(name);
+  return e ? std::atoi(e) : dflt;
+}
+
+// Fill the tile-grid and tile-order fields of one group's arguments.
 void set_tiles(int epi, GemmArgs& a, const BucketPlan& p) {
+  // Defaults measured on the MI355X (env knobs for tuning): bands of 4 row panels for
+  // both tile orders, XCD renumbering on, spread DMA issue for 256-tiles only.
+  static const int band_combine = env_int("MA_NS_BAND_COMBINE", 4);
+  static const int band_tri = env_int("MA_NS_BAND_TRI", 4);
+  static const int xcd = env_int("MA_NS_XCD", 1);
+  static const int spread = env_int("MA_NS_SPREAD", -1);
+  a.band = epi == kCombine ? (band_combine > 0 ? band_combine : 1) : band_tri;
+  a.xcd_remap = xcd;
+  a.spread = spread >= 0 ? spread : (p.tile == 256 ? 1 : 0);
   const int T = p.tile;
   if (epi == kCombine) {
     a.tiles_m = static_cast<int>(p.m_pad / T);
