@@ -181,7 +181,7 @@ ma_status run_ns(const Phase& ph, const ma_muon_hparams* hp, char* ws, hipStream
     if (e != hipSuccess) return hip_fail(e, "gram launch");
     e = launch_poly(g, ph.n, c.b, c.c, s);
     if (e != hipSuccess) return hip_fail(e, "poly launch");
-    e = launch_combine(g, ph.n, c.a, sc, s);
+    e = launch_combine(g, ph.n, c.a, sc, it + 1 == hp->ns_steps, s);
     if (e != hipSuccess) return hip_fail(e, "combine launch");
     cur ^= 1;
   }

@@ -77,9 +77,10 @@ struct NsGroup {
 hipError_t launch_gram(const NsGroup* g, int n, const float* const* scale, hipStream_t s);
 // P = b R + c R R^T (lower-triangle tiles, mirrored)
 hipError_t launch_poly(const NsGroup* g, int n, float b, float c, hipStream_t s);
-// Xn = a X + P X (times scale[i][k] where given), written row-major and transposed
+// Xn = a X + P X (times scale[i][k] where given), written row-major and transposed;
+// with `last`, only the orientation of the parameter (X^T when A > B, else X)
 hipError_t launch_combine(const NsGroup* g, int n, float a, const float* const* scale,
-                          hipStream_t s);
+                          bool last, hipStream_t s);
 // param <- param - lr*wd*mask*param - lr*scale*O with O = oscale[k] * (bf16 O) (oscale
 // may be null: 1), row stride ldo
 hipError_t launch_muon_apply(const BucketPlan& p, float* param, const unsigned short* O,

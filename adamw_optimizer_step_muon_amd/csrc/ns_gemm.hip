@@ -246,6 +246,10 @@ __global__ __launch_bounds__(C::kThreads) void ns_gemm_kernel(GemmTable table) {
   // wait until stage `st` has landed: the stages issued after it may stay in flight
   auto wait_stage = [&](int st) {
     const int pending = min(C::STAGES - 2, nk - 1 - st);
+    static_assert(C::STAGES <= 5 && 3 * L < 64, "vmcnt range");
+    if constexpr (C::STAGES >= 5) {
+      if (pending >= 3) { wait_vmcnt<3 * L>(); return; }
+    }
     if constexpr (C::STAGES >= 4) {
       if (pending >= 2) { wait_vmcnt<2 * L>(); return; }
     }
@@ -352,7 +356,10 @@ __global__ __launch_bounds__(C::kThreads) void ns_gemm_kernel(GemmTable table) {
   // The a X / b R term is read from the transposed copy (X^T for combine; R is
   // symmetric), where a lane's 4 consecutive rows are 8 contiguous bytes.
   const bool mirror = (kEpi != kCombine) && (ti != tj);
-  const bool need_t = (kEpi == kCombine) || mirror;
+  // the combine may skip either orientation (the last iteration keeps only the one
+  // the update reads)
+  const bool need_t = (kEpi == kCombine) ? (args.C2 != nullptr) : mirror;
+  const bool need_c = (kEpi != kCombine) || (args.C != nullptr);
   constexpr int kTChunks = C::BM / 8;  // 16-byte chunks per row of the transposed tile
   unsigned short* Ts = smem;           // [BN][BM], chunk c of row j at c ^ (j % kTChunks)
   unsigned short* Cp = args.C + batch * args.strideC;
@@ -409,7 +416,7 @@ __global__ __launch_bounds__(C::kThreads) void ns_gemm_kernel(GemmTable table) {
               v = (sc * sc) * v;
             }
             h[e] = f2bf(v);
-            Cp[(m0 + il0 + e) * args.ldc + gj] = h[e];
+            if (need_c) Cp[(m0 + il0 + e) * args.ldc + gj] = h[e];
           }
           if (need_t) {
             u32x2 packed;
@@ -446,6 +453,7 @@ using Big8K64 = Cfg<256, 256, 64, 2, 4, 2>;
 using Big4 = Cfg<256, 256, 32, 2, 2, 4>;
 using Big4K64 = Cfg<256, 256, 64, 2, 2, 2>;
 using Big8 = Cfg<256, 256, 32, 2, 4, 4>;
+using Big8S5 = Cfg<256, 256, 32, 2, 4, 5>;
 using SmallCfg = Cfg<128, 128, 64, 2, 2, 2>;
 
 template <class C>
@@ -513,6 +521,7 @@ hipError_t launch_table(int epi, GemmTable& t, int tile, hipStream_t s) {
       case 1: return launch_cfg<Big4>(epi, t, s);
       case 2: return launch_cfg<Big4K64>(epi, t, s);
       case 3: return launch_cfg<Big8>(epi, t, s);
+      case 4: return launch_cfg<Big8S5>(epi, t, s);
       default: return launch_cfg<Big8K64>(epi, t, s);
     }
   }
@@ -572,7 +581,7 @@ hipError_t launch_poly(const NsGroup* g, int n, float b, float c, hipStream_t s)
 }
 
 hipError_t launch_combine(const NsGroup* g, int n, float alpha, const float* const* scale,
-                          hipStream_t s) {
+                          bool last, hipStream_t s) {
   GemmTable t{};
   t.ngroups = n;
   for (int i = 0; i < n; ++i) {
@@ -583,7 +592,9 @@ hipError_t launch_combine(const NsGroup* g, int n, float alpha, const float* con
     a.strideA = p.m_pad * p.m_pad;
     a.strideB = p.m_pad * p.n_pad;
     a.kdim = static_cast<int>(p.m_pad);
-    a.C = g[i].Xn; a.C2 = g[i].XTn;
+    // the last iteration writes only the orientation the update reads
+    a.C = (last && p.transposed) ? nullptr : g[i].Xn;
+    a.C2 = (last && !p.transposed) ? nullptr : g[i].XTn;
     a.ldc = p.n_pad; a.ldc2 = p.m_pad;
     a.strideC = a.strideC2 = p.m_pad * p.n_pad;
     a.aux = g[i].XT;  // X[i][j] read as X^T[j][i]
