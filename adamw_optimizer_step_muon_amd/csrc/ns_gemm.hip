@@ -28,9 +28,9 @@
 //   * blocks are renumbered so each XCD (blocks go round-robin to the 8 XCDs) works
 //     on a contiguous run of tiles, and those runs are grouped by row panels, so
 //     the blocks resident on one XCD share operand panels in its L2;
-//   * epilogue in registers (a/b/c terms in fp32, round to bf16), row-major stores
-//     straight from the accumulator layout, the transposed / mirrored copy through
-//     an XOR-swizzled LDS tile with 16-byte stores.
+//   * epilogue: a/b/c terms in fp32 in registers, round to bf16; each orientation
+//     (row-major, and the transposed / mirrored copy) is staged through an
+//     XOR-swizzled LDS tile and written with 16-byte row stores.
 // Sizes are padded to the tile by the caller and the padding is zero (preserved by
 // the iteration), so there are no bounds checks inside.
 #include <cstdlib>
@@ -97,13 +97,15 @@ struct Cfg {
 };
 
 // 16-byte chunk swizzle inside an operand row (an involution in c).  A fragment read
-// has 32 lanes on 32 consecutive rows at one logical chunk; the swizzle spreads every
-// 16 lanes over 16 distinct 16-byte slots of a 256-byte bank row (and every 8 lanes
-// over the 8 slots of 128 bytes), so the b128 reads are free of bank conflicts.
+// has 32 lanes on 32 consecutive rows at one logical chunk (the other half-wave on the
+// next chunk).  Both masks were measured free of bank conflicts for that read on gfx950
+// (ds_read_b128 throughput at 16 waves per CU equal to the best pattern; the 64-byte
+// row mask ((r >> 1) ^ (r >> 3)) & 3, which also looks conflict-free on a plain 64-bank
+// model, measured 2-way).
 template <int BK>
 __device__ __forceinline__ int swz(int r, int c) {
   if constexpr (BK == 64) return c ^ ((r ^ (r >> 3)) & 7);         // 8 chunks per row
-  else return c ^ (((r >> 1) ^ (r >> 3)) & 3);                     // 4 chunks per row
+  else return c ^ ((r ^ (r >> 2)) & 3);                            // 4 chunks per row
 }
 
 // wait until at most n vector-memory operations of this wave are outstanding
@@ -360,15 +362,12 @@ __global__ __launch_bounds__(C::kThreads) void ns_gemm_kernel(GemmTable table) {
   // the update reads)
   const bool need_t = (kEpi == kCombine) ? (args.C2 != nullptr) : mirror;
   const bool need_c = (kEpi != kCombine) || (args.C != nullptr);
-  constexpr int kTChunks = C::BM / 8;  // 16-byte chunks per row of the transposed tile
-  unsigned short* Ts = smem;           // [BN][BM], chunk c of row j at c ^ (j % kTChunks)
-  unsigned short* Cp = args.C + batch * args.strideC;
   const unsigned short* auxT =
       (kEpi == kGram) ? nullptr : args.aux + batch * args.strideAux;
-  if (need_t) __syncthreads();  // every wave is done reading the operand stages
   float sc = 1.0f;
   if (kEpi != kPoly && args.scale) sc = args.scale[batch];
 
+  // 1. final values in fp32, in place in the accumulators
   constexpr int kHalves = C::WTM >= 2 ? 2 : 1;  // aux loads in two batches (registers)
 #pragma unroll
   for (int hh = 0; hh < kHalves; ++hh) {
@@ -398,13 +397,9 @@ __global__ __launch_bounds__(C::kThreads) void ns_gemm_kernel(GemmTable table) {
     for (int ii = 0; ii < kI; ++ii) {
       const int i = hh * kI + ii;
 #pragma unroll
-      for (int j = 0; j < C::WTN; ++j) {
-        const int jl = wn * (C::WTN * 32) + j * 32 + (lane & 31);
-        const int64_t gj = n0 + jl;
+      for (int j = 0; j < C::WTN; ++j)
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const int il0 = wm * (C::WTM * 32) + i * 32 + 8 * q + 4 * fkh;
-          unsigned short h[4];
+        for (int q = 0; q < 4; ++q)
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
             float v = acc[i][j][q * 4 + e];
@@ -415,21 +410,67 @@ __global__ __launch_bounds__(C::kThreads) void ns_gemm_kernel(GemmTable table) {
             } else {
               v = (sc * sc) * v;
             }
-            h[e] = f2bf(v);
-            if (need_c) Cp[(m0 + il0 + e) * args.ldc + gj] = h[e];
+            acc[i][j][q * 4 + e] = v;
           }
-          if (need_t) {
-            u32x2 packed;
-            packed[0] = static_cast<unsigned>(h[0]) | (static_cast<unsigned>(h[1]) << 16);
-            packed[1] = static_cast<unsigned>(h[2]) | (static_cast<unsigned>(h[3]) << 16);
-            const int c = il0 >> 3, half = (il0 >> 2) & 1;
-            *reinterpret_cast<u32x2*>(Ts + jl * C::BM + ((c ^ (jl % kTChunks)) * 8) + half * 4) = packed;
-          }
-        }
-      }
     }
   }
+
+  // 2. each orientation goes through LDS (bf16) and out with 16-byte row stores
+  __syncthreads();  // every wave is done reading the operand stages
+  if (need_c) {
+    // row-major tile [BM][BN]: 2-byte writes, chunk c of row r at c ^ (r % kCChunks)
+    // (the two half-waves write rows 4 apart, which land on different 64-byte groups)
+    constexpr int kCChunks = C::BN / 8;
+    unsigned short* Cs = smem;
+#pragma unroll
+    for (int i = 0; i < C::WTM; ++i)
+#pragma unroll
+      for (int j = 0; j < C::WTN; ++j) {
+        const int jl = wn * (C::WTN * 32) + j * 32 + (lane & 31);
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const int r = wm * (C::WTM * 32) + i * 32 + 8 * q + 4 * fkh + e;
+            Cs[r * C::BN + ((((jl >> 3) ^ (r % kCChunks)) << 3) | (jl & 7))] = f2bf(acc[i][j][q * 4 + e]);
+          }
+      }
+    __syncthreads();
+    unsigned short* Cp = args.C + batch * args.strideC;
+    constexpr int kAll = C::BM * kCChunks;
+    static_assert(kAll % C::kThreads == 0, "epilogue copy");
+#pragma unroll
+    for (int it = 0; it < kAll / C::kThreads; ++it) {
+      const int idx = tid + it * C::kThreads;
+      const int row = idx / kCChunks;
+      const int c = idx - row * kCChunks;
+      const u32x4 v = *reinterpret_cast<const u32x4*>(Cs + row * C::BN + ((c ^ (row % kCChunks)) * 8));
+      *reinterpret_cast<u32x4*>(Cp + (m0 + row) * args.ldc + n0 + c * 8) = v;
+    }
+    if (need_t) __syncthreads();  // the transposed tile reuses the buffer
+  }
   if (!need_t) return;
+  // transposed tile [BN][BM]: a lane's 4 consecutive rows are one 8-byte write,
+  // chunk c of row j at c ^ (j % kTChunks)
+  constexpr int kTChunks = C::BM / 8;
+  unsigned short* Ts = smem;
+#pragma unroll
+  for (int i = 0; i < C::WTM; ++i)
+#pragma unroll
+    for (int j = 0; j < C::WTN; ++j) {
+      const int jl = wn * (C::WTN * 32) + j * 32 + (lane & 31);
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int il0 = wm * (C::WTM * 32) + i * 32 + 8 * q + 4 * fkh;
+        u32x2 packed;
+        packed[0] = static_cast<unsigned>(f2bf(acc[i][j][q * 4 + 0])) |
+                    (static_cast<unsigned>(f2bf(acc[i][j][q * 4 + 1])) << 16);
+        packed[1] = static_cast<unsigned>(f2bf(acc[i][j][q * 4 + 2])) |
+                    (static_cast<unsigned>(f2bf(acc[i][j][q * 4 + 3])) << 16);
+        const int c = il0 >> 3, half = (il0 >> 2) & 1;
+        *reinterpret_cast<u32x2*>(Ts + jl * C::BM + ((c ^ (jl % kTChunks)) * 8) + half * 4) = packed;
+      }
+    }
   __syncthreads();
   unsigned short* C2 = args.C2 + batch * args.strideC2;
   constexpr int kAll = C::BN * kTChunks;
@@ -447,14 +488,12 @@ __global__ __launch_bounds__(C::kThreads) void ns_gemm_kernel(GemmTable table) {
 // Tile shapes.  Big: 256 x 256 per block (128 KiB LDS, one block per CU); the default
 // runs 8 waves of 128 x 64 over 2 stages of k = 64 (one barrier per 64 of k).  Small:
 // 128 x 128, 4 waves of 64 x 64, 2 stages of k = 64 (64 KiB, two blocks per CU) for
-// Gram sides too short to fill the chip.  Other big variants stay compiled for tuning
-// (MA_NS_BIG=1: 4 waves k=32 x 4 stages, 2: 4 waves k=64 x 2, 3: 8 waves k=32 x 4).
+// Gram sides too short to fill the chip.  MA_NS_BIG=1 selects 8 waves over 4 stages of
+// k = 32 instead (deeper prefetch, twice the barriers; measured 3-6 % slower).
 using Big8K64 = Cfg<256, 256, 64, 2, 4, 2>;
-using Big4 = Cfg<256, 256, 32, 2, 2, 4>;
-using Big4K64 = Cfg<256, 256, 64, 2, 2, 2>;
 using Big8 = Cfg<256, 256, 32, 2, 4, 4>;
-using Big8S5 = Cfg<256, 256, 32, 2, 4, 5>;
 using SmallCfg = Cfg<128, 128, 64, 2, 2, 2>;
+enum TileCfg { kTileSmall = 0, kTileBig = 1 };
 
 template <class C>
 hipError_t launch_cfg(int epi, const GemmTable& t, hipStream_t s) {
@@ -482,8 +521,8 @@ int env_int(const char* name, int dflt) {
   return e ? std::atoi(e) : dflt;
 }
 
-// Fill the tile-grid and tile-order fields of one group's arguments.
-void set_tiles(int epi, GemmArgs& a, const BucketPlan& p) {
+// Fill the tile-grid and tile-order fields of one group's arguments (bm x bn tiles).
+void set_tiles(int epi, GemmArgs& a, const BucketPlan& p, int bm, int bn) {
   // Defaults measured on the MI355X (env knobs for tuning): bands of 4 row panels for
   // both tile orders, XCD renumbering on, spread DMA issue for 256-tiles only.
   static const int band_combine = env_int("MA_NS_BAND_COMBINE", 4);
@@ -492,19 +531,18 @@ void set_tiles(int epi, GemmArgs& a, const BucketPlan& p) {
   static const int spread = env_int("MA_NS_SPREAD", -1);
   a.band = epi == kCombine ? (band_combine > 0 ? band_combine : 1) : band_tri;
   a.xcd_remap = xcd;
-  a.spread = spread >= 0 ? spread : (p.tile == 256 ? 1 : 0);
-  const int T = p.tile;
+  a.spread = spread >= 0 ? spread : (bm == 256 ? 1 : 0);
   if (epi == kCombine) {
-    a.tiles_m = static_cast<int>(p.m_pad / T);
-    a.tiles_n = static_cast<int>(p.n_pad / T);
+    a.tiles_m = static_cast<int>(p.m_pad / bm);
+    a.tiles_n = static_cast<int>(p.n_pad / bn);
     a.tiles_per_batch = a.tiles_m * a.tiles_n;
   } else {
-    a.tiles_m = a.tiles_n = static_cast<int>(p.m_pad / T);
+    a.tiles_m = a.tiles_n = static_cast<int>(p.m_pad / bm);
     a.tiles_per_batch = a.tiles_m * (a.tiles_m + 1) / 2;
   }
 }
 
-hipError_t launch_table(int epi, GemmTable& t, int tile, hipStream_t s) {
+hipError_t launch_table(int epi, GemmTable& t, TileCfg cfg, hipStream_t s) {
   // longest contraction first, so the blocks with the most work are dispatched first
   for (int i = 1; i < t.ngroups; ++i)
     for (int j = i; j > 0 && t.g[j].kdim > t.g[j - 1].kdim; --j) {
@@ -516,17 +554,12 @@ hipError_t launch_table(int epi, GemmTable& t, int tile, hipStream_t s) {
   for (int i = 0; i < t.ngroups; ++i)
     t.start[i + 1] = t.start[i] + ((t.g[i].tiles_per_batch * t.g[i].tiles_k + 7) & ~7);
   for (int i = t.ngroups + 1; i <= kMaxGemmGroups; ++i) t.start[i] = t.start[t.ngroups];
-  if (tile == 256) {
-    switch (big_variant()) {
-      case 1: return launch_cfg<Big4>(epi, t, s);
-      case 2: return launch_cfg<Big4K64>(epi, t, s);
-      case 3: return launch_cfg<Big8>(epi, t, s);
-      case 4: return launch_cfg<Big8S5>(epi, t, s);
-      default: return launch_cfg<Big8K64>(epi, t, s);
-    }
-  }
+  if (cfg == kTileBig)
+    return big_variant() == 1 ? launch_cfg<Big8>(epi, t, s) : launch_cfg<Big8K64>(epi, t, s);
   return launch_cfg<SmallCfg>(epi, t, s);
 }
+
+TileCfg square_cfg(const BucketPlan& p) { return p.tile == 256 ? kTileBig : kTileSmall; }
 
 }  // namespace
 
@@ -552,9 +585,9 @@ hipError_t launch_gram(const NsGroup* g, int n, const float* const* scale, hipSt
     a.strideC = a.strideC2 = p.m_pad * p.m_pad;
     a.scale = scale ? scale[i] : nullptr;
     a.tiles_k = static_cast<int>(p.K);
-    set_tiles(kGram, a, p);
+    set_tiles(kGram, a, p, p.tile, p.tile);
   }
-  return launch_table(kGram, t, g[0].plan->tile, s);
+  return launch_table(kGram, t, square_cfg(*g[0].plan), s);
 }
 
 hipError_t launch_poly(const NsGroup* g, int n, float b, float c, hipStream_t s) {
@@ -575,13 +608,14 @@ hipError_t launch_poly(const NsGroup* g, int n, float b, float c, hipStream_t s)
     a.strideAux = p.m_pad * p.m_pad;
     a.alpha = b; a.beta = c;
     a.tiles_k = static_cast<int>(p.K);
-    set_tiles(kPoly, a, p);
+    set_tiles(kPoly, a, p, p.tile, p.tile);
   }
-  return launch_table(kPoly, t, g[0].plan->tile, s);
+  return launch_table(kPoly, t, square_cfg(*g[0].plan), s);
 }
 
 hipError_t launch_combine(const NsGroup* g, int n, float alpha, const float* const* scale,
                           bool last, hipStream_t s) {
+  const TileCfg cfg = square_cfg(*g[0].plan);
   GemmTable t{};
   t.ngroups = n;
   for (int i = 0; i < n; ++i) {
@@ -603,9 +637,9 @@ hipError_t launch_combine(const NsGroup* g, int n, float alpha, const float* con
     a.alpha = alpha; a.beta = 1.0f;
     a.scale = scale ? scale[i] : nullptr;
     a.tiles_k = static_cast<int>(p.K);
-    set_tiles(kCombine, a, p);
+    set_tiles(kCombine, a, p, p.tile, p.tile);
   }
-  return launch_table(kCombine, t, g[0].plan->tile, s);
+  return launch_table(kCombine, t, cfg, s);
 }
 
 }  // namespace ma
