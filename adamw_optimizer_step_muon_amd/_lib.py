@@ -24,7 +24,7 @@ MA_MAX_NS_STEPS = 64
 
 EXPORTED = (
     "ma_abi_version", "ma_status_string", "ma_last_error", "ma_muon_route_of",
-    "ma_muon_workspace_bytes", "ma_muon_step", "ma_adamw_step",
+    "ma_muon_workspace_bytes", "ma_muon_phases", "ma_muon_step", "ma_adamw_step",
     "ma_newton_schulz_workspace_bytes", "ma_newton_schulz",
 )
 
@@ -97,6 +97,9 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.ma_muon_workspace_bytes.restype = ctypes.c_size_t
     lib.ma_muon_workspace_bytes.argtypes = [ctypes.POINTER(_MuonBucket), ctypes.c_int32,
                                             ctypes.POINTER(_MuonHParams)]
+    lib.ma_muon_phases.restype = ctypes.c_int32
+    lib.ma_muon_phases.argtypes = [ctypes.POINTER(_MuonBucket), ctypes.c_int32,
+                                   ctypes.POINTER(ctypes.c_int32)]
     lib.ma_muon_step.restype = ctypes.c_int
     lib.ma_muon_step.argtypes = [ctypes.POINTER(_MuonBucket), ctypes.c_int32,
                                  ctypes.POINTER(_MuonHParams), ctypes.c_void_p, ctypes.c_size_t,
@@ -205,6 +208,20 @@ def muon_workspace_bytes(shapes: Sequence[Sequence[int]]) -> int:
     for i, (K, A, B) in enumerate(shapes):
         arr[i] = _MuonBucket(int(K), int(A), int(B), 0, 0, 0)
     return int(load().ma_muon_workspace_bytes(arr, len(shapes), None))
+
+
+def muon_phases(shapes: Sequence[Sequence[int]]):
+    """(number of phases, phase index per bucket) for buckets of these (K, A, B) shapes:
+    each phase runs 3 x ns_steps Newton-Schulz GEMM launches (ma_muon_phases)."""
+    n = len(shapes)
+    arr = (_MuonBucket * max(n, 1))()
+    for i, (K, A, B) in enumerate(shapes):
+        arr[i] = _MuonBucket(int(K), int(A), int(B), 0, 0, 0)
+    out = (ctypes.c_int32 * max(n, 1))()
+    count = int(load().ma_muon_phases(arr, n, out))
+    if count < 0:
+        _check(count)
+    return count, [int(out[i]) for i in range(n)]
 
 
 def muon_step(buckets, *, lr: float, momentum: float = 0.95, weight_decay: float = 0.0,

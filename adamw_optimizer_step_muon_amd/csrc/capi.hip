@@ -295,6 +295,25 @@ size_t ma_muon_workspace_bytes(const ma_muon_bucket* buckets, int32_t n_buckets,
   return need;
 }
 
+int32_t ma_muon_phases(const ma_muon_bucket* buckets, int32_t n_buckets, int32_t* phase_of) {
+  g_last_error.clear();
+  if (n_buckets < 0) return fail(MA_ERR_INVALID_ARG, "n_buckets %d < 0", n_buckets);
+  if (n_buckets > 0 && !buckets) return fail(MA_ERR_INVALID_ARG, "buckets is NULL");
+  for (int32_t i = 0; i < n_buckets; ++i) {
+    const ma_status st = check_shape(buckets[i].K, buckets[i].A, buckets[i].B);
+    if (st != MA_OK) return fail(st, "bucket %d: %s", i, g_last_error.c_str());
+    if (phase_of) phase_of[i] = -1;
+  }
+  int32_t count = 0;
+  for_each_phase(buckets, n_buckets, [&](const Phase& ph) {
+    if (phase_of)
+      for (int j = 0; j < ph.n; ++j) phase_of[ph.bucket[j]] = count;
+    ++count;
+    return MA_OK;
+  });
+  return count;
+}
+
 ma_status ma_muon_step(const ma_muon_bucket* buckets, int32_t n_buckets,
                        const ma_muon_hparams* hp, void* workspace, size_t workspace_bytes,
                        void* stream, ma_muon_route* route_out) {

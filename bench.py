@@ -203,8 +203,10 @@ def main():
     reps = max(3, args.steps)
     muon_ms = timed(lambda: muon(mh.ns_steps), reps)
     muon0_ms = timed(lambda: muon(0), reps)
-    ns_ms = max(muon_ms - muon0_ms, 1e-9)          # the 3 x ns_steps GEMM launches per bucket
-    launches = 3 * mh.ns_steps * len(wl.muon)
+    ns_ms = max(muon_ms - muon0_ms, 1e-9)          # exactly the Newton-Schulz GEMM launches
+    # same-tile buckets share launches: 3 x ns_steps per phase of the bucket list
+    phases, _ = ma.muon_phases([(b.K, b.A, b.B) for b in wl.muon])
+    launches = 3 * mh.ns_steps * phases
     flops = ns_flops(wl)
     ns_tflops = flops / (ns_ms * 1e-3) / 1e12
     state["t"] = 1

@@ -123,6 +123,14 @@ ma_status ma_muon_route_of(int64_t A, int64_t B, const ma_muon_hparams* hp, ma_m
 size_t ma_muon_workspace_bytes(const ma_muon_bucket* buckets, int32_t n_buckets,
                                const ma_muon_hparams* hp);
 
+/* Host only: how ma_muon_step groups the buckets (the phases of
+ * ma_muon_workspace_bytes).  Each phase runs 3 x ns_steps Newton-Schulz GEMM launches
+ * (Gram, polynomial, combine per iteration) covering all of its buckets.  Returns the
+ * number of phases, or a negative ma_status for invalid arguments (NULL buckets with
+ * n_buckets > 0, n_buckets < 0, K < 0, A or B < 1 with K > 0).  phase_of: host, NULL or
+ * n_buckets entries, receives each bucket's phase index (-1 for an empty bucket). */
+int32_t ma_muon_phases(const ma_muon_bucket* buckets, int32_t n_buckets, int32_t* phase_of);
+
 /* One Muon step on every bucket [HB], in this order per bucket:
  *   M <- mu M + G;  U <- G + mu M (nesterov) or M;  X0 <- U / (||U||_F + ns_eps)  (bf16,
  *   transposed when A > B);  ns_steps times: R <- X X^T, P <- b R + c R R,

@@ -74,6 +74,26 @@ def test_workspace_bytes(lib):
     assert ma.muon_workspace_bytes([(0, 10, 10)]) == 0
 
 
+def test_phases(lib):
+    import workloads
+    assert ma.muon_phases([]) == (0, [])
+    # the 12-layer GPT's three 128-tile buckets share one phase
+    shapes = [(b.K, b.A, b.B) for b in workloads.workload(1).muon]
+    assert ma.muon_phases(shapes) == (1, [0, 0, 0])
+    # owner subset: every bucket needs more than the 4 GiB a phase may hold
+    shapes = [(b.K, b.A, b.B) for b in workloads.workload(4).muon]
+    assert ma.muon_phases(shapes) == (3, [0, 1, 2])
+    # at most four buckets per phase; empty buckets belong to none
+    count, of = ma.muon_phases([(1, 64, 64)] * 5 + [(0, 64, 64)])
+    assert (count, of) == (2, [0, 0, 0, 0, 1, -1])
+    # a change of tile closes the phase: the workspace is the maximum over phases
+    shapes = [(1, 64, 64), (16, 8192, 8192), (1, 64, 64)]
+    assert ma.muon_phases(shapes)[0] == 3
+    assert ma.muon_workspace_bytes(shapes) == ma.muon_workspace_bytes([shapes[1]])
+    with pytest.raises(ma.MuonAdamWError):
+        ma.muon_phases([(1, 0, 5)])
+
+
 def _hp(**kw):
     base = dict(lr=0.02, momentum=0.95, weight_decay=0.1, ns_eps=1e-7, nesterov=1,
                 cautious_wd=0, ns_steps=5, scale_mode=0)
