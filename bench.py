@@ -63,9 +63,9 @@ def source_hash(name):
         return hashlib.sha256(f.read()).hexdigest()[:16]
 
 
-def counted_traffic(summary, source):
-    """HBM bytes per launch from a committed rocprofv3 FETCH_SIZE/WRITE_SIZE summary,
-    or None when the summary is missing or the kernel source changed since."""
+def counted_traffic(summary, source, key="traffic_bytes_per_launch"):
+    """A figure (HBM bytes per launch by default) from a committed rocprofv3 counter
+    summary, or None when the summary is missing or the kernel source changed since."""
     path = os.path.join(PROFILES, summary)
     if not os.path.exists(path):
         return None
@@ -78,7 +78,7 @@ def counted_traffic(summary, source):
     if vals.get("source_sha256") != source_hash(source):
         return None
     try:
-        return float(vals["traffic_bytes_per_launch"])
+        return float(vals[key])
     except (KeyError, ValueError):
         return None
 
@@ -244,6 +244,10 @@ def main():
             "unit": "TFLOP/s",
             "frac": round(ns_tflops / MFMA_BF16_PEAK_TFLOPS, 4),
             "traffic": counted_traffic(f"ns_gemm_traffic_workload{args.workload}.txt", "ns_gemm.hip"),
+            # fraction of the kernel's cycles the matrix cores were busy (rocprofv3
+            # SQ_VALU_MFMA_BUSY_CYCLES / GRBM_GUI_ACTIVE, at the clock the part ran)
+            "mfma_busy_counter": counted_traffic(f"ns_gemm_mfma_workload{args.workload}.txt",
+                                                 "ns_gemm.hip", key="mfma_busy"),
             "flops_per_launch": flops / launches,
             "avg_launch_ms": ns_ms / launches,
         },
