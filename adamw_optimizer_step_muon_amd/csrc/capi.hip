@@ -101,7 +101,8 @@ ma_muon_route route_of(const BucketPlan& p, int ns_steps) {
   return r;
 }
 
-// Buckets run in phases: consecutive buckets with the same GEMM tile, at most
+// Buckets run in phases: consecutive buckets with the same GEMM tile (and the same
+// choice of keeping X^T, which fixes the combine's operand layout), at most
 // kMaxGemmGroups of them and kPhaseBytes of workspace together, share each Newton-Schulz
 // launch (short Gram sides fill the chip together); each has its own workspace region.
 constexpr size_t kPhaseBytes = size_t(4) << 30;
@@ -117,7 +118,7 @@ struct Phase {
 
 bool phase_accepts(const Phase& ph, const BucketPlan& p) {
   return ph.n > 0 && ph.n < kMaxGemmGroups && ph.tile == p.tile &&
-         ph.bytes + p.bytes <= kPhaseBytes;
+         ph.plan[0].keeps_xt == p.keeps_xt && ph.bytes + p.bytes <= kPhaseBytes;
 }
 
 void phase_add(Phase& ph, const BucketPlan& p, int bucket) {
@@ -152,8 +153,9 @@ T* at(char* ws, size_t off) {
   return reinterpret_cast<T*>(ws + off);
 }
 
-// Newton-Schulz for every bucket of a phase whose unnormalised bf16 U sits in its X[0] /
-// XT[0] and whose normalisers inv[k] = 1 / (||U_k|| + eps) are in its workspace.  On
+// Newton-Schulz for every bucket of a phase whose unnormalised bf16 U sits in its X[0]
+// (and, with no iteration, in its own orientation in X[1]) and whose normalisers
+// inv[k] = 1 / (||U_k|| + eps) are in its workspace.  On
 // return out[j] holds bucket j's result in the matrix's own orientation (row stride
 // ldo[j]) and oscale[j] the per-matrix factor still to apply (inv when no iteration ran).
 ma_status run_ns(const Phase& ph, const ma_muon_hparams* hp, char* ws, hipStream_t s,
@@ -168,9 +170,9 @@ ma_status run_ns(const Phase& ph, const ma_muon_hparams* hp, char* ws, hipStream
       char* w = ws + ph.base[j];
       g[j].plan = &p;
       g[j].X = at<unsigned short>(w, p.off_x[cur]);
-      g[j].XT = at<unsigned short>(w, p.off_xt[cur]);
       g[j].Xn = at<unsigned short>(w, p.off_x[cur ^ 1]);
-      g[j].XTn = at<unsigned short>(w, p.off_xt[cur ^ 1]);
+      g[j].XT = p.keeps_xt ? at<unsigned short>(w, p.off_xt[cur]) : nullptr;
+      g[j].XTn = p.keeps_xt ? at<unsigned short>(w, p.off_xt[cur ^ 1]) : nullptr;
       g[j].R = at<unsigned short>(w, p.off_r);
       g[j].P = at<unsigned short>(w, p.off_p);
     }
@@ -188,8 +190,15 @@ ma_status run_ns(const Phase& ph, const ma_muon_hparams* hp, char* ws, hipStream
   for (int j = 0; j < ph.n; ++j) {
     const BucketPlan& p = ph.plan[j];
     char* w = ws + ph.base[j];
-    // own orientation: X (m_pad x n_pad) if not transposed, X^T (n_pad x m_pad) if it is
-    out[j] = at<unsigned short>(w, p.transposed ? p.off_xt[cur] : p.off_x[cur]);
+    // own orientation: X (m_pad x n_pad) if not transposed, X^T (n_pad x m_pad) if it is;
+    // written by the last combine, or by the cast when no iteration ran (one-orientation
+    // buckets: the transposed bucket's own orientation then sits in X[1])
+    if (p.keeps_xt) {
+      out[j] = at<unsigned short>(w, p.transposed ? p.off_xt[cur] : p.off_x[cur]);
+    } else {
+      const int o = (hp->ns_steps == 0 && p.transposed) ? 1 : cur;
+      out[j] = at<unsigned short>(w, p.off_x[o]);
+    }
     ldo[j] = p.transposed ? p.m_pad : p.n_pad;
     oscale[j] = hp->ns_steps == 0 ? inv[j] : nullptr;
   }
@@ -199,8 +208,15 @@ ma_status run_ns(const Phase& ph, const ma_muon_hparams* hp, char* ws, hipStream
 // momentum update + bf16 cast + norm of one bucket into its workspace region
 ma_status prep_bucket(const BucketPlan& p, const float* grad, float* momentum,
                       const ma_muon_hparams* hp, char* w, hipStream_t s) {
-  unsigned short* S = at<unsigned short>(w, p.transposed ? p.off_xt[0] : p.off_x[0]);
-  unsigned short* T = at<unsigned short>(w, p.transposed ? p.off_x[0] : p.off_xt[0]);
+  // X0 (the Gram-side orientation) in X[0], and X0^T in XT[0] for 256-tile buckets; a
+  // one-orientation transposed bucket with no iteration also needs its own
+  // orientation, in X[1]
+  unsigned short* X0 = at<unsigned short>(w, p.off_x[0]);
+  unsigned short* XT0 = p.keeps_xt ? at<unsigned short>(w, p.off_xt[0]) : nullptr;
+  unsigned short* own = p.keeps_xt ? XT0
+                        : (hp->ns_steps == 0 ? at<unsigned short>(w, p.off_x[1]) : nullptr);
+  unsigned short* S = p.transposed ? own : X0;   // the matrix's own orientation
+  unsigned short* T = p.transposed ? X0 : XT0;   // its transpose
   float* partials = at<float>(w, p.off_part);
   float* inv = at<float>(w, p.off_inv);
   hipError_t e = launch_muon_prep(p, grad, momentum, momentum ? hp->momentum : 0.0f,
@@ -232,11 +248,12 @@ BucketPlan plan_bucket(int64_t K, int64_t A, int64_t B) {
   const size_t xb = static_cast<size_t>(K * p.m_pad * p.n_pad) * 2;
   const size_t rb = static_cast<size_t>(K * p.m_pad * p.m_pad) * 2;
   size_t off = 0;
+  p.keeps_xt = p.tile == 256 && p.m_pad > 2048;
   for (int i = 0; i < 2; ++i) {
     p.off_x[i] = off;
     off = align256(off + xb);
     p.off_xt[i] = off;
-    off = align256(off + xb);
+    if (p.keeps_xt) off = align256(off + xb);
   }
   p.off_r = off;
   off = align256(off + rb);

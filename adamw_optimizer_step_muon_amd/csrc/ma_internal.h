@@ -38,7 +38,11 @@ struct BucketPlan {
   int64_t m, n, m_pad, n_pad;
   int64_t nblk;  // momentum/cast tiles per matrix (one partial sum of U^2 each)
   // byte offsets inside the workspace
-  size_t off_x[2], off_xt[2], off_r, off_p, off_part, off_inv, bytes;
+  size_t off_x[2], off_r, off_p, off_part, off_inv, bytes;
+  // buckets with 256-tiles and a Gram side above 2048 also keep X^T (n_pad x m_pad),
+  // which their combine reads
+  bool keeps_xt;
+  size_t off_xt[2];
 };
 
 BucketPlan plan_bucket(int64_t K, int64_t A, int64_t B);
@@ -53,8 +57,8 @@ struct NsCoeffs {
 };
 
 // M <- mu M + G (when M != nullptr), U = G + mu M_new | M_new | G, cast to bf16 as the
-// orientation copy S (Ap x Bp) and transposed copy T (Bp x Ap), zero in the padding;
-// per-tile sums of U^2.
+// orientation copy S (Ap x Bp) and/or the transposed copy T (Bp x Ap) (either may be
+// null), zero in the padding; per-tile sums of U^2.
 hipError_t launch_muon_prep(const BucketPlan& p, const float* G, float* M, float mu,
                             int nesterov, float* partials, unsigned short* S,
                             unsigned short* T, hipStream_t s);
@@ -67,8 +71,9 @@ constexpr int kMaxGemmGroups = 4;
 struct NsGroup {
   const BucketPlan* plan;
   unsigned short* X;    // current iterate, m_pad x n_pad per matrix
-  unsigned short* XT;   // its transpose, n_pad x m_pad
-  unsigned short* Xn;   // next iterate and its transpose
+  unsigned short* Xn;   // next iterate (one-orientation buckets: the last iteration of
+                        // a transposed bucket writes its transpose here)
+  unsigned short* XT;   // X^T and the next X^T, n_pad x m_pad (keeps_xt buckets only)
   unsigned short* XTn;
   unsigned short* R;    // m_pad x m_pad
   unsigned short* P;
@@ -77,8 +82,9 @@ struct NsGroup {
 hipError_t launch_gram(const NsGroup* g, int n, const float* const* scale, hipStream_t s);
 // P = b R + c R R^T (lower-triangle tiles, mirrored)
 hipError_t launch_poly(const NsGroup* g, int n, float b, float c, hipStream_t s);
-// Xn = a X + P X (times scale[i][k] where given), written row-major and transposed;
-// with `last`, only the orientation of the parameter (X^T when A > B, else X)
+// Xn = a X + P X (times scale[i][k] where given), written row-major (and as X^T into
+// XTn for keeps_xt buckets); with `last`, only in the orientation of the parameter
+// (X^T when A > B: n_pad x m_pad, into XTn, or into Xn for one-orientation buckets)
 hipError_t launch_combine(const NsGroup* g, int n, float a, const float* const* scale,
                           bool last, hipStream_t s);
 // param <- param - lr*wd*mask*param - lr*scale*O with O = oscale[k] * (bf16 O) (oscale

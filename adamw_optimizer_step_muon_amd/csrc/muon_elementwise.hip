@@ -3,9 +3,9 @@
 // "Optimizers: AdamW, Muon and the distributed optimizer", section "Muon:
 // orthogonalising the update" (update steps 1-3 and the newton_schulz listing):
 //   prep:      one pass per 64 x 64 tile: M <- mu M + G, U = G + mu M (Nesterov, new M)
-//              or M; U in bf16, written in the matrix's own orientation and transposed
-//              (the Gram side is the short side: transposed when A > B); per-tile sums
-//              of U^2.  U is cast before it is normalised: the normalisation is a
+//              or M; U in bf16 in the Gram-side orientation X (transposed when A > B,
+//              through an LDS tile), and in the matrix's own orientation too when no
+//              iteration runs; per-tile sums of U^2.  U is cast before it is normalised: the normalisation is a
 //              scalar per matrix, applied by the first Newton-Schulz products
 //              (R = inv^2 U U^T, X1 = inv (a U + P U)), which is X0 = inv U up to the
 //              order of rounding, and saves a second pass over G and M.
@@ -40,6 +40,7 @@ __device__ __forceinline__ float nesterov_input(float g, float m_new, float mu, 
 
 // grid (Bp/64, Ap/64, K).  Source A x B; S is the same orientation padded to Ap x Bp
 // (row stride Bp), T the transpose padded to Bp x Ap (row stride Ap); zero padding.
+// Either may be null (only the Gram-side orientation X is needed by the iteration).
 // partials[k * tiles + tile] = sum of U^2 over the tile (fixed order).
 template <bool kVec, bool kHasM>
 __global__ __launch_bounds__(kThreads) void muon_prep_kernel(
@@ -54,8 +55,8 @@ __global__ __launch_bounds__(kThreads) void muon_prep_kernel(
   const int64_t b0 = static_cast<int64_t>(blockIdx.x) * kT;
   const float* g = G + k * A * B;
   float* mm = kHasM ? M + k * A * B : nullptr;
-  unsigned short* s = S + k * Ap * Bp;
-  unsigned short* t = T + k * Ap * Bp;
+  unsigned short* s = S ? S + k * Ap * Bp : nullptr;
+  unsigned short* t = T ? T + k * Ap * Bp : nullptr;
   const int c4 = (threadIdx.x & 15) * 4;
   float ss = 0.0f;
 #pragma unroll
@@ -106,7 +107,7 @@ __global__ __launch_bounds__(kThreads) void muon_prep_kernel(
     u32x2 packed;
     packed[0] = static_cast<unsigned>(h[0]) | (static_cast<unsigned>(h[1]) << 16);
     packed[1] = static_cast<unsigned>(h[2]) | (static_cast<unsigned>(h[3]) << 16);
-    *reinterpret_cast<u32x2*>(s + a * Bp + b) = packed;
+    if (s) *reinterpret_cast<u32x2*>(s + a * Bp + b) = packed;
   }
   ss = wave_sum(ss);
   if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = ss;
@@ -117,6 +118,7 @@ __global__ __launch_bounds__(kThreads) void muon_prep_kernel(
     for (int w = 0; w < kThreads / 64; ++w) tot += red[w];
     partials[k * gridDim.x * gridDim.y + blockIdx.y * gridDim.x + blockIdx.x] = tot;
   }
+  if (!t) return;
 #pragma unroll
   for (int r = 0; r < 4; ++r) {
     const int trow = (threadIdx.x >> 4) + 16 * r;  // local b

@@ -8,11 +8,14 @@
 //   poly:     P  = b R + c R R^T       m x m, symmetric (R R^T = R^2 as R = R^T)
 //   combine:  X' = a X + P X           m x n
 //
-// Every product is C = A B^T with both operands stored row-major along the
-// contraction index, which is the layout the MFMA operands want:
+// The Gram and polynomial products are C = A B^T with both operands stored row-major
+// along the contraction index, the layout of the MFMA operands:
 //   gram     A = B = X  (contraction over n)
 //   poly     A = B = R  (contraction over m)
-//   combine  A = P, B = X^T (the library keeps X in both orientations; contraction m)
+// The combine is C = A B with B = X stored row-major along n: its LDS stage holds k
+// rows of X and the B fragments are read with gfx950's transposing LDS load
+// (ds_read_b64_tr_b16), so X is kept in one orientation only:
+//   combine  A = P, B = X (contraction over m)
 // Symmetric outputs are computed on lower-triangle tiles only and mirrored, halving
 // the work of the two symmetric products ("DMuon: Efficient Distributed Muon Training
 // with Near-Adam Overhead", section 2.2, symmetry exploitation); same-shape matrices
@@ -50,7 +53,7 @@ struct GemmArgs {
   unsigned short* C;    // row-major target
   unsigned short* C2;   // transposed target (combine) or mirror target (gram/poly)
   int64_t ldc, ldc2, strideC, strideC2;
-  const unsigned short* aux;  // transposed a/b-term source: poly R (symmetric), combine X^T
+  const unsigned short* aux;  // a/b-term source: poly R (read transposed), combine X
   int64_t ldaux, strideAux;
   float alpha, beta;    // poly: b, c; combine: a, 1
   const float* scale;   // per-matrix factor or null: gram R *= scale^2, combine X' *= scale
@@ -70,9 +73,12 @@ struct GemmTable {
   int ngroups;
 };
 
-template <int BM_, int BN_, int BK_, int WM_, int WN_, int STAGES_>
+template <int BM_, int BN_, int BK_, int WM_, int WN_, int STAGES_, bool READS_X_>
 struct Cfg {
   static constexpr int BM = BM_, BN = BN_, BK = BK_, WM = WM_, WN = WN_, STAGES = STAGES_;
+  // combine operand B: X itself through transposing LDS reads (true), or the stored
+  // transpose X^T through plain b128 reads (false)
+  static constexpr bool kCombineReadsX = READS_X_;
   static constexpr int kWaves = WM * WN;
   static constexpr int kThreads = 64 * kWaves;
   static constexpr int WTM = BM / (WM * 32);  // 32x32 MFMA tiles per wave along M
@@ -106,6 +112,22 @@ template <int BK>
 __device__ __forceinline__ int swz(int r, int c) {
   if constexpr (BK == 64) return c ^ ((r ^ (r >> 3)) & 7);         // 8 chunks per row
   else return c ^ ((r ^ (r >> 2)) & 3);                            // 4 chunks per row
+}
+
+// 16-byte chunk swizzle of a k row of the combine's B stage ([BK][BN], n contiguous):
+// the transposing reads of one instruction cover 4 consecutive k rows of 64 bytes per
+// 16-lane group; XOR-ing the chunk with 4 (r % 4) puts those rows on distinct banks
+// (measured conflict-free on gfx950, like (r % 8) combined with higher row bits; with
+// no swizzle the read runs at about a third of the rate).
+__device__ __forceinline__ int swz_kn(int r, int c) { return c ^ ((r & 3) << 2); }
+
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef short s16x8 __attribute__((ext_vector_type(8)));
+
+// 4 bf16 of a column block: lane i of each 16-lane group receives element i % 4 of the
+// 8 bytes addressed by lane 4 e + i / 4 of its group, as element e (e = 0..3).
+__device__ __forceinline__ s16x4 lds_read_tr(const unsigned short* p) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)(p));
 }
 
 // wait until at most n vector-memory operations of this wave are outstanding
@@ -204,8 +226,10 @@ __global__ __launch_bounds__(C::kThreads) void ns_gemm_kernel(GemmTable table) {
   const int64_t m0 = static_cast<int64_t>(ti) * C::BM;
   const int64_t n0 = static_cast<int64_t>(tj) * C::BN;
 
+  // combine reading X: B is staged as k rows of BN columns starting at column n0
+  constexpr bool kBT = (kEpi == kCombine) && C::kCombineReadsX;
   const unsigned short* gA = args.A + batch * args.strideA + m0 * args.lda;
-  const unsigned short* gB = args.B + batch * args.strideB + n0 * args.ldb;
+  const unsigned short* gB = args.B + batch * args.strideB + (kBT ? n0 : n0 * args.ldb);
 
   // LDS-DMA source pointers for this lane (k offset added per stage)
   const int drow = lane / C::kChunks;  // row inside one DMA
@@ -219,8 +243,17 @@ __global__ __launch_bounds__(C::kThreads) void ns_gemm_kernel(GemmTable table) {
     const int i = isA ? d : d - C::kDmaA;
     const int r0 = (i * C::kWaves + wave) * C::kRowsPerDma;
     const int r = r0 + drow;
-    if (isA) dma16(gA + r * args.lda + k0 + swz<C::BK>(r, dpc) * 8, as + r0 * C::BK);
-    else dma16(gB + r * args.ldb + k0 + swz<C::BK>(r, dpc) * 8, bs + r0 * C::BK);
+    if (isA) {
+      dma16(gA + r * args.lda + k0 + swz<C::BK>(r, dpc) * 8, as + r0 * C::BK);
+    } else if constexpr (kBT) {
+      // [BK][BN] stage: one DMA fills kBRows k rows of BN columns (1 KiB)
+      constexpr int kBChunks = C::BN / 8, kBRows = 64 / kBChunks;
+      const int q0 = (i * C::kWaves + wave) * kBRows;
+      const int q = q0 + lane / kBChunks, pc = lane % kBChunks;
+      dma16(gB + static_cast<int64_t>(k0 + q) * args.ldb + swz_kn(q, pc) * 8, bs + q0 * C::BN);
+    } else {
+      dma16(gB + r * args.ldb + k0 + swz<C::BK>(r, dpc) * 8, bs + r0 * C::BK);
+    }
   };
   auto issue_stage = [&](int kt, int slot) {
 #pragma unroll
@@ -271,8 +304,21 @@ __global__ __launch_bounds__(C::kThreads) void ns_gemm_kernel(GemmTable table) {
     }
 #pragma unroll
     for (int j = 0; j < C::WTN; ++j) {
-      const int r = wn * (C::WTN * 32) + j * 32 + frow;
-      bfr[j] = *reinterpret_cast<const bf16x8*>(bs + r * C::BK + swz<C::BK>(r, ch) * 8);
+      if constexpr (kBT) {
+        // k rows kk*16 + 8*(lane/32) + 0..7 of column wn*.. + j*32 + lane%32, as two
+        // transposing reads of 4 rows each (same k order as the A fragment)
+        const int g16 = lane >> 4, sl = lane & 15;
+        const int col = wn * (C::WTN * 32) + j * 32 + 16 * (g16 & 1) + 4 * (sl & 3);
+        const int row = kk * 16 + 8 * (g16 >> 1) + (sl >> 2);
+        const s16x4 lo = lds_read_tr(bs + row * C::BN + swz_kn(row, col >> 3) * 8 + (col & 7));
+        const s16x4 hi =
+            lds_read_tr(bs + (row + 4) * C::BN + swz_kn(row + 4, col >> 3) * 8 + (col & 7));
+        const s16x8 both = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+        bfr[j] = __builtin_bit_cast(bf16x8, both);
+      } else {
+        const int r = wn * (C::WTN * 32) + j * 32 + frow;
+        bfr[j] = *reinterpret_cast<const bf16x8*>(bs + r * C::BK + swz<C::BK>(r, ch) * 8);
+      }
     }
   };
 
@@ -296,8 +342,18 @@ __global__ __launch_bounds__(C::kThreads) void ns_gemm_kernel(GemmTable table) {
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
               const int kl = rbase - k0 + 8 * q + 4 * fkh;  // local k of rows gi0..gi0+3
-              cap[i][j][q] = *reinterpret_cast<const u32x2*>(
-                  bs + jl * C::BK + swz<C::BK>(jl, kl >> 3) * 8 + (kl & 4));
+              if constexpr (kBT) {
+                // X[k][j] at k row kl + e of the [BK][BN] stage
+                unsigned short v[4];
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                  v[e] = bs[(kl + e) * C::BN + swz_kn(kl + e, jl >> 3) * 8 + (jl & 7)];
+                cap[i][j][q][0] = static_cast<unsigned>(v[0]) | (static_cast<unsigned>(v[1]) << 16);
+                cap[i][j][q][1] = static_cast<unsigned>(v[2]) | (static_cast<unsigned>(v[3]) << 16);
+              } else {
+                cap[i][j][q] = *reinterpret_cast<const u32x2*>(
+                    bs + jl * C::BK + swz<C::BK>(jl, kl >> 3) * 8 + (kl & 4));
+              }
             }
           }
         }
@@ -355,8 +411,9 @@ __global__ __launch_bounds__(C::kThreads) void ns_gemm_kernel(GemmTable table) {
   // ---------------- epilogue ----------------
   // MFMA 32x32 accumulator layout: lane holds column (lane & 31) of the 32x32 tile and
   // rows 8*(r/4) + 4*(lane/32) + r%4 for r = 0..15, i.e. four runs of 4 rows.
-  // The a X / b R term is read from the transposed copy (X^T for combine; R is
-  // symmetric), where a lane's 4 consecutive rows are 8 contiguous bytes.
+  // The b R term is read from R's transposed position (R is symmetric), where a lane's
+  // 4 consecutive rows are 8 contiguous bytes; the a X term from X^T the same way, or
+  // from X itself when the combine reads X.
   const bool mirror = (kEpi != kCombine) && (ti != tj);
   // the combine may skip either orientation (the last iteration keeps only the one
   // the update reads)
@@ -390,7 +447,18 @@ __global__ __launch_bounds__(C::kThreads) void ns_gemm_kernel(GemmTable table) {
             const int i = hh * kI + ii;
             const int64_t gj = n0 + wn * (C::WTN * 32) + j * 32 + (lane & 31);
             const int64_t gi0 = m0 + wm * (C::WTM * 32) + i * 32 + 8 * q + 4 * fkh;
-            ax[ii][j][q] = *reinterpret_cast<const u32x2*>(auxT + gj * args.ldaux + gi0);
+            if constexpr (kBT) {
+              // X[gi0 + e][gj], 2-byte loads (32 lanes cover 64 contiguous bytes)
+              unsigned short v[4];
+#pragma unroll
+              for (int e = 0; e < 4; ++e) v[e] = auxT[(gi0 + e) * args.ldaux + gj];
+              ax[ii][j][q][0] = static_cast<unsigned>(v[0]) | (static_cast<unsigned>(v[1]) << 16);
+              ax[ii][j][q][1] = static_cast<unsigned>(v[2]) | (static_cast<unsigned>(v[3]) << 16);
+            } else {
+              // R[gi0 + e][gj] = R[gj][gi0 + e] (poly) or X^T[gj][gi0 + e] (combine):
+              // 8 contiguous bytes
+              ax[ii][j][q] = *reinterpret_cast<const u32x2*>(auxT + gj * args.ldaux + gi0);
+            }
           }
     }
 #pragma unroll
@@ -488,12 +556,18 @@ __global__ __launch_bounds__(C::kThreads) void ns_gemm_kernel(GemmTable table) {
 // Tile shapes.  Big: 256 x 256 per block (128 KiB LDS, one block per CU); the default
 // runs 8 waves of 128 x 64 over 2 stages of k = 64 (one barrier per 64 of k).  Small:
 // 128 x 128, 4 waves of 64 x 64, 2 stages of k = 64 (64 KiB, two blocks per CU) for
-// Gram sides too short to fill the chip.  MA_NS_BIG=1 selects 8 waves over 4 stages of
+// Gram sides too short to fill the chip.  The combine reads X with transposing LDS
+// loads when the Gram side is at most 2048 (BucketPlan::keeps_xt false), so those
+// buckets keep one orientation of X and skip writing and casting X^T; longer Gram sides
+// read the stored X^T with b128 loads (two transposing loads per fragment measured
+// 15 % slower at m = 8192, where the long contraction makes the X^T write negligible,
+// and 2-3 % faster at m = 1280 and 2048).  MA_NS_BIG=1 selects 8 waves over 4 stages of
 // k = 32 instead (deeper prefetch, twice the barriers; measured 3-6 % slower).
-using Big8K64 = Cfg<256, 256, 64, 2, 4, 2>;
-using Big8 = Cfg<256, 256, 32, 2, 4, 4>;
-using SmallCfg = Cfg<128, 128, 64, 2, 2, 2>;
-enum TileCfg { kTileSmall = 0, kTileBig = 1 };
+using Big8K64 = Cfg<256, 256, 64, 2, 4, 2, false>;
+using Big8K64X = Cfg<256, 256, 64, 2, 4, 2, true>;  // combine of Gram sides <= 2048
+using Big8 = Cfg<256, 256, 32, 2, 4, 4, false>;
+using SmallCfg = Cfg<128, 128, 64, 2, 2, 2, true>;
+enum TileCfg { kTileSmall = 0, kTileBig = 1, kTileBigX = 2 };
 
 template <class C>
 hipError_t launch_cfg(int epi, const GemmTable& t, hipStream_t s) {
@@ -556,6 +630,7 @@ hipError_t launch_table(int epi, GemmTable& t, TileCfg cfg, hipStream_t s) {
   for (int i = t.ngroups + 1; i <= kMaxGemmGroups; ++i) t.start[i] = t.start[t.ngroups];
   if (cfg == kTileBig)
     return big_variant() == 1 ? launch_cfg<Big8>(epi, t, s) : launch_cfg<Big8K64>(epi, t, s);
+  if (cfg == kTileBigX) return launch_cfg<Big8K64X>(epi, t, s);
   return launch_cfg<SmallCfg>(epi, t, s);
 }
 
@@ -615,25 +690,36 @@ hipError_t launch_poly(const NsGroup* g, int n, float b, float c, hipStream_t s)
 
 hipError_t launch_combine(const NsGroup* g, int n, float alpha, const float* const* scale,
                           bool last, hipStream_t s) {
-  const TileCfg cfg = square_cfg(*g[0].plan);
+  // a phase's buckets agree on the tile and on keeping X^T
+  const TileCfg cfg = g[0].plan->keeps_xt ? kTileBig : square_cfg(*g[0].plan) == kTileBig ? kTileBigX : kTileSmall;
   GemmTable t{};
   t.ngroups = n;
   for (int i = 0; i < n; ++i) {
     const BucketPlan& p = *g[i].plan;
     GemmArgs& a = t.g[i];
-    a.A = g[i].P; a.B = g[i].XT;
-    a.lda = p.m_pad; a.ldb = p.m_pad;
+    const bool reads_x = !p.keeps_xt;  // the launched Cfg::kCombineReadsX
+    a.A = g[i].P;
+    a.lda = p.m_pad;
     a.strideA = p.m_pad * p.m_pad;
-    a.strideB = p.m_pad * p.n_pad;
+    a.strideB = a.strideAux = p.m_pad * p.n_pad;
     a.kdim = static_cast<int>(p.m_pad);
-    // the last iteration writes only the orientation the update reads
-    a.C = (last && p.transposed) ? nullptr : g[i].Xn;
-    a.C2 = (last && !p.transposed) ? nullptr : g[i].XTn;
     a.ldc = p.n_pad; a.ldc2 = p.m_pad;
     a.strideC = a.strideC2 = p.m_pad * p.n_pad;
-    a.aux = g[i].XT;  // X[i][j] read as X^T[j][i]
-    a.ldaux = p.m_pad;
-    a.strideAux = p.m_pad * p.n_pad;
+    // the last iteration writes only the orientation the update reads (X'^T when the
+    // bucket is transposed)
+    const bool tr = last && p.transposed;
+    if (reads_x) {
+      // one orientation: X' row-major, or X'^T (n_pad x m_pad) into the same buffer
+      a.B = a.aux = g[i].X;
+      a.ldb = a.ldaux = p.n_pad;
+      a.C = tr ? nullptr : g[i].Xn;
+      a.C2 = tr ? g[i].Xn : nullptr;
+    } else {
+      a.B = a.aux = g[i].XT;  // X[i][j] read as X^T[j][i]
+      a.ldb = a.ldaux = p.m_pad;
+      a.C = tr ? nullptr : g[i].Xn;
+      a.C2 = (last && !p.transposed) ? nullptr : g[i].XTn;
+    }
     a.alpha = alpha; a.beta = 1.0f;
     a.scale = scale ? scale[i] : nullptr;
     a.tiles_k = static_cast<int>(p.K);

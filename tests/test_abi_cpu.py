@@ -59,8 +59,10 @@ def test_routing_matches_oracle(lib, A, B, steps):
 def test_workspace_bytes(lib):
     assert ma.muon_workspace_bytes([]) == 0
     one = ma.muon_workspace_bytes([(1, 768, 3072)])
-    # X, X^T twice (bf16, m x n) plus R and P (bf16, m x m), plus norm scratch
-    assert one >= 4 * 768 * 3072 * 2 + 2 * 768 * 768 * 2
+    # X twice (bf16 ping-pong, m x n, one orientation) plus R and P (bf16, m x m), plus
+    # a little norm scratch
+    xr = 2 * 768 * 3072 * 2 + 2 * 768 * 768 * 2
+    assert xr <= one < xr + 65536
     assert ma.muon_workspace_bytes([(2, 768, 3072)]) > one
     # small buckets with the same tile share a phase: their needs add up
     other = ma.muon_workspace_bytes([(1, 3072, 768)])
