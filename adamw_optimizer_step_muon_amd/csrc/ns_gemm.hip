@@ -555,8 +555,10 @@ __global__ __launch_bounds__(C::kThreads) void ns_gemm_kernel(GemmTable table) {
 
 // Tile shapes.  Big: 256 x 256 per block (128 KiB LDS, one block per CU); the default
 // runs 8 waves of 128 x 64 over 2 stages of k = 64 (one barrier per 64 of k).  Small:
-// 128 x 128, 4 waves of 64 x 64, 2 stages of k = 64 (64 KiB, two blocks per CU) for
-// Gram sides too short to fill the chip.  The combine reads X with transposing LDS
+// 128 x 128, 8 waves of 32 x 64, 2 stages of k = 64 (64 KiB, two blocks per CU: four
+// waves per SIMD, at most 126 registers each) for Gram sides too short to fill the chip
+// (measured 4.5 % faster there than 4 waves of 64 x 64; 8 waves of 64 x 32 or 16 of
+// 32 x 32 lose the second block per CU to register use and run 25 % slower).  The combine reads X with transposing LDS
 // loads when the Gram side is at most 2048 (BucketPlan::keeps_xt false), so those
 // buckets keep one orientation of X and skip writing and casting X^T; longer Gram sides
 // read the stored X^T with b128 loads (two transposing loads per fragment measured
@@ -566,7 +568,7 @@ __global__ __launch_bounds__(C::kThreads) void ns_gemm_kernel(GemmTable table) {
 using Big8K64 = Cfg<256, 256, 64, 2, 4, 2, false>;
 using Big8K64X = Cfg<256, 256, 64, 2, 4, 2, true>;  // combine of Gram sides <= 2048
 using Big8 = Cfg<256, 256, 32, 2, 4, 4, false>;
-using SmallCfg = Cfg<128, 128, 64, 2, 2, 2, true>;
+using SmallCfg = Cfg<128, 128, 64, 4, 2, 2, true>;
 enum TileCfg { kTileSmall = 0, kTileBig = 1, kTileBigX = 2 };
 
 template <class C>
