@@ -126,7 +126,9 @@ def cautious_check(prev, got, ref_ortho, lr, wd, scale, tol):
 
 
 def _check_muon(P0, grads, hist, routes, *, lr=LR, momentum=MU, weight_decay=WD,
-                cautious_wd=False, nesterov=True, scale_mode=0, ns_steps=5):
+                cautious_wd=False, nesterov=True, scale_mode=0, ns_steps=5, only=None):
+    """Every matrix of every bucket against the oracle, step by step (``only``: a
+    list of matrix indices per bucket to check instead of all)."""
     ohp = dict(lr=f32(lr), mu=f32(momentum), weight_decay=f32(weight_decay),
                cautious_wd=cautious_wd, nesterov=nesterov, scale_mode=scale_mode,
                ns_steps=ns_steps)
@@ -136,7 +138,7 @@ def _check_muon(P0, grads, hist, routes, *, lr=LR, momentum=MU, weight_decay=WD,
         r = routes[bi]
         o = oracle.route(A, B, ns_steps)
         assert (r.transposed, r.m, r.n, r.ns_steps_run) == (o.transposed, o.m, o.n, o.ns_steps)
-        for k in range(K):
+        for k in (range(K) if only is None else only[bi]):
             prev = p0[k].astype(np.float64)
             mom = np.zeros((A, B))
             for t, step_grads in enumerate(grads):
@@ -186,12 +188,26 @@ def test_muon_ragged_buckets():
 
 
 @pytest.mark.parametrize("variant", [dict(cautious_wd=True), dict(nesterov=False),
-                                     dict(scale_mode=1), dict(ns_steps=3), dict(weight_decay=0.0)])
+                                     dict(scale_mode=1), dict(ns_steps=3), dict(ns_steps=0),
+                                     dict(weight_decay=0.0)])
 def test_muon_variants(variant):
     P0, grads = _buckets(SHAPES[:3], 22, 2)
     hist, routes = _muon_run(P0, grads, lr=LR, momentum=MU, weight_decay=variant.get("weight_decay", WD),
                              **{k: v for k, v in variant.items() if k != "weight_decay"})
     _check_muon(P0, grads, hist, routes, **variant)
+
+
+def test_muon_mixed_configurations():
+    """One call whose buckets need three GEMM configurations, so they run as three
+    phases over the same workspace: 128-tiles, a 256-tile bucket with a short Gram side
+    (combine reads X), and a transposed 128-tile bucket; first and last matrix of each
+    checked against the oracle over two steps."""
+    shapes = [(3, 200, 330), (32, 512, 2048), (2, 390, 130)]
+    count, _ = ma.muon_phases(shapes)
+    assert count == 3
+    P0, grads = _buckets(shapes, 24, 2)
+    hist, routes = _muon_run(P0, grads, lr=LR, momentum=MU, weight_decay=WD)
+    _check_muon(P0, grads, hist, routes, only=[[0, 2], [0, 31], [0, 1]])
 
 
 def test_muon_zero_gradient_is_pure_decay():
