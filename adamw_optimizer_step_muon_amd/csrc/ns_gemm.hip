@@ -14,14 +14,15 @@
 //   poly     A = B = R  (contraction over m)
 // The combine is C = A B with B = X stored row-major along n: its LDS stage holds k
 // rows of X and the B fragments are read with gfx950's transposing LDS load
-// (ds_read_b64_tr_b16), so X is kept in one orientation only:
-//   combine  A = P, B = X (contraction over m)
+// (ds_read_b64_tr_b16), so X is kept in one orientation only; for Gram sides above
+// 2048 it reads a stored X^T instead (C = A B^T like the others):
+//   combine  A = P, B = X or X^T (contraction over m)
 // Symmetric outputs are computed on lower-triangle tiles only and mirrored, halving
 // the work of the two symmetric products ("DMuon: Efficient Distributed Muon Training
 // with Near-Adam Overhead", section 2.2, symmetry exploitation); same-shape matrices
 // are batched in one launch (same section, batching).
 //
-// Kernel structure (one template, two tile shapes):
+// Kernel structure (one template, 256 x 256 and 128 x 128 tiles):
 //   * BM x BN output tile per block, WM x WN waves, v_mfma_f32_32x32x16_bf16;
 //   * operands stream HBM/L2 -> LDS with global_load_lds_dwordx4 (no register
 //     staging) into STAGES ring buffers; each 16-byte chunk of an operand row is
@@ -51,9 +52,10 @@ struct GemmArgs {
   int64_t lda, ldb, strideA, strideB;
   int kdim;
   unsigned short* C;    // row-major target
-  unsigned short* C2;   // transposed target (combine) or mirror target (gram/poly)
+  unsigned short* C2;   // transposed target (combine) or mirror target (gram/poly); the
+                        // combine may leave either C or C2 null
   int64_t ldc, ldc2, strideC, strideC2;
-  const unsigned short* aux;  // a/b-term source: poly R (read transposed), combine X
+  const unsigned short* aux;  // a/b-term source: poly R (read transposed), combine X or X^T
   int64_t ldaux, strideAux;
   float alpha, beta;    // poly: b, c; combine: a, 1
   const float* scale;   // per-matrix factor or null: gram R *= scale^2, combine X' *= scale
