@@ -158,6 +158,19 @@ def _stream_handle(stream, device) -> int:
     return int(stream.cuda_stream)
 
 
+def _scratch(nbytes: int, device, stream):
+    """A workspace allocated for one call.  It is freed when the call returns, so when
+    the kernels run on another stream than the current one it is recorded on that
+    stream: the caching allocator then does not hand the memory out again before that
+    stream's work is done."""
+    import torch
+
+    ws = torch.empty(nbytes, dtype=torch.uint8, device=device)
+    if stream is not None and stream != torch.cuda.current_stream(device):
+        ws.record_stream(stream)
+    return ws
+
+
 def _muon_hparams(lr, momentum, weight_decay, nesterov, ns_steps, ns_coeffs, ns_eps,
                   cautious_wd, scale_mode):
     hp = _MuonHParams(lr=lr, momentum=momentum, weight_decay=weight_decay, ns_eps=ns_eps,
@@ -246,7 +259,7 @@ def muon_step(buckets, *, lr: float, momentum: float = 0.95, weight_decay: float
     need = int(lib.ma_muon_workspace_bytes(arr, len(stacks), ctypes.byref(hp)))
     device = stacks[0][0].device if stacks else None
     if workspace is None and need > 0:
-        workspace = torch.empty(need, dtype=torch.uint8, device=device)
+        workspace = _scratch(need, device, stream)
     routes = (_MuonRoute * max(len(stacks), 1))()
     ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
     _check(lib.ma_muon_step(arr, len(stacks), ctypes.byref(hp), _ptr(workspace), ws_bytes,
@@ -290,7 +303,7 @@ def newton_schulz(inp, out, *, ns_steps: int = 5, ns_coeffs=None, ns_eps: float 
     hp, _keep = _muon_hparams(0.0, 0.0, 0.0, True, ns_steps, ns_coeffs, ns_eps, False, 0)
     need = newton_schulz_workspace_bytes(K, A, B)
     if workspace is None and need > 0:
-        workspace = torch.empty(need, dtype=torch.uint8, device=inp.device)
+        workspace = _scratch(need, inp.device, stream)
     ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
     _check(load().ma_newton_schulz(_ptr(i3), _ptr(o3), K, A, B, ctypes.byref(hp), _ptr(workspace),
                                    ws_bytes, _stream_handle(stream, inp.device)))

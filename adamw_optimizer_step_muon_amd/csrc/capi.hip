@@ -49,7 +49,9 @@ Range range_of(const void* p, int64_t bytes) {
 
 // Largest sizes the kernels' index arithmetic is written for.
 constexpr int64_t kMaxSide = int64_t(1) << 20;   // m_pad, n_pad
-constexpr int64_t kMaxBlocks = (int64_t(1) << 31) - 1;
+// (with room for the GEMM launch rounding each group's block count up to a multiple of 8
+// in int arithmetic)
+constexpr int64_t kMaxBlocks = (int64_t(1) << 31) - 4096;
 
 ma_status check_hparams(const ma_muon_hparams* hp) {
   if (!hp) return fail(MA_ERR_INVALID_ARG, "hparams is NULL");
