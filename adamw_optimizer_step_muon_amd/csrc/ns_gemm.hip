@@ -24,7 +24,7 @@
 //
 // Kernel structure (one template, 256 x 256 and 128 x 128 tiles):
 //   * BM x BN output tile per block, WM x WN waves, v_mfma_f32_32x32x16_bf16;
-//   * operands stream HBM/L2 -> LDS with global_load_lds_dwordx4 (no register
+//   * operands stream HBM/L2 -> LDS with buffer_load_dwordx4 ... lds (no register
 //     staging) into STAGES ring buffers; each 16-byte chunk of an operand row is
 //     XOR-swizzled so the 32 rows one MFMA fragment reads fall on distinct banks;
 //     the swizzle is applied on the global side, since LDS-DMA writes each wave's
@@ -140,10 +140,25 @@ __device__ __forceinline__ void wait_vmcnt() {
   __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
 }
 
-__device__ __forceinline__ void dma16(const unsigned short* g, unsigned short* l) {
-  // address-space casts (generic -> global / LDS) need C-style casts
-  __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)(g),
-                                   (__attribute__((address_space(3))) void*)(l), 16, 0, 0);
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+// buffer_load_dwordx4 ... lds: 16 bytes per lane from a buffer resource into LDS (the
+// wave's 64 chunks land contiguously from l).  Measured faster than the global form
+// (global_load_lds_dwordx4) by 2-6 % on 8192-wide and 13 % on 768-wide Gram products.
+__device__ void raw_buffer_load_lds(i32x4 rsrc, __attribute__((address_space(3))) unsigned* lds,
+                                    int size, int voffset, int soffset, int offset,
+                                    int aux) __asm("llvm.amdgcn.raw.buffer.load.lds");
+
+// 16-byte load at byte offset voff (per lane) of a buffer of `bytes` bytes at the
+// wave-uniform `base`; reads past `bytes` return zero (the hardware range check).
+__device__ __forceinline__ void dma16(const unsigned short* base, int voff, unsigned bytes,
+                                      unsigned short* l) {
+  const unsigned long long a = reinterpret_cast<unsigned long long>(base);
+  i32x4 r;
+  r[0] = __builtin_amdgcn_readfirstlane(static_cast<int>(a & 0xffffffffu));
+  r[1] = __builtin_amdgcn_readfirstlane(static_cast<int>(a >> 32));  // stride 0
+  r[2] = __builtin_amdgcn_readfirstlane(static_cast<int>(bytes));     // num_records
+  r[3] = 0x00020000;  // gfx9 raw buffer: 32-bit data format, no swizzle
+  raw_buffer_load_lds(r, (__attribute__((address_space(3))) unsigned*)(l), 16, voff, 0, 0, 0);
 }
 
 // Block id -> logical id so that each XCD's blocks (bid % 8) are a contiguous run.
@@ -245,16 +260,22 @@ __global__ __launch_bounds__(C::kThreads) void ns_gemm_kernel(GemmTable table) {
     const int i = isA ? d : d - C::kDmaA;
     const int r0 = (i * C::kWaves + wave) * C::kRowsPerDma;
     const int r = r0 + drow;
+    // one buffer per operand stage, based at its first element; offsets and extents
+    // stay below 2^30 bytes (sides are at most 2^20)
+    const int lda = static_cast<int>(args.lda), ldb = static_cast<int>(args.ldb);
     if (isA) {
-      dma16(gA + r * args.lda + k0 + swz<C::BK>(r, dpc) * 8, as + r0 * C::BK);
+      dma16(gA + k0, (r * lda + swz<C::BK>(r, dpc) * 8) * 2,
+            static_cast<unsigned>(((C::BM - 1) * lda + C::BK) * 2), as + r0 * C::BK);
     } else if constexpr (kBT) {
       // [BK][BN] stage: one DMA fills kBRows k rows of BN columns (1 KiB)
       constexpr int kBChunks = C::BN / 8, kBRows = 64 / kBChunks;
       const int q0 = (i * C::kWaves + wave) * kBRows;
       const int q = q0 + lane / kBChunks, pc = lane % kBChunks;
-      dma16(gB + static_cast<int64_t>(k0 + q) * args.ldb + swz_kn(q, pc) * 8, bs + q0 * C::BN);
+      dma16(gB + static_cast<int64_t>(k0) * args.ldb, (q * ldb + swz_kn(q, pc) * 8) * 2,
+            static_cast<unsigned>(((C::BK - 1) * ldb + C::BN) * 2), bs + q0 * C::BN);
     } else {
-      dma16(gB + r * args.ldb + k0 + swz<C::BK>(r, dpc) * 8, bs + r0 * C::BK);
+      dma16(gB + k0, (r * ldb + swz<C::BK>(r, dpc) * 8) * 2,
+            static_cast<unsigned>(((C::BN - 1) * ldb + C::BK) * 2), bs + r0 * C::BK);
     }
   };
   auto issue_stage = [&](int kt, int slot) {

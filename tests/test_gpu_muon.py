@@ -5,6 +5,8 @@ on the parameters, except for the cautious mask; so each step's update is compar
 on its own: update = P_{t-1} (1 - lr wd) - P_t (non-cautious), and for cautious
 decay the oracle steps from the GPU's own P_{t-1}.
 """
+import os
+
 import numpy as np
 import pytest
 
@@ -204,7 +206,8 @@ def test_muon_mixed_configurations():
     checked against the oracle over two steps."""
     shapes = [(3, 200, 330), (43, 768, 1024), (2, 390, 130)]
     count, _ = ma.muon_phases(shapes)
-    assert count == 3
+    if "MA_NS_TILE" not in os.environ:  # a forced tile makes them one phase
+        assert count == 3
     P0, grads = _buckets(shapes, 24, 2)
     hist, routes = _muon_run(P0, grads, lr=LR, momentum=MU, weight_decay=WD)
     _check_muon(P0, grads, hist, routes, only=[[0, 2], [0, 42], [0, 1]])
