@@ -224,7 +224,8 @@ def main():
         "higher_is_better": False,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16 MFMA (fp32 accumulate) + fp32 elementwise",
+        "dtype": "bf16",
+        "dtype_detail": "bf16 MFMA operands, fp32 accumulation; fp32 elementwise state",
         "data": "synthetic (seeded device-generated gradients and N(0,1) parameters)",
         "config": {"workload": wl.name, "muon_buckets": [[b.K, b.A, b.B] for b in wl.muon],
                    "adamw_elements": n, "ns_steps": mh.ns_steps,
