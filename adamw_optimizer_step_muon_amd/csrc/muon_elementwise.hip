@@ -70,13 +70,13 @@ __global__ __launch_bounds__(kThreads) void muon_prep_kernel(
         const f32x4 gv = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(g + a * B + b));
         if (kHasM) {
           f32x4* mp = reinterpret_cast<f32x4*>(mm + a * B + b);
-          f32x4 mv = *mp;
+          f32x4 mv = __builtin_nontemporal_load(mp);
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
             mv[e] = mu * mv[e] + gv[e];
             u[e] = nesterov_input(gv[e], mv[e], mu, nesterov);
           }
-          *mp = mv;
+          __builtin_nontemporal_store(mv, mp);
         } else {
 #pragma unroll
           for (int e = 0; e < 4; ++e) u[e] = gv[e];
@@ -167,12 +167,13 @@ __global__ __launch_bounds__(kThreads) void muon_apply_kernel(
   const unsigned short* o = O + k * slab + a * ldo + b;
   const float osc = oscale ? oscale[k] : 1.0f;
   if (kVec) {
-    const u32x2 ov = *reinterpret_cast<const u32x2*>(o);
+    // single-use streams (O, the parameters) go through with non-temporal accesses
+    const u32x2 ov = __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(o));
     float of[4] = {osc * bf2f(ov[0] & 0xffffu), osc * bf2f(ov[0] >> 16),
                    osc * bf2f(ov[1] & 0xffffu), osc * bf2f(ov[1] >> 16)};
     f32x4* p4 = reinterpret_cast<f32x4*>(P + e0);
     f32x4 pv;
-    if (!kExtract) pv = *p4;
+    if (!kExtract) pv = __builtin_nontemporal_load(p4);
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       if (kExtract) {
@@ -182,7 +183,7 @@ __global__ __launch_bounds__(kThreads) void muon_apply_kernel(
         pv[e] = pv[e] - d * pv[e] - lr_scale * of[e];
       }
     }
-    *p4 = pv;
+    __builtin_nontemporal_store(pv, p4);
   } else {
     const float of = osc * bf2f(*o);
     if (kExtract) {
