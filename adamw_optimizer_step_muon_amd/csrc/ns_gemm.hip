@@ -141,13 +141,19 @@ __device__ __forceinline__ void wait_vmcnt() {
 }
 
 typedef int i32x4 __attribute__((ext_vector_type(4)));
-// buffer_load_dwordx4 ... lds: 16 bytes per lane from a buffer resource into LDS (the
-// wave's 64 chunks land contiguously from l).  Measured faster than the global form
-// (global_load_lds_dwordx4) by 2-6 % on 8192-wide and 13 % on 768-wide Gram products.
-__device__ void raw_buffer_load_lds(i32x4 rsrc, __attribute__((address_space(3))) unsigned* lds,
-                                    int size, int voffset, int soffset, int offset,
-                                    int aux) __asm("llvm.amdgcn.raw.buffer.load.lds");
-
+// buffer_load_dwordx4 ... lds: 16 bytes per lane from a buffer resource into LDS, the
+// wave's 64 chunks contiguous from LDS byte address m0.  Measured faster than the
+// global form (global_load_lds_dwordx4) by 2-6 % on 8192-wide and 13 % on 768-wide
+// Gram products.
+//
+// Issued as inline assembly on purpose: the compiler's wait-count pass treats an LDS
+// DMA it knows about as a write that may alias any later LDS read carrying a memory
+// operand (ds_read_b64_tr_b16 does), and put an s_waitcnt vmcnt(0) before every
+// transposing read -- each stage then waited for the next stage's DMA, exposing its
+// full latency.  Here the kernel orders DMA and reads itself (wait_vmcnt on its own
+// stage, then s_barrier); any wait the compiler derives for its own memory ops only
+// gets more conservative, since it does not count these.
+//
 // 16-byte load at byte offset voff (per lane) of a buffer of `bytes` bytes at the
 // wave-uniform `base`; reads past `bytes` return zero (the hardware range check).
 __device__ __forceinline__ void dma16(const unsigned short* base, int voff, unsigned bytes,
@@ -158,7 +164,15 @@ __device__ __forceinline__ void dma16(const unsigned short* base, int voff, unsi
   r[1] = __builtin_amdgcn_readfirstlane(static_cast<int>(a >> 32));  // stride 0
   r[2] = __builtin_amdgcn_readfirstlane(static_cast<int>(bytes));     // num_records
   r[3] = 0x00020000;  // gfx9 raw buffer: 32-bit data format, no swizzle
-  raw_buffer_load_lds(r, (__attribute__((address_space(3))) unsigned*)(l), 16, voff, 0, 0, 0);
+  const int lds = __builtin_amdgcn_readfirstlane(static_cast<int>(
+      reinterpret_cast<uintptr_t>((__attribute__((address_space(3))) unsigned short*)(l))));
+  asm volatile(
+      "s_mov_b32 m0, %0\n\t"
+      "s_nop 0\n\t"
+      "buffer_load_dwordx4 %1, %2, 0 offen lds"
+      :
+      : "s"(lds), "v"(voff), "s"(r)
+      : "memory", "m0");
 }
 
 // Block id -> logical id so that each XCD's blocks (bid % 8) are a contiguous run.
