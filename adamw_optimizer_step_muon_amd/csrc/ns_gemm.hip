@@ -145,34 +145,49 @@ typedef int i32x4 __attribute__((ext_vector_type(4)));
 // wave's 64 chunks contiguous from LDS byte address m0.  Measured faster than the
 // global form (global_load_lds_dwordx4) by 2-6 % on 8192-wide and 13 % on 768-wide
 // Gram products.
-//
-// Issued as inline assembly on purpose: the compiler's wait-count pass treats an LDS
-// DMA it knows about as a write that may alias any later LDS read carrying a memory
-// operand (ds_read_b64_tr_b16 does), and put an s_waitcnt vmcnt(0) before every
-// transposing read -- each stage then waited for the next stage's DMA, exposing its
-// full latency.  Here the kernel orders DMA and reads itself (wait_vmcnt on its own
-// stage, then s_barrier); any wait the compiler derives for its own memory ops only
-// gets more conservative, since it does not count these.
-//
-// 16-byte load at byte offset voff (per lane) of a buffer of `bytes` bytes at the
-// wave-uniform `base`; reads past `bytes` return zero (the hardware range check).
-__device__ __forceinline__ void dma16(const unsigned short* base, int voff, unsigned bytes,
-                                      unsigned short* l) {
+__device__ void raw_buffer_load_lds(i32x4 rsrc, __attribute__((address_space(3))) unsigned* lds,
+                                    int size, int voffset, int soffset, int offset,
+                                    int aux) __asm("llvm.amdgcn.raw.buffer.load.lds");
+
+// Resource of a buffer of `bytes` bytes at the wave-uniform `base` (reads past `bytes`
+// return zero: the hardware range check).
+__device__ __forceinline__ i32x4 buffer_rsrc(const unsigned short* base, unsigned bytes) {
   const unsigned long long a = reinterpret_cast<unsigned long long>(base);
   i32x4 r;
   r[0] = __builtin_amdgcn_readfirstlane(static_cast<int>(a & 0xffffffffu));
   r[1] = __builtin_amdgcn_readfirstlane(static_cast<int>(a >> 32));  // stride 0
   r[2] = __builtin_amdgcn_readfirstlane(static_cast<int>(bytes));     // num_records
   r[3] = 0x00020000;  // gfx9 raw buffer: 32-bit data format, no swizzle
-  const int lds = __builtin_amdgcn_readfirstlane(static_cast<int>(
-      reinterpret_cast<uintptr_t>((__attribute__((address_space(3))) unsigned short*)(l))));
-  asm volatile(
-      "s_mov_b32 m0, %0\n\t"
-      "s_nop 0\n\t"
-      "buffer_load_dwordx4 %1, %2, 0 offen lds"
-      :
-      : "s"(lds), "v"(voff), "s"(r)
-      : "memory", "m0");
+  return r;
+}
+
+// 16-byte load at byte offset voff (per lane) of that buffer into LDS at l.
+//
+// kAsm: issued as inline assembly.  The compiler's wait-count pass treats an LDS DMA
+// it knows about as a write that may alias any later LDS read carrying a memory
+// operand (ds_read_b64_tr_b16 does; the plain fragment reads do not), and put an
+// s_waitcnt vmcnt(0) before every transposing read -- each stage then waited for the
+// next stage's DMA.  The kernel orders DMA and reads itself (wait_vmcnt on its own
+// stage, then s_barrier).  Only the kernels with transposing reads use it: elsewhere
+// the intrinsic schedules better (the asm's memory clobber measured 3 % slower on the
+// 256-tile kernels that read X^T).
+template <bool kAsm>
+__device__ __forceinline__ void dma16(const unsigned short* base, int voff, unsigned bytes,
+                                      unsigned short* l) {
+  const i32x4 r = buffer_rsrc(base, bytes);
+  if constexpr (kAsm) {
+    const int lds = __builtin_amdgcn_readfirstlane(static_cast<int>(
+        reinterpret_cast<uintptr_t>((__attribute__((address_space(3))) unsigned short*)(l))));
+    asm volatile(
+        "s_mov_b32 m0, %0\n\t"
+        "s_nop 0\n\t"
+        "buffer_load_dwordx4 %1, %2, 0 offen lds"
+        :
+        : "s"(lds), "v"(voff), "s"(r)
+        : "memory", "m0");
+  } else {
+    raw_buffer_load_lds(r, (__attribute__((address_space(3))) unsigned*)(l), 16, voff, 0, 0, 0);
+  }
 }
 
 // Block id -> logical id so that each XCD's blocks (bid % 8) are a contiguous run.
@@ -278,18 +293,18 @@ __global__ __launch_bounds__(C::kThreads) void ns_gemm_kernel(GemmTable table) {
     // stay below 2^30 bytes (sides are at most 2^20)
     const int lda = static_cast<int>(args.lda), ldb = static_cast<int>(args.ldb);
     if (isA) {
-      dma16(gA + k0, (r * lda + swz<C::BK>(r, dpc) * 8) * 2,
-            static_cast<unsigned>(((C::BM - 1) * lda + C::BK) * 2), as + r0 * C::BK);
+      dma16<kBT>(gA + k0, (r * lda + swz<C::BK>(r, dpc) * 8) * 2,
+                 static_cast<unsigned>(((C::BM - 1) * lda + C::BK) * 2), as + r0 * C::BK);
     } else if constexpr (kBT) {
       // [BK][BN] stage: one DMA fills kBRows k rows of BN columns (1 KiB)
       constexpr int kBChunks = C::BN / 8, kBRows = 64 / kBChunks;
       const int q0 = (i * C::kWaves + wave) * kBRows;
       const int q = q0 + lane / kBChunks, pc = lane % kBChunks;
-      dma16(gB + static_cast<int64_t>(k0) * args.ldb, (q * ldb + swz_kn(q, pc) * 8) * 2,
-            static_cast<unsigned>(((C::BK - 1) * ldb + C::BN) * 2), bs + q0 * C::BN);
+      dma16<kBT>(gB + static_cast<int64_t>(k0) * args.ldb, (q * ldb + swz_kn(q, pc) * 8) * 2,
+                 static_cast<unsigned>(((C::BK - 1) * ldb + C::BN) * 2), bs + q0 * C::BN);
     } else {
-      dma16(gB + k0, (r * ldb + swz<C::BK>(r, dpc) * 8) * 2,
-            static_cast<unsigned>(((C::BN - 1) * ldb + C::BK) * 2), bs + r0 * C::BK);
+      dma16<kBT>(gB + k0, (r * ldb + swz<C::BK>(r, dpc) * 8) * 2,
+                 static_cast<unsigned>(((C::BN - 1) * ldb + C::BK) * 2), bs + r0 * C::BK);
     }
   };
   auto issue_stage = [&](int kt, int slot) {
