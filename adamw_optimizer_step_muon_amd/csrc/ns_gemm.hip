@@ -25,8 +25,9 @@
 // Kernel structure (one template, 256 x 256 and 128 x 128 tiles):
 //   * BM x BN output tile per block, WM x WN waves, v_mfma_f32_32x32x16_bf16;
 //   * operands stream HBM/L2 -> LDS with buffer_load_dwordx4 ... lds (no register
-//     staging) into STAGES ring buffers; each 16-byte chunk of an operand row is
-//     XOR-swizzled so the 32 rows one MFMA fragment reads fall on distinct banks;
+//     staging) into rings of SA stages of A and SB of B; each 16-byte chunk of an
+//     operand row is XOR-swizzled so the 32 rows one MFMA fragment reads fall on
+//     distinct banks;
 //     the swizzle is applied on the global side, since LDS-DMA writes each wave's
 //     64 chunks contiguously;
 //   * blocks are renumbered so each XCD (blocks go round-robin to the 8 XCDs) works
@@ -75,9 +76,19 @@ struct GemmTable {
   int ngroups;
 };
 
-template <int BM_, int BN_, int BK_, int WM_, int WN_, int STAGES_, bool READS_X_>
+template <int BM_, int BN_, int BK_, int WM_, int WN_, int STAGES_, bool READS_X_,
+          int BSTAGES_ = STAGES_>
 struct Cfg {
   static constexpr int BM = BM_, BN = BN_, BK = BK_, WM = WM_, WN = WN_, STAGES = STAGES_;
+  // ring depths of the A and B operand stages: equal, or 3 and 2 (either way round),
+  // the deeper operand being loaded one stage further ahead
+  static constexpr int SA = STAGES_, SB = BSTAGES_;
+  static constexpr int LA = SA - 1, LB = SB - 1;  // stages loaded ahead
+  static constexpr int kLead = LA > LB ? LA : LB;
+  static_assert(SB == SA || (SB == SA + 1 && SA == 2) || (SA == SB + 1 && SB == 2),
+                "ring depths");
+  // in each issue group the operand with the shorter lead goes first
+  static constexpr bool kBFirst = SA > SB;
   // combine operand B: X itself through transposing LDS reads (true), or the stored
   // transpose X^T through plain b128 reads (false)
   static constexpr bool kCombineReadsX = READS_X_;
@@ -90,8 +101,9 @@ struct Cfg {
   static constexpr int kDmaA = BM / kRowsPerDma / kWaves;  // per wave per stage
   static constexpr int kDmaB = BN / kRowsPerDma / kWaves;
   static constexpr int kDmaPerStage = kDmaA + kDmaB;
-  static constexpr int kStageElems = (BM + BN) * BK;
-  static constexpr int kMainElems = STAGES * kStageElems;
+  static constexpr int kAElems = BM * BK, kBElems = BN * BK;  // one stage of A / of B
+  static constexpr int kBBase = SA * kAElems;                   // B ring after the A ring
+  static constexpr int kMainElems = SA * kAElems + SB * kBElems;
   static constexpr int kEpiElems = BM * BN;
   static constexpr int kLdsElems = kMainElems > kEpiElems ? kMainElems : kEpiElems;
   // Take the a X / b R term of the epilogue from the B operand stage that covers the
@@ -277,16 +289,19 @@ __global__ __launch_bounds__(C::kThreads) void ns_gemm_kernel(GemmTable table) {
   const unsigned short* gA = args.A + batch * args.strideA + m0 * args.lda;
   const unsigned short* gB = args.B + batch * args.strideB + (kBT ? n0 : n0 * args.ldb);
 
+  const int nk = args.kdim / C::BK;
   // LDS-DMA source pointers for this lane (k offset added per stage)
   const int drow = lane / C::kChunks;  // row inside one DMA
   const int dpc = lane % C::kChunks;   // physical chunk this lane fills
-  // DMA number d of this wave's stage load: d < kDmaA fills A rows, the rest B rows
-  auto issue_one = [&](int kt, int slot, int d) {
-    unsigned short* as = smem + slot * C::kStageElems;
-    unsigned short* bs = as + C::BM * C::BK;
+  // DMA number d of one issue group of this wave: the operand with the shorter lead
+  // first (A when the rings are equal), then the other
+  auto is_a = [](int d) { return C::kBFirst ? d >= C::kDmaB : d < C::kDmaA; };
+  auto issue_one = [&](int kt, int d) {
+    unsigned short* as = smem + (kt % C::SA) * C::kAElems;
+    unsigned short* bs = smem + C::kBBase + (kt % C::SB) * C::kBElems;
     const int k0 = kt * C::BK;
-    const bool isA = d < C::kDmaA;
-    const int i = isA ? d : d - C::kDmaA;
+    const bool isA = is_a(d);
+    const int i = C::kBFirst ? (isA ? d - C::kDmaB : d) : (isA ? d : d - C::kDmaA);
     const int r0 = (i * C::kWaves + wave) * C::kRowsPerDma;
     const int r = r0 + drow;
     // one buffer per operand stage, based at its first element; offsets and extents
@@ -307,9 +322,12 @@ __global__ __launch_bounds__(C::kThreads) void ns_gemm_kernel(GemmTable table) {
                  static_cast<unsigned>(((C::BN - 1) * ldb + C::BK) * 2), bs + r0 * C::BK);
     }
   };
-  auto issue_stage = [&](int kt, int slot) {
-#pragma unroll
-    for (int d = 0; d < C::kDmaPerStage; ++d) issue_one(kt, slot, d);
+  // DMA d of issue group v: A of stage v + LA when is_a(d), else B of stage v + LB.
+  // Group v goes out at the start of stage v, after the barrier that ended stage v - 1,
+  // into the slots that stage v - 1 read; the prologue issues groups -kLead .. -1.
+  auto issue_group_one = [&](int v, int d) {
+    const int st = v + (is_a(d) ? C::LA : C::LB);
+    if (st >= 0 && st < nk) issue_one(st, d);
   };
 
   f32x16 acc[C::WTM][C::WTN];
@@ -320,18 +338,26 @@ __global__ __launch_bounds__(C::kThreads) void ns_gemm_kernel(GemmTable table) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
 
-  const int nk = args.kdim / C::BK;
   constexpr int KK = C::BK / 16;  // MFMA k-slices per stage
   constexpr int L = C::kDmaPerStage;
 #pragma unroll
-  for (int s = 0; s < C::STAGES - 1; ++s)
-    if (s < nk) issue_stage(s, s);
+  for (int v = -C::kLead; v < 0; ++v)
+#pragma unroll
+    for (int d = 0; d < L; ++d) issue_group_one(v, d);
 
   const int frow = lane & 31;  // fragment row (A) / column (B)
   const int fkh = lane >> 5;   // which 8-wide half of a 16-wide k slice
 
-  // wait until stage `st` has landed: the stages issued after it may stay in flight
+  // wait until stage `st` has landed (called once groups up to st - 1 are issued):
+  // the DMAs issued after its last one may stay in flight
   auto wait_stage = [&](int st) {
+    if constexpr (C::SB != C::SA) {
+      // the shallow operand's stage st went out first in group st - 1; only the deep
+      // operand's stage st + 1 follows it
+      constexpr int kDeep = C::kBFirst ? C::kDmaA : C::kDmaB;
+      if (st + 1 < nk) wait_vmcnt<kDeep>(); else wait_vmcnt<0>();
+      return;
+    }
     const int pending = min(C::STAGES - 2, nk - 1 - st);
     static_assert(C::STAGES <= 5 && 3 * L < 64, "vmcnt range");
     if constexpr (C::STAGES >= 5) {
@@ -345,9 +371,9 @@ __global__ __launch_bounds__(C::kThreads) void ns_gemm_kernel(GemmTable table) {
     }
     wait_vmcnt<0>();
   };
-  auto load_frags = [&](int slot, int kk, bf16x8 (&af)[C::WTM], bf16x8 (&bfr)[C::WTN]) {
-    const unsigned short* as = smem + slot * C::kStageElems;
-    const unsigned short* bs = as + C::BM * C::BK;
+  auto load_frags = [&](int kt, int kk, bf16x8 (&af)[C::WTM], bf16x8 (&bfr)[C::WTN]) {
+    const unsigned short* as = smem + (kt % C::SA) * C::kAElems;
+    const unsigned short* bs = smem + C::kBBase + (kt % C::SB) * C::kBElems;
     const int ch = kk * 2 + fkh;
 #pragma unroll
     for (int i = 0; i < C::WTM; ++i) {
@@ -382,7 +408,7 @@ __global__ __launch_bounds__(C::kThreads) void ns_gemm_kernel(GemmTable table) {
   u32x2 cap[C::kCaptureAux ? C::WTM : 1][C::WTN][4];
   auto capture = [&](int kt_stage) {
     if constexpr (C::kCaptureAux && kEpi != kGram) {
-      const unsigned short* bs = smem + (kt_stage % C::STAGES) * C::kStageElems + C::BM * C::BK;
+      const unsigned short* bs = smem + C::kBBase + (kt_stage % C::SB) * C::kBElems;
       const int k0 = kt_stage * C::BK;
 #pragma unroll
       for (int i = 0; i < C::WTM; ++i) {
@@ -418,11 +444,12 @@ __global__ __launch_bounds__(C::kThreads) void ns_gemm_kernel(GemmTable table) {
   load_frags(0, 0, fa[0], fb[0]);
   capture(0);
   for (int kt = 0; kt < nk; ++kt) {
-    const int slot = kt % C::STAGES;
-    // slot (kt - 1) % STAGES was last read before the barrier that preceded this stage
-    const int nxt = kt + C::STAGES - 1;
-    const bool load_next = nxt < nk;
-    if (load_next && !args.spread) issue_stage(nxt, nxt % C::STAGES);
+    // issue group kt: its slots were last read before the barrier that ended stage kt - 1
+    const bool load_next = kt + (C::LA < C::LB ? C::LA : C::LB) < nk;  // group kt not empty
+    if (load_next && !args.spread) {
+#pragma unroll
+      for (int d = 0; d < L; ++d) issue_group_one(kt, d);
+    }
 #pragma unroll
     for (int kk = 0; kk < KK; ++kk) {
       const int cur = kk & 1;
@@ -433,16 +460,16 @@ __global__ __launch_bounds__(C::kThreads) void ns_gemm_kernel(GemmTable table) {
       if (load_next && args.spread && kk < kHalf) {
 #pragma unroll
         for (int e = 0; e < kPer; ++e)
-          if (kk * kPer + e < C::kDmaPerStage) issue_one(nxt, nxt % C::STAGES, kk * kPer + e);
+          if (kk * kPer + e < C::kDmaPerStage) issue_group_one(kt, kk * kPer + e);
       }
       if (kk + 1 < KK) {
-        load_frags(slot, kk + 1, fa[cur ^ 1], fb[cur ^ 1]);
+        load_frags(kt, kk + 1, fa[cur ^ 1], fb[cur ^ 1]);
       } else if (kt + 1 < nk) {
         // every wave's reads of this stage are done and stage kt+1 has landed
         __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0), vmcnt and expcnt untouched
         wait_stage(kt + 1);
         __builtin_amdgcn_s_barrier();
-        load_frags((kt + 1) % C::STAGES, 0, fa[cur ^ 1], fb[cur ^ 1]);
+        load_frags(kt + 1, 0, fa[cur ^ 1], fb[cur ^ 1]);
         capture(kt + 1);
       }
 #pragma unroll
@@ -605,20 +632,27 @@ __global__ __launch_bounds__(C::kThreads) void ns_gemm_kernel(GemmTable table) {
   }
 }
 
-// Tile shapes.  Big: 256 x 256 per block (128 KiB LDS, one block per CU); the default
-// runs 8 waves of 128 x 64 over 2 stages of k = 64 (one barrier per 64 of k).  Small:
+// Tile shapes.  Big: 256 x 256 per block (160 KiB LDS, one block per CU); the default
+// runs 8 waves of 128 x 64 over stages of k = 64 (one barrier per 64 of k), with a ring
+// of 3 A stages and 2 B stages: A is loaded two stages ahead, B one.  The 32 KiB the
+// third A slot takes is the LDS a 2 + 2 ring leaves unused; with one stage of each
+// operand in flight the loads did not cover the fetch latency, and the deeper A ring
+// measured 4-5 % faster on 8192-wide Gram sides, 3-5 % at 2048 and 7 % at 1280 (a deeper
+// B ring instead: 1-3 % less; 4 waves of 128 x 128, which cut the LDS reads per MFMA by
+// a third: 6-9 % slower, one wave per SIMD hides less latency).  Small:
 // 128 x 128, 8 waves of 32 x 64, 2 stages of k = 64 (64 KiB, two blocks per CU: four
 // waves per SIMD, at most 126 registers each) for Gram sides too short to fill the chip
 // (measured 4.5 % faster there than 4 waves of 64 x 64; 8 waves of 64 x 32 or 16 of
-// 32 x 32 lose the second block per CU to register use and run 25 % slower).  The combine reads X with transposing LDS
+// 32 x 32 lose the second block per CU to register use and run 25 % slower; a third A or
+// B slot, 80 KiB per block, is no faster there).  The combine reads X with transposing LDS
 // loads when the Gram side is at most 2048 (BucketPlan::keeps_xt false), so those
 // buckets keep one orientation of X and skip writing and casting X^T; longer Gram sides
 // read the stored X^T with b128 loads (two transposing loads per fragment measured
 // 15 % slower at m = 8192, where the long contraction makes the X^T write negligible,
 // and 2-3 % faster at m = 1280 and 2048).  MA_NS_BIG=1 selects 8 waves over 4 stages of
 // k = 32 instead (deeper prefetch, twice the barriers; measured 3-6 % slower).
-using Big8K64 = Cfg<256, 256, 64, 2, 4, 2, false>;
-using Big8K64X = Cfg<256, 256, 64, 2, 4, 2, true>;  // combine of Gram sides <= 2048
+using Big8K64 = Cfg<256, 256, 64, 2, 4, 3, false, 2>;
+using Big8K64X = Cfg<256, 256, 64, 2, 4, 3, true, 2>;  // combine of Gram sides <= 2048
 using Big8 = Cfg<256, 256, 32, 2, 4, 4, false>;
 using SmallCfg = Cfg<128, 128, 64, 4, 2, 2, true>;
 enum TileCfg { kTileSmall = 0, kTileBig = 1, kTileBigX = 2 };
