@@ -45,9 +45,20 @@ struct BucketPlan {
   size_t off_xt[2];
 };
 
-BucketPlan plan_bucket(int64_t K, int64_t A, int64_t B);
-// GEMM tile for a bucket of K matrices with Gram side m and long side n
+// Plan of one bucket on the given GEMM tile (128 or 256), or on pick_tile's choice
+// (tile 0); MA_NS_TILE, when set to 128 or 256, overrides either.
+BucketPlan plan_bucket(int64_t K, int64_t A, int64_t B, int tile = 0);
+// Whether GEMM launches holding `tri` lower-triangle and `comb` combine tiles of
+// 256 x 256 fill the chip well enough for 256-tiles.
+bool fills_256(int64_t tri, int64_t comb);
+// 256 x 256 tiles of a bucket of K matrices with Gram side m and long side n: the
+// lower triangle of the Gram products and the combine
+int64_t tri_tiles_256(int64_t K, int64_t m);
+int64_t comb_tiles_256(int64_t K, int64_t m, int64_t n);
+// GEMM tile for a bucket of K matrices with Gram side m and long side n, alone
 int pick_tile(int64_t K, int64_t m, int64_t n);
+// Gram sides below this always run on 128-tiles
+constexpr int64_t kMinGram256 = 512;
 
 // ---------------------------------------------------------------------------
 // Kernel launchers (return hipSuccess or the launch error)

@@ -190,13 +190,13 @@ __device__ __forceinline__ void dma16(const unsigned short* base, int voff, unsi
   if constexpr (kAsm) {
     const int lds = __builtin_amdgcn_readfirstlane(static_cast<int>(
         reinterpret_cast<uintptr_t>((__attribute__((address_space(3))) unsigned short*)(l))));
+    // m0 (the LDS address) is an input operand: the compiler sets it and knows its value
     asm volatile(
-        "s_mov_b32 m0, %0\n\t"
         "s_nop 0\n\t"
-        "buffer_load_dwordx4 %1, %2, 0 offen lds"
+        "buffer_load_dwordx4 %0, %1, 0 offen lds"
         :
-        : "s"(lds), "v"(voff), "s"(r)
-        : "memory", "m0");
+        : "v"(voff), "s"(r), "{m0}"(lds)
+        : "memory");
   } else {
     raw_buffer_load_lds(r, (__attribute__((address_space(3))) unsigned*)(l), 16, voff, 0, 0, 0);
   }
@@ -726,14 +726,27 @@ TileCfg square_cfg(const BucketPlan& p) { return p.tile == 256 ? kTileBig : kTil
 
 }  // namespace
 
+int64_t tri_tiles_256(int64_t K, int64_t m) {
+  const int64_t m256 = (m + 255) / 256;
+  return K * m256 * (m256 + 1) / 2;
+}
+
+int64_t comb_tiles_256(int64_t K, int64_t m, int64_t n) {
+  return K * ((m + 255) / 256) * ((n + 255) / 256);
+}
+
+bool fills_256(int64_t tri, int64_t comb) {
+  // 256-tiles once the combine tiles fill the chip twice over at one block per CU and
+  // the Gram triangle fills it once; smaller problems keep 128-tiles (two blocks per
+  // CU, 4x the blocks).  Measured per bucket: 48 x 512 x 2048 runs 19 % faster on
+  // 128-tiles (144 Gram tiles at 256), 48 x 768 x 768 14 % faster (432 combine
+  // tiles); 80 x 1280 x 1280 12 % faster on 256-tiles, 48 x 2048 x 2048 16 %.
+  return comb >= 512 && tri >= 256;
+}
+
 int pick_tile(int64_t K, int64_t m, int64_t n) {
-  // 256-tiles once the batch of combine tiles fills the chip twice over at one block
-  // per CU and the Gram triangle fills it once; smaller problems keep 128-tiles (two
-  // blocks per CU, 4x the blocks).  Measured: 48 x 512 x 2048 runs 7-11 % faster on
-  // 128-tiles (144 Gram tiles at 256), 80 x 1280 x 1280 5 % faster on 256-tiles.
-  const int64_t m256 = (m + 255) / 256, n256 = (n + 255) / 256;
-  const bool fills = K * m256 * n256 >= 512 && K * m256 * (m256 + 1) / 2 >= 256;
-  return (fills && m >= 512) ? 256 : SmallCfg::BM;
+  return (m >= kMinGram256 && fills_256(tri_tiles_256(K, m), comb_tiles_256(K, m, n)))
+             ? 256 : SmallCfg::BM;
 }
 
 hipError_t launch_gram(const NsGroup* g, int n, const float* const* scale, hipStream_t s) {

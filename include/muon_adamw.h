@@ -117,10 +117,12 @@ ma_status ma_muon_route_of(int64_t A, int64_t B, const ma_muon_hparams* hp, ma_m
 
 /* Host only: workspace bytes ma_muon_step needs for these buckets.  Buckets run in
  * phases: consecutive buckets with the same GEMM configuration (tile size and operand
- * layout, both fixed by the bucket's shape), at most 4 of them and 4 GiB of workspace
- * together, share each Newton-Schulz launch; the result is the maximum over phases of
- * the phase's summed need.  0 when there is nothing to do, and for invalid
- * arguments (ma_muon_step then reports them). */
+ * layout, fixed by the bucket's shape), at most 4 of them and 4 GiB of workspace
+ * together, share each Newton-Schulz launch; a phase of small-tile buckets whose large
+ * tiles fill the GPU together is planned on large tiles (its buckets' m_pad / n_pad,
+ * and so the need, follow).  The result is the maximum over phases of the phase's
+ * summed need.  0 when there is nothing to do, and for invalid arguments (ma_muon_step
+ * then reports them). */
 size_t ma_muon_workspace_bytes(const ma_muon_bucket* buckets, int32_t n_buckets,
                                const ma_muon_hparams* hp);
 

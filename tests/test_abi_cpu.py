@@ -76,10 +76,33 @@ def test_workspace_bytes(lib):
     assert ma.muon_workspace_bytes([(0, 10, 10)]) == 0
 
 
+def test_phase_tile_promotion(lib):
+    """Buckets that each pick 128-tiles alone but whose 256-tiles fill the chip together
+    are planned on 256-tiles as one phase: their 640-wide Gram sides pad to 768."""
+    if os.environ.get("MA_NS_TILE"):
+        pytest.skip("GEMM tile forced")
+
+    def need(K, m_pad):  # X twice, R and P, all m_pad x m_pad bf16 (m == n)
+        return 4 * K * m_pad * m_pad * 2
+
+    one = ma.muon_workspace_bytes([(40, 640, 640)])  # 240 Gram tiles at 256: too few
+    assert need(40, 640) <= one < need(40, 640) + 65536
+    assert ma.muon_phases([(40, 640, 640)] * 2) == (1, [0, 0])
+    two = ma.muon_workspace_bytes([(40, 640, 640)] * 2)  # 480 Gram, 720 combine tiles
+    assert 2 * need(40, 768) <= two < 2 * need(40, 768) + 2 * 65536
+    # together still too few (240 Gram tiles): both stay on 128-tiles
+    assert ma.muon_workspace_bytes([(20, 640, 640)] * 2) == 2 * ma.muon_workspace_bytes(
+        [(20, 640, 640)])
+    # Gram sides under 512 stay on 128-tiles however many there are
+    assert ma.muon_workspace_bytes([(64, 384, 384)] * 4) == 4 * ma.muon_workspace_bytes(
+        [(64, 384, 384)])
+
+
 def test_phases(lib):
     import workloads
     assert ma.muon_phases([]) == (0, [])
-    # the 12-layer GPT's three 128-tile buckets share one phase
+    # the 12-layer GPT's three 768-wide buckets share one phase (on 256-tiles: each
+    # alone would take 128-tiles, together they fill the chip)
     shapes = [(b.K, b.A, b.B) for b in workloads.workload(1).muon]
     assert ma.muon_phases(shapes) == (1, [0, 0, 0])
     # owner subset: every bucket needs more than the 4 GiB a phase may hold

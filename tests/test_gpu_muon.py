@@ -213,6 +213,20 @@ def test_muon_mixed_configurations():
     _check_muon(P0, grads, hist, routes, only=[[0, 2], [0, 42], [0, 1]])
 
 
+def test_muon_promoted_phase():
+    """Buckets that each run on 128-tiles alone but fill the chip together share a phase
+    planned on 256-tiles (640-wide Gram sides padded to 768: ragged 256-tile edges, one
+    bucket transposed); first and last matrix of each checked against the oracle over
+    two steps."""
+    shapes = [(24, 640, 640), (12, 640, 2560), (12, 2560, 640)]
+    assert ma.muon_phases(shapes) == (1, [0, 0, 0])
+    P0, grads = _buckets(shapes, 25, 2)
+    hist, routes = _muon_run(P0, grads, lr=LR, momentum=MU, weight_decay=WD)
+    if os.environ.get("MA_NS_TILE") != "128":
+        assert [r.m_pad for r in routes] == [768, 768, 768]
+    _check_muon(P0, grads, hist, routes, only=[[0, 23], [0, 11], [0, 11]])
+
+
 def test_muon_zero_gradient_is_pure_decay():
     P0 = [np.random.default_rng(1).standard_normal((2, 130, 70)).astype(np.float32)]
     grads = [[np.zeros((2, 130, 70), np.float32)]] * 2
