@@ -103,16 +103,6 @@ ma_muon_route route_of(const BucketPlan& p, int ns_steps) {
   return r;
 }
 
-// Tuning override of the GEMM tile (MA_NS_TILE = 128 or 256), 0 when unset.
-int forced_tile() {
-  static const int t = [] {
-    const char* env = std::getenv("MA_NS_TILE");
-    const int v = env ? std::atoi(env) : 0;
-    return (v == 128 || v == 256) ? v : 0;
-  }();
-  return t;
-}
-
 // Buckets run in phases: consecutive buckets with the same GEMM tile (and the same
 // choice of keeping X^T, which fixes the combine's operand layout), at most
 // kMaxGemmGroups of them and kPhaseBytes of workspace together, share each Newton-Schulz
@@ -269,6 +259,15 @@ ma_status prep_bucket(const BucketPlan& p, const float* grad, float* momentum,
 }
 
 }  // namespace
+
+int forced_tile() {
+  static const int t = [] {
+    const char* env = std::getenv("MA_NS_TILE");
+    const int v = env ? std::atoi(env) : 0;
+    return (v == 128 || v == 256) ? v : 0;
+  }();
+  return t;
+}
 
 BucketPlan plan_bucket(int64_t K, int64_t A, int64_t B, int tile) {
   BucketPlan p{};

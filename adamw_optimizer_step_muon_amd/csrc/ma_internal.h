@@ -59,6 +59,8 @@ int64_t comb_tiles_256(int64_t K, int64_t m, int64_t n);
 int pick_tile(int64_t K, int64_t m, int64_t n);
 // Gram sides below this always run on 128-tiles
 constexpr int64_t kMinGram256 = 512;
+// Tuning override of the GEMM tile (MA_NS_TILE = 128 or 256), 0 when unset.
+int forced_tile();
 
 // ---------------------------------------------------------------------------
 // Kernel launchers (return hipSuccess or the launch error)

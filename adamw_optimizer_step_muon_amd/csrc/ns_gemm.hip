@@ -770,6 +770,16 @@ hipError_t launch_gram(const NsGroup* g, int n, const float* const* scale, hipSt
 }
 
 hipError_t launch_poly(const NsGroup* g, int n, float b, float c, hipStream_t s) {
+  // The polynomial contracts over the Gram side alone.  Where a 256-tile phase's
+  // triangles fill less than two rounds of the chip, it runs on 128-tiles (two blocks
+  // per CU, four times the blocks) over the same 256-padded layout: measured 17 %
+  // faster for the 12-layer GPT's 768-wide buckets (432 tiles at 256).
+  int tile = g[0].plan->tile;
+  if (tile == 256 && !forced_tile()) {
+    int64_t tri = 0;
+    for (int i = 0; i < n; ++i) tri += tri_tiles_256(g[i].plan->K, g[i].plan->m_pad);
+    if (tri < 512) tile = SmallCfg::BM;
+  }
   GemmTable t{};
   t.ngroups = n;
   for (int i = 0; i < n; ++i) {
@@ -787,9 +797,9 @@ hipError_t launch_poly(const NsGroup* g, int n, float b, float c, hipStream_t s)
     a.strideAux = p.m_pad * p.m_pad;
     a.alpha = b; a.beta = c;
     a.tiles_k = static_cast<int>(p.K);
-    set_tiles(kPoly, a, p, p.tile, p.tile);
+    set_tiles(kPoly, a, p, tile, tile);
   }
-  return launch_table(kPoly, t, square_cfg(*g[0].plan), s);
+  return launch_table(kPoly, t, tile == 256 ? kTileBig : kTileSmall, s);
 }
 
 hipError_t launch_combine(const NsGroup* g, int n, float alpha, const float* const* scale,
