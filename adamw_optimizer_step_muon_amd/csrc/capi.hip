@@ -212,9 +212,9 @@ ma_status run_ns(const Phase& ph, const ma_muon_hparams* hp, char* ws, hipStream
     const float* const* sc = it == 0 ? inv : nullptr;
     hipError_t e = launch_gram(g, ph.n, sc, s);
     if (e != hipSuccess) return hip_fail(e, "gram launch");
-    e = launch_poly(g, ph.n, c.b, c.c, s);
+    e = launch_poly(g, ph.n, c.a, c.b, c.c, s);
     if (e != hipSuccess) return hip_fail(e, "poly launch");
-    e = launch_combine(g, ph.n, c.a, sc, it + 1 == hp->ns_steps, s);
+    e = launch_combine(g, ph.n, sc, it + 1 == hp->ns_steps, s);
     if (e != hipSuccess) return hip_fail(e, "combine launch");
     cur ^= 1;
   }

@@ -93,12 +93,12 @@ struct NsGroup {
 };
 // R = X X^T (lower-triangle tiles, mirrored); R *= scale[i][k]^2 where scale[i] is given
 hipError_t launch_gram(const NsGroup* g, int n, const float* const* scale, hipStream_t s);
-// P = b R + c R R^T (lower-triangle tiles, mirrored)
-hipError_t launch_poly(const NsGroup* g, int n, float b, float c, hipStream_t s);
-// Xn = a X + P X (times scale[i][k] where given), written row-major (and as X^T into
+// P = a I + b R + c R R^T (lower-triangle tiles, mirrored)
+hipError_t launch_poly(const NsGroup* g, int n, float a, float b, float c, hipStream_t s);
+// Xn = P X (times scale[i][k] where given), written row-major (and as X^T into
 // XTn for keeps_xt buckets); with `last`, only in the orientation of the parameter
 // (X^T when A > B: n_pad x m_pad, into XTn, or into Xn for one-orientation buckets)
-hipError_t launch_combine(const NsGroup* g, int n, float a, const float* const* scale,
+hipError_t launch_combine(const NsGroup* g, int n, const float* const* scale,
                           bool last, hipStream_t s);
 // param <- param - lr*wd*mask*param - lr*scale*O with O = oscale[k] * (bf16 O) (oscale
 // may be null: 1), row stride ldo

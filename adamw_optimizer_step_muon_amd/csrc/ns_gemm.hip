@@ -4,9 +4,13 @@
 // optimizer", section "Muon: orthogonalising the update", newton_schulz listing) on
 // an m x n bf16 matrix X (m <= n):
 //
-//   gram:     R  = X X^T               m x m, symmetric
-//   poly:     P  = b R + c R R^T       m x m, symmetric (R R^T = R^2 as R = R^T)
-//   combine:  X' = a X + P X           m x n
+//   gram:     R  = X X^T                  m x m, symmetric
+//   poly:     P  = a I + b R + c R R^T    m x m, symmetric (R R^T = R^2 as R = R^T)
+//   combine:  X' = P X                    m x n
+//
+// a X + (b R + c R^2) X = (a I + b R + c R^2) X, so the a X term rides on P's
+// diagonal: P is formed in fp32 and rounded to bf16 once, and the combine is a plain
+// product with no second read of X in its epilogue.
 //
 // The Gram and polynomial products are C = A B^T with both operands stored row-major
 // along the contraction index, the layout of the MFMA operands:
@@ -33,7 +37,8 @@
 //   * blocks are renumbered so each XCD (blocks go round-robin to the 8 XCDs) works
 //     on a contiguous run of tiles, and those runs are grouped by row panels, so
 //     the blocks resident on one XCD share operand panels in its L2;
-//   * epilogue: a/b/c terms in fp32 in registers, round to bf16; each orientation
+//   * epilogue: b/c terms (and a on the diagonal) or the first iteration's
+//     normalisation in fp32 in registers, round to bf16; each orientation
 //     (row-major, and the transposed / mirrored copy) is staged through an
 //     XOR-swizzled LDS tile and written with 16-byte row stores.
 // Sizes are padded to the tile by the caller and the padding is zero (preserved by
@@ -56,9 +61,9 @@ struct GemmArgs {
   unsigned short* C2;   // transposed target (combine) or mirror target (gram/poly); the
                         // combine may leave either C or C2 null
   int64_t ldc, ldc2, strideC, strideC2;
-  const unsigned short* aux;  // a/b-term source: poly R (read transposed), combine X or X^T
+  const unsigned short* aux;  // poly: R, source of the b R term (read transposed)
   int64_t ldaux, strideAux;
-  float alpha, beta;    // poly: b, c; combine: a, 1
+  float alpha, beta, diag;  // poly: P = alpha R + beta R R^T + diag I
   const float* scale;   // per-matrix factor or null: gram R *= scale^2, combine X' *= scale
   int tiles_m, tiles_n; // tile grid (triangular for gram/poly)
   int tiles_per_batch;
@@ -106,9 +111,9 @@ struct Cfg {
   static constexpr int kMainElems = SA * kAElems + SB * kBElems;
   static constexpr int kEpiElems = BM * BN;
   static constexpr int kLdsElems = kMainElems > kEpiElems ? kMainElems : kEpiElems;
-  // Take the a X / b R term of the epilogue from the B operand stage that covers the
-  // tile's rows (X[i][j] = X^T[j][i], R[i][j] = R[j][i]) instead of reading it again
-  // from memory; held in registers, so only where the wave tile is small.
+  // Take the polynomial's b R term from the B operand stage that covers the tile's
+  // rows (R[i][j] = R[j][i]) instead of reading it again from memory; held in
+  // registers, so only where the wave tile is small.
   static constexpr bool kCaptureAux = (WTM * WTN) <= 4;
   static_assert(BM % (WM * 32) == 0 && BN % (WN * 32) == 0, "wave tiling");
   static_assert(BM % (kRowsPerDma * kWaves) == 0 && BN % (kRowsPerDma * kWaves) == 0, "dma");
@@ -404,10 +409,10 @@ __global__ __launch_bounds__(C::kThreads) void ns_gemm_kernel(GemmTable table) {
   // MFMAs of slice kk, and across a stage boundary the barrier wait and the first
   // reads of the next stage sit before the MFMAs of the last slice, so the matrix
   // cores keep working while the block synchronises.
-  // a X / b R epilogue term captured from the B stage (see Cfg::kCaptureAux)
+  // the polynomial's b R term captured from the B stage (see Cfg::kCaptureAux)
   u32x2 cap[C::kCaptureAux ? C::WTM : 1][C::WTN][4];
   auto capture = [&](int kt_stage) {
-    if constexpr (C::kCaptureAux && kEpi != kGram) {
+    if constexpr (C::kCaptureAux && kEpi == kPoly) {
       const unsigned short* bs = smem + C::kBBase + (kt_stage % C::SB) * C::kBElems;
       const int k0 = kt_stage * C::BK;
 #pragma unroll
@@ -420,18 +425,8 @@ __global__ __launch_bounds__(C::kThreads) void ns_gemm_kernel(GemmTable table) {
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
               const int kl = rbase - k0 + 8 * q + 4 * fkh;  // local k of rows gi0..gi0+3
-              if constexpr (kBT) {
-                // X[k][j] at k row kl + e of the [BK][BN] stage
-                unsigned short v[4];
-#pragma unroll
-                for (int e = 0; e < 4; ++e)
-                  v[e] = bs[(kl + e) * C::BN + swz_kn(kl + e, jl >> 3) * 8 + (jl & 7)];
-                cap[i][j][q][0] = static_cast<unsigned>(v[0]) | (static_cast<unsigned>(v[1]) << 16);
-                cap[i][j][q][1] = static_cast<unsigned>(v[2]) | (static_cast<unsigned>(v[3]) << 16);
-              } else {
-                cap[i][j][q] = *reinterpret_cast<const u32x2*>(
-                    bs + jl * C::BK + swz<C::BK>(jl, kl >> 3) * 8 + (kl & 4));
-              }
+              cap[i][j][q] = *reinterpret_cast<const u32x2*>(
+                  bs + jl * C::BK + swz<C::BK>(jl, kl >> 3) * 8 + (kl & 4));
             }
           }
         }
@@ -490,76 +485,70 @@ __global__ __launch_bounds__(C::kThreads) void ns_gemm_kernel(GemmTable table) {
   // ---------------- epilogue ----------------
   // MFMA 32x32 accumulator layout: lane holds column (lane & 31) of the 32x32 tile and
   // rows 8*(r/4) + 4*(lane/32) + r%4 for r = 0..15, i.e. four runs of 4 rows.
-  // The b R term is read from R's transposed position (R is symmetric), where a lane's
-  // 4 consecutive rows are 8 contiguous bytes; the a X term from X^T the same way, or
-  // from X itself when the combine reads X.
+  // The polynomial's b R term is read from R's transposed position (R is symmetric),
+  // where a lane's 4 consecutive rows are 8 contiguous bytes, and a is added on the
+  // diagonal; the Gram and the combine only scale their accumulators.
   const bool mirror = (kEpi != kCombine) && (ti != tj);
   // the combine may skip either orientation (the last iteration keeps only the one
   // the update reads)
   const bool need_t = (kEpi == kCombine) ? (args.C2 != nullptr) : mirror;
   const bool need_c = (kEpi != kCombine) || (args.C != nullptr);
-  const unsigned short* auxT =
-      (kEpi == kGram) ? nullptr : args.aux + batch * args.strideAux;
-  float sc = 1.0f;
-  if (kEpi != kPoly && args.scale) sc = args.scale[batch];
 
   // 1. final values in fp32, in place in the accumulators
-  constexpr int kHalves = C::WTM >= 2 ? 2 : 1;  // aux loads in two batches (registers)
+  if constexpr (kEpi == kPoly) {
+    const unsigned short* auxT = args.aux + batch * args.strideAux;
+    const bool diag_tile = ti == tj;
+    constexpr int kHalves = C::WTM >= 2 ? 2 : 1;  // aux loads in two batches (registers)
 #pragma unroll
-  for (int hh = 0; hh < kHalves; ++hh) {
-    constexpr int kI = C::WTM / kHalves;
-    u32x2 ax[kI][C::WTN][4];
-    if (kEpi != kGram && C::kCaptureAux) {
-#pragma unroll
-      for (int ii = 0; ii < kI; ++ii)
-#pragma unroll
-        for (int j = 0; j < C::WTN; ++j)
-#pragma unroll
-          for (int q = 0; q < 4; ++q) ax[ii][j][q] = cap[hh * kI + ii][j][q];
-    } else if (kEpi != kGram) {
+    for (int hh = 0; hh < kHalves; ++hh) {
+      constexpr int kI = C::WTM / kHalves;
+      u32x2 ax[kI][C::WTN][4];
 #pragma unroll
       for (int ii = 0; ii < kI; ++ii)
 #pragma unroll
         for (int j = 0; j < C::WTN; ++j)
 #pragma unroll
           for (int q = 0; q < 4; ++q) {
-            const int i = hh * kI + ii;
-            const int64_t gj = n0 + wn * (C::WTN * 32) + j * 32 + (lane & 31);
-            const int64_t gi0 = m0 + wm * (C::WTM * 32) + i * 32 + 8 * q + 4 * fkh;
-            if constexpr (kBT) {
-              // X[gi0 + e][gj], 2-byte loads (32 lanes cover 64 contiguous bytes)
-              unsigned short v[4];
-#pragma unroll
-              for (int e = 0; e < 4; ++e) v[e] = auxT[(gi0 + e) * args.ldaux + gj];
-              ax[ii][j][q][0] = static_cast<unsigned>(v[0]) | (static_cast<unsigned>(v[1]) << 16);
-              ax[ii][j][q][1] = static_cast<unsigned>(v[2]) | (static_cast<unsigned>(v[3]) << 16);
+            if constexpr (C::kCaptureAux) {
+              ax[ii][j][q] = cap[hh * kI + ii][j][q];
             } else {
-              // R[gi0 + e][gj] = R[gj][gi0 + e] (poly) or X^T[gj][gi0 + e] (combine):
-              // 8 contiguous bytes
+              // R[gi0 + e][gj] = R[gj][gi0 + e]: 8 contiguous bytes
+              const int i = hh * kI + ii;
+              const int64_t gj = n0 + wn * (C::WTN * 32) + j * 32 + (lane & 31);
+              const int64_t gi0 = m0 + wm * (C::WTM * 32) + i * 32 + 8 * q + 4 * fkh;
               ax[ii][j][q] = *reinterpret_cast<const u32x2*>(auxT + gj * args.ldaux + gi0);
             }
           }
-    }
 #pragma unroll
-    for (int ii = 0; ii < kI; ++ii) {
-      const int i = hh * kI + ii;
+      for (int ii = 0; ii < kI; ++ii) {
+        const int i = hh * kI + ii;
+#pragma unroll
+        for (int j = 0; j < C::WTN; ++j) {
+          const int jl = wn * (C::WTN * 32) + j * 32 + (lane & 31);
+#pragma unroll
+          for (int q = 0; q < 4; ++q)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              const int il = wm * (C::WTM * 32) + i * 32 + 8 * q + 4 * fkh + e;
+              const unsigned int w = ax[ii][j][q][e >> 1];
+              const float t = bf2f(static_cast<unsigned short>((e & 1) ? (w >> 16) : (w & 0xffffu)));
+              float v = args.alpha * t + args.beta * acc[i][j][q * 4 + e];
+              if (diag_tile && il == jl) v += args.diag;
+              acc[i][j][q * 4 + e] = v;
+            }
+        }
+      }
+    }
+  } else if (args.scale) {
+    // first iteration: R = (inv U)(inv U)^T = inv^2 U U^T, X1 = P (inv U) = inv P U
+    const float sc = args.scale[batch];
+    const float f = (kEpi == kGram) ? sc * sc : sc;
+#pragma unroll
+    for (int i = 0; i < C::WTM; ++i)
 #pragma unroll
       for (int j = 0; j < C::WTN; ++j)
 #pragma unroll
-        for (int q = 0; q < 4; ++q)
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            float v = acc[i][j][q * 4 + e];
-            if (kEpi != kGram) {
-              const unsigned int w = ax[ii][j][q][e >> 1];
-              const float t = bf2f(static_cast<unsigned short>((e & 1) ? (w >> 16) : (w & 0xffffu)));
-              v = (kEpi == kPoly) ? args.alpha * t + args.beta * v : sc * (args.alpha * t + v);
-            } else {
-              v = (sc * sc) * v;
-            }
-            acc[i][j][q * 4 + e] = v;
-          }
-    }
+        for (int r = 0; r < 16; ++r) acc[i][j][r] *= f;
   }
 
   // 2. each orientation goes through LDS (bf16) and out with 16-byte row stores
@@ -769,7 +758,7 @@ hipError_t launch_gram(const NsGroup* g, int n, const float* const* scale, hipSt
   return launch_table(kGram, t, square_cfg(*g[0].plan), s);
 }
 
-hipError_t launch_poly(const NsGroup* g, int n, float b, float c, hipStream_t s) {
+hipError_t launch_poly(const NsGroup* g, int n, float a_coef, float b, float c, hipStream_t s) {
   // The polynomial contracts over the Gram side alone.  Where a 256-tile phase's
   // triangles fill less than two rounds of the chip, it runs on 128-tiles (two blocks
   // per CU, four times the blocks) over the same 256-padded layout: measured 17 %
@@ -795,14 +784,14 @@ hipError_t launch_poly(const NsGroup* g, int n, float b, float c, hipStream_t s)
     a.aux = g[i].R;
     a.ldaux = p.m_pad;
     a.strideAux = p.m_pad * p.m_pad;
-    a.alpha = b; a.beta = c;
+    a.alpha = b; a.beta = c; a.diag = a_coef;
     a.tiles_k = static_cast<int>(p.K);
     set_tiles(kPoly, a, p, tile, tile);
   }
   return launch_table(kPoly, t, tile == 256 ? kTileBig : kTileSmall, s);
 }
 
-hipError_t launch_combine(const NsGroup* g, int n, float alpha, const float* const* scale,
+hipError_t launch_combine(const NsGroup* g, int n, const float* const* scale,
                           bool last, hipStream_t s) {
   // a phase's buckets agree on the tile and on keeping X^T
   const TileCfg cfg = g[0].plan->keeps_xt ? kTileBig : square_cfg(*g[0].plan) == kTileBig ? kTileBigX : kTileSmall;
@@ -815,7 +804,7 @@ hipError_t launch_combine(const NsGroup* g, int n, float alpha, const float* con
     a.A = g[i].P;
     a.lda = p.m_pad;
     a.strideA = p.m_pad * p.m_pad;
-    a.strideB = a.strideAux = p.m_pad * p.n_pad;
+    a.strideB = p.m_pad * p.n_pad;
     a.kdim = static_cast<int>(p.m_pad);
     a.ldc = p.n_pad; a.ldc2 = p.m_pad;
     a.strideC = a.strideC2 = p.m_pad * p.n_pad;
@@ -824,17 +813,16 @@ hipError_t launch_combine(const NsGroup* g, int n, float alpha, const float* con
     const bool tr = last && p.transposed;
     if (reads_x) {
       // one orientation: X' row-major, or X'^T (n_pad x m_pad) into the same buffer
-      a.B = a.aux = g[i].X;
-      a.ldb = a.ldaux = p.n_pad;
+      a.B = g[i].X;
+      a.ldb = p.n_pad;
       a.C = tr ? nullptr : g[i].Xn;
       a.C2 = tr ? g[i].Xn : nullptr;
     } else {
-      a.B = a.aux = g[i].XT;  // X[i][j] read as X^T[j][i]
-      a.ldb = a.ldaux = p.m_pad;
+      a.B = g[i].XT;  // X[i][j] read as X^T[j][i]
+      a.ldb = p.m_pad;
       a.C = tr ? nullptr : g[i].Xn;
       a.C2 = (last && !p.transposed) ? nullptr : g[i].XTn;
     }
-    a.alpha = alpha; a.beta = 1.0f;
     a.scale = scale ? scale[i] : nullptr;
     a.tiles_k = static_cast<int>(p.K);
     set_tiles(kCombine, a, p, p.tile, p.tile);

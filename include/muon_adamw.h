@@ -136,8 +136,9 @@ int32_t ma_muon_phases(const ma_muon_bucket* buckets, int32_t n_buckets, int32_t
 
 /* One Muon step on every bucket [HB], in this order per bucket:
  *   M <- mu M + G;  U <- G + mu M (nesterov) or M;  X0 <- U / (||U||_F + ns_eps)  (bf16,
- *   transposed when A > B);  ns_steps times: R <- X X^T, P <- b R + c R R,
- *   X <- a X + P X  (bf16 operands, fp32 accumulation);  O <- X (un-transposed);
+ *   transposed when A > B);  ns_steps times: R <- X X^T, P <- a I + b R + c R R,
+ *   X <- P X  (= a X + (b R + c R R) X; bf16 operands, fp32 accumulation);
+ *   O <- X (un-transposed);
  *   s <- scale(A, B);  P <- P - eta lambda [mask] P - eta s O,
  *   mask = (s O * P > 0) when cautious_wd, else 1.
  * buckets:    host array of n_buckets descriptors (n_buckets >= 0).
