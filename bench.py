@@ -84,9 +84,13 @@ def counted_traffic(summary, source, key="traffic_bytes_per_launch"):
 
 
 def cpu_baseline(wl, budget_s):
-    """The fp64 oracle as it stands on the host cores, on a bounded sample: one matrix
-    per Muon bucket for one step, and a slice of the AdamW buffer; scaled to one full
-    step (x K per bucket, x n / slice for AdamW)."""
+    """The fp64 oracle as it stands on the host cores, timed on a bounded sample of one
+    step and scaled to the whole step.  About budget_s seconds of oracle work: half on
+    Muon matrices taken round-robin over the buckets (matrix k of every bucket before
+    matrix k + 1 of any), half on AdamW slices of 4M elements.  Each bucket's time is
+    its mean per sampled matrix x K; a bucket the budget never reached is extrapolated
+    from the sampled ones by its dense Newton-Schulz FLOP count, and the sample text
+    says so.  Input generation is not timed."""
     import numpy as np
 
     import oracle
@@ -99,35 +103,61 @@ def cpu_baseline(wl, budget_s):
     except Exception:
         cores = os.cpu_count() or 1
     hp = wl.muon_hp
-    muon_s = 0.0
-    parts = []
-    for bi, b in enumerate(wl.muon):
-        p0 = gen.np_param(wl.seed, gen.muon_index(wl, bi, 0), (b.A, b.B))
-        g1 = gen.np_grad(wl.seed, 1, gen.muon_index(wl, bi, 0), (b.A, b.B), wl.muon_grad,
+    nb = len(wl.muon)
+    per_t, per_n = [0.0] * nb, [0] * nb
+    order = [(bi, k) for k in range(max(b.K for b in wl.muon)) for bi, b in enumerate(wl.muon)
+             if k < b.K]
+    t_muon = 0.0
+    for bi, k in order:
+        if per_n != [0] * nb and t_muon >= budget_s / 2:
+            break
+        b = wl.muon[bi]
+        p0 = gen.np_param(wl.seed, gen.muon_index(wl, bi, k), (b.A, b.B))
+        g1 = gen.np_grad(wl.seed, 1, gen.muon_index(wl, bi, k), (b.A, b.B), wl.muon_grad,
                          gen.MUON_SIGMA)
         t0 = time.perf_counter()
         oracle.muon_step(p0, g1, np.zeros((b.A, b.B)), lr=hp.lr, mu=hp.momentum,
                          weight_decay=hp.weight_decay, cautious_wd=hp.cautious_wd)
         dt = time.perf_counter() - t0
-        muon_s += dt * b.K
-        parts.append(f"1 of {b.K} {b.A}x{b.B}")
-        if dt * len(wl.muon) > budget_s:
-            break
+        per_t[bi] += dt
+        per_n[bi] += 1
+        t_muon += dt
+
+    def dense(b):
+        m, n = min(b.A, b.B), max(b.A, b.B)
+        return hp.ns_steps * (4 * m * m * n + 2 * m ** 3)
+
+    s_per_flop = sum(per_t) / sum(dense(b) * per_n[i] for i, b in enumerate(wl.muon))
+    muon_s = 0.0
+    parts = []
+    for bi, b in enumerate(wl.muon):
+        if per_n[bi]:
+            muon_s += per_t[bi] / per_n[bi] * b.K
+            parts.append(f"{per_n[bi]} of {b.K} {b.A}x{b.B}")
+        else:
+            muon_s += s_per_flop * dense(b) * b.K
+            parts.append(f"0 of {b.K} {b.A}x{b.B} (extrapolated by FLOP count)")
     n = wl.adamw_numel
-    n_s = min(n, 4_000_000)
-    rng = np.random.default_rng(0)
-    p = rng.standard_normal(n_s).astype(np.float32)
-    g = (1e-3 * rng.standard_normal(n_s)).astype(np.float32)
     ah = wl.adamw_hp
-    t0 = time.perf_counter()
-    oracle.adamw_step(p, g, np.zeros(n_s), np.zeros(n_s), step=1, lr=ah.lr, beta1=ah.beta1,
-                      beta2=ah.beta2, eps=ah.eps, weight_decay=ah.weight_decay)
-    adamw_s = (time.perf_counter() - t0) * (n / n_s)
+    chunk = min(n, 4_000_000)
+    rng = np.random.default_rng(0)
+    t_adamw, n_done = 0.0, 0
+    while n_done < n and (n_done == 0 or t_adamw < budget_s / 2):
+        c = min(chunk, n - n_done)
+        p = rng.standard_normal(c).astype(np.float32)
+        g = (1e-3 * rng.standard_normal(c)).astype(np.float32)
+        t0 = time.perf_counter()
+        oracle.adamw_step(p, g, np.zeros(c), np.zeros(c), step=1, lr=ah.lr, beta1=ah.beta1,
+                          beta2=ah.beta2, eps=ah.eps, weight_decay=ah.weight_decay)
+        t_adamw += time.perf_counter() - t0
+        n_done += c
+    adamw_s = t_adamw * (n / n_done)
     return {"value": round((muon_s + adamw_s) * 1e3, 1), "unit": "ms", "cores": int(cores),
             "kind": "oracle",
-            "sample": (f"Muon: one step of {', '.join(parts)} matrices, scaled by K; AdamW: "
-                       f"{n_s} of {n} elements, scaled; numpy float64 (BLAS threads={cores}, "
-                       "elementwise single-threaded)")}
+            "sample": (f"one step, {t_muon + t_adamw:.1f} s of oracle work: Muon {', '.join(parts)} "
+                       f"matrices, each bucket scaled by K; AdamW {n_done} of {n} elements, "
+                       f"scaled; numpy float64 (BLAS threads={cores}, elementwise "
+                       "single-threaded)")}
 
 
 def main():
