@@ -5,10 +5,11 @@ include/muon_adamw.h); this package is its thin Python binding plus the MuonAdam
 parameter-group wrapper.  PyTorch supplies device memory and streams only.
 """
 from ._lib import (LIB_PATH, MuonAdamWError, Route, abi_version, adamw_step, load,
-                   muon_phases, muon_route_of, muon_step, muon_workspace_bytes,
-                   newton_schulz, newton_schulz_workspace_bytes)
+                   muon_phases, muon_route_of, muon_step, muon_tune, muon_tune_reset,
+                   muon_workspace_bytes, newton_schulz, newton_schulz_workspace_bytes)
 from .optim import MuonAdamW
 
 __all__ = ["LIB_PATH", "MuonAdamWError", "Route", "abi_version", "adamw_step", "load",
-           "muon_phases", "muon_route_of", "muon_step", "muon_workspace_bytes", "newton_schulz",
+           "muon_phases", "muon_route_of", "muon_step", "muon_tune", "muon_tune_reset",
+           "muon_workspace_bytes", "newton_schulz",
            "newton_schulz_workspace_bytes", "MuonAdamW"]

@@ -25,7 +25,7 @@ MA_MAX_NS_STEPS = 64
 EXPORTED = (
     "ma_abi_version", "ma_status_string", "ma_last_error", "ma_muon_route_of",
     "ma_muon_workspace_bytes", "ma_muon_phases", "ma_muon_step", "ma_adamw_step",
-    "ma_newton_schulz_workspace_bytes", "ma_newton_schulz",
+    "ma_newton_schulz_workspace_bytes", "ma_newton_schulz", "ma_muon_tune", "ma_muon_tune_reset",
 )
 
 
@@ -115,6 +115,12 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
                                      ctypes.c_int64, ctypes.c_int64,
                                      ctypes.POINTER(_MuonHParams), ctypes.c_void_p,
                                      ctypes.c_size_t, ctypes.c_void_p]
+    lib.ma_muon_tune.restype = ctypes.c_int
+    lib.ma_muon_tune.argtypes = [ctypes.POINTER(_MuonBucket), ctypes.c_int32,
+                                 ctypes.POINTER(_MuonHParams), ctypes.c_void_p, ctypes.c_size_t,
+                                 ctypes.c_void_p, ctypes.c_int32, ctypes.POINTER(ctypes.c_int32)]
+    lib.ma_muon_tune_reset.restype = None
+    lib.ma_muon_tune_reset.argtypes = []
     _lib = lib
     return lib
 
@@ -235,6 +241,44 @@ def muon_phases(shapes: Sequence[Sequence[int]]):
     if count < 0:
         _check(count)
     return count, [int(out[i]) for i in range(n)]
+
+
+def muon_tune(shapes: Sequence[Sequence[int]], *, reps: int = 3, tiles=None, workspace=None,
+              stream=None, device=None):
+    """Per-shape Newton-Schulz GEMM tiles (ma_muon_tune) for buckets of these (K, A, B)
+    shapes.  reps > 0: time the available tiles on the workspace (scratch; allocated for
+    the call when None) and keep the fastest; reps == 0: pin `tiles`.  Returns the tiles
+    in force, one [gram, poly, combine] list per phase."""
+    import torch
+
+    n = len(shapes)
+    arr = (_MuonBucket * max(n, 1))()
+    for i, (K, A, B) in enumerate(shapes):
+        arr[i] = _MuonBucket(int(K), int(A), int(B), 0, 0, 0)
+    nph, _ = muon_phases(shapes)
+    out = (ctypes.c_int32 * max(3 * nph, 1))()
+    lib = load()
+    if int(reps) == 0:
+        flat = [int(t) for ph in (tiles or []) for t in ph]
+        if len(flat) != 3 * nph:
+            raise ValueError(f"tiles needs {nph} phases of 3 entries")
+        for i, t in enumerate(flat):
+            out[i] = t
+        _check(lib.ma_muon_tune(arr, n, None, None, 0, None, 0, out))
+    else:
+        device = torch.device("cuda", torch.cuda.current_device()) if device is None else device
+        need = int(lib.ma_muon_workspace_bytes(arr, n, None))
+        if workspace is None and need > 0:
+            workspace = _scratch(need, device, stream)
+        ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+        _check(lib.ma_muon_tune(arr, n, None, _ptr(workspace), ws_bytes,
+                                _stream_handle(stream, device), int(reps), out))
+    return [[int(out[3 * i + q]) for q in range(3)] for i in range(nph)]
+
+
+def muon_tune_reset() -> None:
+    """Forget every tuned or pinned tile (ma_muon_tune_reset)."""
+    load().ma_muon_tune_reset()
 
 
 def muon_step(buckets, *, lr: float, momentum: float = 0.95, weight_decay: float = 0.0,

@@ -1,11 +1,15 @@
 // Exported C ABI (include/muon_adamw.h): argument checks, routing, workspace layout
 // and the launch sequence of one optimizer step.  Host code only; the arithmetic is
 // in the kernels of adamw.hip, muon_elementwise.hip and ns_gemm.hip.
+#include <array>
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
 #include <cstdlib>
+#include <map>
+#include <mutex>
 #include <string>
+#include <vector>
 
 #include "muon_adamw.h"
 #include "ma_internal.h"
@@ -179,9 +183,71 @@ ma_status for_each_phase(const ma_muon_bucket* buckets, int32_t n_buckets, Fn&& 
   return MA_OK;
 }
 
+// Tuned GEMM tiles ("DMuon: Efficient Distributed Muon Training with Near-Adam
+// Overhead", section 2.4, autotuning per shape): one entry per phase shape (its buckets'
+// K, padded sides, orientation and X^T choice), the tile of the Gram, polynomial and
+// combine launches (0: the default rule).  Filled by ma_muon_tune, read by every
+// Newton-Schulz run; process-wide, guarded by a mutex.
+enum Product { kProdGram = 0, kProdPoly = 1, kProdCombine = 2 };
+using Tiles = std::array<int, 3>;
+std::mutex g_tune_mu;
+std::map<std::vector<int64_t>, Tiles> g_tune;
+
+std::vector<int64_t> phase_key(const Phase& ph) {
+  std::vector<int64_t> k{ph.n};
+  for (int j = 0; j < ph.n; ++j) {
+    const BucketPlan& p = ph.plan[j];
+    k.insert(k.end(), {p.K, p.m_pad, p.n_pad, p.transposed ? 1 : 0, p.keeps_xt ? 1 : 0});
+  }
+  return k;
+}
+
+Tiles tuned_tiles(const Phase& ph) {
+  std::lock_guard<std::mutex> lock(g_tune_mu);
+  const auto it = g_tune.find(phase_key(ph));
+  return it == g_tune.end() ? Tiles{0, 0, 0} : it->second;
+}
+
+// Tiles a product of this phase can run: 256 and 128 on a 256-padded phase (the
+// combine of a phase that keeps X^T only its 256-tile configuration), 128 otherwise.
+int tile_candidates(const Phase& ph, int prod, int (&out)[2]) {
+  if (ph.tile != 256 || forced_tile()) {
+    out[0] = ph.tile;
+    return 1;
+  }
+  out[0] = 256;
+  if (prod == kProdCombine && ph.plan[0].keeps_xt) return 1;
+  out[1] = 128;
+  return 2;
+}
+
+bool tile_available(const Phase& ph, int prod, int tile) {
+  int c[2];
+  const int nc = tile_candidates(ph, prod, c);
+  for (int i = 0; i < nc; ++i)
+    if (c[i] == tile) return true;
+  return false;
+}
+
 template <class T>
 T* at(char* ws, size_t off) {
   return reinterpret_cast<T*>(ws + off);
+}
+
+// The GEMM operands of a phase's buckets for an iteration reading X[cur] (and writing
+// X[cur ^ 1]).
+void phase_groups(const Phase& ph, char* ws, int cur, NsGroup* g) {
+  for (int j = 0; j < ph.n; ++j) {
+    const BucketPlan& p = ph.plan[j];
+    char* w = ws + ph.base[j];
+    g[j].plan = &p;
+    g[j].X = at<unsigned short>(w, p.off_x[cur]);
+    g[j].Xn = at<unsigned short>(w, p.off_x[cur ^ 1]);
+    g[j].XT = p.keeps_xt ? at<unsigned short>(w, p.off_xt[cur]) : nullptr;
+    g[j].XTn = p.keeps_xt ? at<unsigned short>(w, p.off_xt[cur ^ 1]) : nullptr;
+    g[j].R = at<unsigned short>(w, p.off_r);
+    g[j].P = at<unsigned short>(w, p.off_p);
+  }
 }
 
 // Newton-Schulz for every bucket of a phase whose unnormalised bf16 U sits in its X[0]
@@ -194,27 +260,18 @@ ma_status run_ns(const Phase& ph, const ma_muon_hparams* hp, char* ws, hipStream
   NsGroup g[kMaxGemmGroups];
   const float* inv[kMaxGemmGroups];
   for (int j = 0; j < ph.n; ++j) inv[j] = at<const float>(ws, ph.base[j] + ph.plan[j].off_inv);
+  const Tiles tiles = tuned_tiles(ph);
   int cur = 0;
   for (int it = 0; it < hp->ns_steps; ++it) {
-    for (int j = 0; j < ph.n; ++j) {
-      const BucketPlan& p = ph.plan[j];
-      char* w = ws + ph.base[j];
-      g[j].plan = &p;
-      g[j].X = at<unsigned short>(w, p.off_x[cur]);
-      g[j].Xn = at<unsigned short>(w, p.off_x[cur ^ 1]);
-      g[j].XT = p.keeps_xt ? at<unsigned short>(w, p.off_xt[cur]) : nullptr;
-      g[j].XTn = p.keeps_xt ? at<unsigned short>(w, p.off_xt[cur ^ 1]) : nullptr;
-      g[j].R = at<unsigned short>(w, p.off_r);
-      g[j].P = at<unsigned short>(w, p.off_p);
-    }
+    phase_groups(ph, ws, cur, g);
     const NsCoeffs c = coeff_at(hp, it);
     // the first iteration applies the normalisation X0 = inv U inside its products
     const float* const* sc = it == 0 ? inv : nullptr;
-    hipError_t e = launch_gram(g, ph.n, sc, s);
+    hipError_t e = launch_gram(g, ph.n, sc, tiles[kProdGram], s);
     if (e != hipSuccess) return hip_fail(e, "gram launch");
-    e = launch_poly(g, ph.n, c.a, c.b, c.c, s);
+    e = launch_poly(g, ph.n, c.a, c.b, c.c, tiles[kProdPoly], s);
     if (e != hipSuccess) return hip_fail(e, "poly launch");
-    e = launch_combine(g, ph.n, sc, it + 1 == hp->ns_steps, s);
+    e = launch_combine(g, ph.n, sc, it + 1 == hp->ns_steps, tiles[kProdCombine], s);
     if (e != hipSuccess) return hip_fail(e, "combine launch");
     cur ^= 1;
   }
@@ -489,6 +546,115 @@ ma_status ma_newton_schulz(const float* in, float* out, int64_t K, int64_t A, in
   const hipError_t e = launch_ns_extract(p, out, O[0], oscale[0], ldo[0], s);
   if (e != hipSuccess) return hip_fail(e, "extract launch");
   return MA_OK;
+}
+
+ma_status ma_muon_tune(const ma_muon_bucket* buckets, int32_t n_buckets,
+                       const ma_muon_hparams* hp, void* workspace, size_t workspace_bytes,
+                       void* stream, int32_t reps, int32_t* tiles) {
+  g_last_error.clear();
+  if (hp) {
+    const ma_status st = check_hparams(hp);
+    if (st != MA_OK) return st;
+  }
+  if (n_buckets < 0) return fail(MA_ERR_INVALID_ARG, "n_buckets %d < 0", n_buckets);
+  if (n_buckets > 0 && !buckets) return fail(MA_ERR_INVALID_ARG, "buckets is NULL");
+  if (reps < 0 || reps > 1000) return fail(MA_ERR_INVALID_ARG, "reps %d outside [0, 1000]", reps);
+  if (reps == 0 && !tiles) return fail(MA_ERR_INVALID_ARG, "tiles is NULL with reps 0");
+  for (int32_t i = 0; i < n_buckets; ++i) {
+    const ma_status st = check_shape(buckets[i].K, buckets[i].A, buckets[i].B);
+    if (st != MA_OK) return fail(st, "bucket %d: %s", i, g_last_error.c_str());
+  }
+  if (reps == 0) {
+    // pin: check every requested tile first, then store (all zero: back to the rule)
+    int phase = 0;
+    ma_status st = for_each_phase(buckets, n_buckets, [&](const Phase& ph) -> ma_status {
+      for (int q = 0; q < 3; ++q) {
+        const int t = tiles[3 * phase + q];
+        if (t != 0 && !tile_available(ph, q, t))
+          return fail(MA_ERR_INVALID_ARG, "phase %d, product %d: tile %d is not available", phase,
+                      q, t);
+      }
+      ++phase;
+      return MA_OK;
+    });
+    if (st != MA_OK) return st;
+    phase = 0;
+    std::lock_guard<std::mutex> lock(g_tune_mu);
+    return for_each_phase(buckets, n_buckets, [&](const Phase& ph) -> ma_status {
+      const Tiles t{tiles[3 * phase], tiles[3 * phase + 1], tiles[3 * phase + 2]};
+      if (t == Tiles{0, 0, 0}) g_tune.erase(phase_key(ph)); else g_tune[phase_key(ph)] = t;
+      ++phase;
+      return MA_OK;
+    });
+  }
+  const size_t need = ma_muon_workspace_bytes(buckets, n_buckets, hp);
+  if (need > 0) {
+    if (!workspace) return fail(MA_ERR_WORKSPACE, "workspace is NULL, %zu bytes needed", need);
+    if (reinterpret_cast<uintptr_t>(workspace) & 255u)
+      return fail(MA_ERR_WORKSPACE, "workspace must be 256-byte aligned");
+    if (workspace_bytes < need)
+      return fail(MA_ERR_WORKSPACE, "workspace has %zu bytes, %zu needed", workspace_bytes, need);
+  }
+  int phases = 0;
+  for_each_phase(buckets, n_buckets, [&](const Phase&) { ++phases; return MA_OK; });
+  if (phases == 0) return MA_OK;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  char* ws = static_cast<char*>(workspace);
+  const NsCoeffs c = hp ? coeff_at(hp, 0) : kQuintic;
+  hipEvent_t e0 = nullptr, e1 = nullptr;
+  hipError_t he = hipEventCreate(&e0);
+  if (he == hipSuccess) he = hipEventCreate(&e1);
+  if (he != hipSuccess) {
+    if (e0) (void)hipEventDestroy(e0);
+    return hip_fail(he, "event create");
+  }
+  int phase = 0;
+  const ma_status st = for_each_phase(buckets, n_buckets, [&](const Phase& ph) -> ma_status {
+    NsGroup g[kMaxGemmGroups];
+    phase_groups(ph, ws, 0, g);
+    auto launch = [&](int q, int tile) {
+      switch (q) {
+        case kProdGram: return launch_gram(g, ph.n, nullptr, tile, s);
+        case kProdPoly: return launch_poly(g, ph.n, c.a, c.b, c.c, tile, s);
+        default: return launch_combine(g, ph.n, nullptr, false, tile, s);
+      }
+    };
+    Tiles best{0, 0, 0};
+    for (int q = 0; q < 3; ++q) {
+      int cand[2];
+      const int nc = tile_candidates(ph, q, cand);
+      float best_ms = 0.0f;
+      for (int i = 0; i < nc; ++i) {
+        hipError_t e = launch(q, cand[i]);  // warm-up
+        if (e == hipSuccess) e = hipEventRecord(e0, s);
+        for (int r = 0; r < reps && e == hipSuccess; ++r) e = launch(q, cand[i]);
+        if (e == hipSuccess) e = hipEventRecord(e1, s);
+        if (e == hipSuccess) e = hipEventSynchronize(e1);
+        float ms = 0.0f;
+        if (e == hipSuccess) e = hipEventElapsedTime(&ms, e0, e1);
+        if (e != hipSuccess) return hip_fail(e, "tuning launch");
+        if (i == 0 || ms < best_ms) {
+          best_ms = ms;
+          best[q] = cand[i];
+        }
+      }
+      if (tiles) tiles[3 * phase + q] = best[q];
+    }
+    {
+      std::lock_guard<std::mutex> lock(g_tune_mu);
+      g_tune[phase_key(ph)] = best;
+    }
+    ++phase;
+    return MA_OK;
+  });
+  (void)hipEventDestroy(e0);
+  (void)hipEventDestroy(e1);
+  return st;
+}
+
+void ma_muon_tune_reset(void) {
+  std::lock_guard<std::mutex> lock(g_tune_mu);
+  g_tune.clear();
 }
 
 ma_status ma_adamw_step(float* param, const float* grad, float* exp_avg, float* exp_avg_sq,

@@ -91,15 +91,21 @@ struct NsGroup {
   unsigned short* R;    // m_pad x m_pad
   unsigned short* P;
 };
+// GEMM tiles: `tile` (and `tile_choice`) 0 takes the default for the phase; 128 or 256
+// picks that tile (256 only on a 256-padded phase; the combine of a phase that keeps
+// X^T always runs its own 256-tile configuration).  Every choice accumulates each
+// output over the same k order, so results do not depend on it.
 // R = X X^T (lower-triangle tiles, mirrored); R *= scale[i][k]^2 where scale[i] is given
-hipError_t launch_gram(const NsGroup* g, int n, const float* const* scale, hipStream_t s);
+hipError_t launch_gram(const NsGroup* g, int n, const float* const* scale, int tile,
+                       hipStream_t s);
 // P = a I + b R + c R R^T (lower-triangle tiles, mirrored)
-hipError_t launch_poly(const NsGroup* g, int n, float a, float b, float c, hipStream_t s);
+hipError_t launch_poly(const NsGroup* g, int n, float a, float b, float c, int tile_choice,
+                       hipStream_t s);
 // Xn = P X (times scale[i][k] where given), written row-major (and as X^T into
 // XTn for keeps_xt buckets); with `last`, only in the orientation of the parameter
 // (X^T when A > B: n_pad x m_pad, into XTn, or into Xn for one-orientation buckets)
-hipError_t launch_combine(const NsGroup* g, int n, const float* const* scale,
-                          bool last, hipStream_t s);
+hipError_t launch_combine(const NsGroup* g, int n, const float* const* scale, bool last,
+                          int tile, hipStream_t s);
 // param <- param - lr*wd*mask*param - lr*scale*O with O = oscale[k] * (bf16 O) (oscale
 // may be null: 1), row stride ldo
 hipError_t launch_muon_apply(const BucketPlan& p, float* param, const unsigned short* O,

@@ -711,7 +711,12 @@ hipError_t launch_table(int epi, GemmTable& t, TileCfg cfg, hipStream_t s) {
   return launch_cfg<SmallCfg>(epi, t, s);
 }
 
-TileCfg square_cfg(const BucketPlan& p) { return p.tile == 256 ? kTileBig : kTileSmall; }
+// The tile a launch runs: a 128 or 256 choice on a 256-padded phase (a 128-padded one
+// only has 128-tiles), else the phase's own; MA_NS_TILE overrides everything.
+int chosen_tile(const BucketPlan& p, int choice) {
+  if (forced_tile() || p.tile != 256) return p.tile;
+  return (choice == 128 || choice == 256) ? choice : p.tile;
+}
 
 }  // namespace
 
@@ -738,7 +743,9 @@ int pick_tile(int64_t K, int64_t m, int64_t n) {
              ? 256 : SmallCfg::BM;
 }
 
-hipError_t launch_gram(const NsGroup* g, int n, const float* const* scale, hipStream_t s) {
+hipError_t launch_gram(const NsGroup* g, int n, const float* const* scale, int tile,
+                       hipStream_t s) {
+  tile = chosen_tile(*g[0].plan, tile);
   GemmTable t{};
   t.ngroups = n;
   for (int i = 0; i < n; ++i) {
@@ -753,18 +760,19 @@ hipError_t launch_gram(const NsGroup* g, int n, const float* const* scale, hipSt
     a.strideC = a.strideC2 = p.m_pad * p.m_pad;
     a.scale = scale ? scale[i] : nullptr;
     a.tiles_k = static_cast<int>(p.K);
-    set_tiles(kGram, a, p, p.tile, p.tile);
+    set_tiles(kGram, a, p, tile, tile);
   }
-  return launch_table(kGram, t, square_cfg(*g[0].plan), s);
+  return launch_table(kGram, t, tile == 256 ? kTileBig : kTileSmall, s);
 }
 
-hipError_t launch_poly(const NsGroup* g, int n, float a_coef, float b, float c, hipStream_t s) {
+hipError_t launch_poly(const NsGroup* g, int n, float a_coef, float b, float c, int tile_choice,
+                       hipStream_t s) {
   // The polynomial contracts over the Gram side alone.  Where a 256-tile phase's
   // triangles fill less than two rounds of the chip, it runs on 128-tiles (two blocks
   // per CU, four times the blocks) over the same 256-padded layout: measured 17 %
   // faster for the 12-layer GPT's 768-wide buckets (432 tiles at 256).
-  int tile = g[0].plan->tile;
-  if (tile == 256 && !forced_tile()) {
+  int tile = chosen_tile(*g[0].plan, tile_choice);
+  if (tile_choice == 0 && tile == 256 && !forced_tile()) {
     int64_t tri = 0;
     for (int i = 0; i < n; ++i) tri += tri_tiles_256(g[i].plan->K, g[i].plan->m_pad);
     if (tri < 512) tile = SmallCfg::BM;
@@ -791,10 +799,12 @@ hipError_t launch_poly(const NsGroup* g, int n, float a_coef, float b, float c, 
   return launch_table(kPoly, t, tile == 256 ? kTileBig : kTileSmall, s);
 }
 
-hipError_t launch_combine(const NsGroup* g, int n, const float* const* scale,
-                          bool last, hipStream_t s) {
-  // a phase's buckets agree on the tile and on keeping X^T
-  const TileCfg cfg = g[0].plan->keeps_xt ? kTileBig : square_cfg(*g[0].plan) == kTileBig ? kTileBigX : kTileSmall;
+hipError_t launch_combine(const NsGroup* g, int n, const float* const* scale, bool last,
+                          int tile, hipStream_t s) {
+  // a phase's buckets agree on the tile and on keeping X^T; a 256-tile phase that reads
+  // X (no X^T) may also run its combine on 128-tiles
+  tile = g[0].plan->keeps_xt ? g[0].plan->tile : chosen_tile(*g[0].plan, tile);
+  const TileCfg cfg = g[0].plan->keeps_xt ? kTileBig : tile == 256 ? kTileBigX : kTileSmall;
   GemmTable t{};
   t.ngroups = n;
   for (int i = 0; i < n; ++i) {
@@ -825,7 +835,7 @@ hipError_t launch_combine(const NsGroup* g, int n, const float* const* scale,
     }
     a.scale = scale ? scale[i] : nullptr;
     a.tiles_k = static_cast<int>(p.K);
-    set_tiles(kCombine, a, p, p.tile, p.tile);
+    set_tiles(kCombine, a, p, tile, tile);
   }
   return launch_table(kCombine, t, cfg, s);
 }

@@ -47,6 +47,9 @@ def parse():
     ap.add_argument("--warmup", type=int, default=2)
     ap.add_argument("--workload", type=int, default=1)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-tune", action="store_true",
+                    help="keep the default GEMM tile rules instead of timing the tiles of each "
+                         "Newton-Schulz product once before the warm-up (ma_muon_tune)")
     ap.add_argument("--cpu-budget-s", type=float, default=20.0)
     ap.add_argument("--calibration-copy-mib", type=int, default=0,
                     help="after timing, copy this many MiB device-to-device once (a plain "
@@ -195,6 +198,10 @@ def main():
                      dtype=torch.uint8, device=dev)
     stream = torch.cuda.current_stream(dev)
     state = {"t": 0}
+    shapes = [(b.K, b.A, b.B) for b in wl.muon]
+    # per-shape GEMM tiles, timed once on the workspace (untimed set-up, like the warm-up)
+    ns_tiles = (ma.muon_phases(shapes)[0] * [[0, 0, 0]] if args.no_tune
+                else ma.muon_tune(shapes, reps=3, workspace=ws, stream=stream))
 
     def adamw():
         ma.adamw_step(ap_, ag, am, av, step=state["t"], lr=ah.lr, beta1=ah.beta1, beta2=ah.beta2,
@@ -260,6 +267,7 @@ def main():
         "config": {"workload": wl.name, "muon_buckets": [[b.K, b.A, b.B] for b in wl.muon],
                    "adamw_elements": n, "ns_steps": mh.ns_steps,
                    "cautious_wd": mh.cautious_wd},
+        "ns_tiles": ns_tiles,
         "ns_tflops": round(ns_tflops, 2),
         "ns_mfma_frac": round(ns_tflops / MFMA_BF16_PEAK_TFLOPS, 4),
         "ns_ms": round(ns_ms, 4),

@@ -174,6 +174,34 @@ ma_status ma_newton_schulz(const float* in, float* out, int64_t K, int64_t A, in
                            const ma_muon_hparams* hp, void* workspace, size_t workspace_bytes,
                            void* stream);
 
+/* Per-shape GEMM tiles for the Newton-Schulz products ([DMuon] section 2.4: autotuning
+ * per shape, cached).  For each phase of the bucket list (ma_muon_phases), the Gram,
+ * polynomial and combine launches can run 256 x 256 or 128 x 128 tiles when the phase
+ * is planned on 256-tiles (128 only, otherwise; the combine of a phase whose Gram side
+ * exceeds 2048 only its 256-tile configuration).  Every choice accumulates each output
+ * over the same k order, so results are bitwise the same; only the time differs.
+ *   reps > 0: time every available tile of each product (one warm-up launch, then reps
+ *             launches between two HIP events on `stream`) on the phase's operands in
+ *             the workspace, whose contents are scratch and are overwritten; keep the
+ *             fastest.  This call SYNCHRONISES with `stream` (per product and tile) and
+ *             creates two HIP events; it launches only GEMMs: parameters, gradients and
+ *             momenta are not touched and their pointers may be NULL.
+ *   reps = 0: pin the tiles given in `tiles` (0: back to the default rule).
+ * tiles:  host, 3 x (number of phases) entries (Gram, polynomial, combine per phase):
+ *         output with reps > 0 (may be NULL), input with reps = 0.
+ * hp:     may be NULL (the quintic's coefficients are used for the timed polynomial).
+ * The chosen tiles are kept for this process, keyed by the phase's shapes, and used by
+ * every later ma_muon_step / ma_newton_schulz call whose phase has those shapes.
+ * Errors: MA_ERR_INVALID_ARG (bad shapes, reps outside [0, 1000], tiles NULL with
+ * reps = 0, a pinned tile the phase cannot run), MA_ERR_WORKSPACE (reps > 0),
+ * MA_ERR_HIP. */
+ma_status ma_muon_tune(const ma_muon_bucket* buckets, int32_t n_buckets,
+                       const ma_muon_hparams* hp, void* workspace, size_t workspace_bytes,
+                       void* stream, int32_t reps, int32_t* tiles);
+
+/* Host only: forget every tuned or pinned tile (back to the default rules). */
+void ma_muon_tune_reset(void);
+
 #ifdef __cplusplus
 }
 #endif

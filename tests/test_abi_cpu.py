@@ -235,3 +235,60 @@ def test_optimizer_state_bytes_match_printed(golden):
     assert (w1.numel() + w2.numel()) / 1e6 == pytest.approx(float(g["params_millions"][0]), abs=0.05)
     assert opt.state_bytes_per_param("adamw") == float(g["adamw_state_bytes_per_param"][0])
     assert opt.state_bytes_per_param("muon") == float(g["muon_state_bytes_per_param"][0])
+
+
+W1 = [(48, 768, 768), (12, 768, 3072), (12, 3072, 768)]   # one 256-tile phase
+SMALL = [(2, 200, 330)]                                   # one 128-tile phase
+LONG = [(2, 4096, 4096)]                                  # 256-tile phase keeping X^T
+
+
+def _tune_raw(lib, shapes, reps, tiles, workspace=None, nbytes=0):
+    arr = (_lib._MuonBucket * max(len(shapes), 1))()
+    for i, (K, A, B) in enumerate(shapes):
+        arr[i] = _lib._MuonBucket(K, A, B, 0, 0, 0)
+    out = None
+    if tiles is not None:
+        out = (ctypes.c_int32 * max(len(tiles), 1))(*tiles)
+    return lib.ma_muon_tune(arr, len(shapes), None, workspace, nbytes, None, reps, out)
+
+
+def test_tune_pins_available_tiles(lib):
+    """Pinning (reps = 0) is host-only: every tile a phase can run is accepted, and
+    pinning zeros returns the phase to the default rule."""
+    if os.environ.get("MA_NS_TILE"):
+        pytest.skip("GEMM tile forced")
+    try:
+        for t in ([256, 256, 256], [128, 128, 128], [128, 256, 128], [0, 128, 0]):
+            assert ma.muon_tune(W1, reps=0, tiles=[t]) == [t]
+        assert ma.muon_tune(SMALL, reps=0, tiles=[[128, 128, 128]]) == [[128, 128, 128]]
+        assert ma.muon_tune(LONG, reps=0, tiles=[[128, 128, 256]]) == [[128, 128, 256]]
+        assert ma.muon_tune(W1, reps=0, tiles=[[0, 0, 0]]) == [[0, 0, 0]]
+    finally:
+        ma.muon_tune_reset()
+
+
+@pytest.mark.parametrize("shapes,tiles", [
+    (SMALL, [256, 128, 128]),     # 256-tiles on a 128-padded phase
+    (SMALL, [128, 128, 256]),
+    (LONG, [256, 256, 128]),      # a combine that reads X^T has no 128-tile form
+    (W1, [192, 256, 256]),        # not a tile
+    (W1, [256, -1, 256]),
+])
+def test_tune_rejects_unavailable_tiles(lib, shapes, tiles):
+    if os.environ.get("MA_NS_TILE"):
+        pytest.skip("GEMM tile forced")
+    assert _tune_raw(lib, shapes, 0, tiles) == _lib.MA_ERR_INVALID_ARG
+    assert b"not available" in lib.ma_last_error()
+
+
+def test_tune_rejects_bad_arguments_before_launch(lib):
+    assert _tune_raw(lib, W1, 0, None) == _lib.MA_ERR_INVALID_ARG       # nothing to pin
+    assert _tune_raw(lib, W1, -1, [0, 0, 0]) == _lib.MA_ERR_INVALID_ARG
+    assert _tune_raw(lib, W1, 1001, None) == _lib.MA_ERR_INVALID_ARG
+    assert _tune_raw(lib, [(1, 0, 5)], 0, [0, 0, 0]) == _lib.MA_ERR_INVALID_ARG
+    # timing needs the workspace: checked before any launch
+    assert _tune_raw(lib, W1, 3, None) == _lib.MA_ERR_WORKSPACE
+    assert _tune_raw(lib, W1, 3, None, workspace=256, nbytes=1024) == _lib.MA_ERR_WORKSPACE
+    with pytest.raises(ValueError):
+        ma.muon_tune(W1, reps=0, tiles=[[256, 256, 256], [256, 256, 256]])
+    assert _tune_raw(lib, [], 3, None) == _lib.MA_OK                   # no phase: no-op

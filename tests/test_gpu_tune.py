@@ -1,0 +1,80 @@
+"""Per-shape GEMM tiles (ma_muon_tune): every tile a phase can run accumulates each
+output over the same k order, so a Muon step with any pinned or tuned choice must be
+bitwise identical to the step with the default rule (whose parity against the oracle
+the other GPU tests establish)."""
+import itertools
+
+import pytest
+import torch
+
+import adamw_optimizer_step_muon_amd as ma
+
+pytestmark = pytest.mark.gpu
+
+CASES = {
+    # the 12-layer GPT's buckets: one 256-tile phase whose combine reads X
+    "gpt12": [(48, 768, 768), (12, 768, 3072), (12, 3072, 768)],
+    # 640-wide Gram sides promoted to 256-tiles together: ragged tile edges, transposed
+    "promoted": [(24, 640, 640), (12, 640, 2560), (12, 2560, 640)],
+    # a Gram side above 2048: the combine reads the stored X^T (256-tiles only)
+    "keeps_xt": [(2, 4096, 4096)],
+}
+
+
+def _state(shapes, seed):
+    gen = torch.Generator(device="cuda").manual_seed(seed)
+    out = []
+    for K, A, B in shapes:
+        p = torch.randn((K, A, B), generator=gen, device="cuda")
+        g = 0.02 * torch.randn((K, A, B), generator=gen, device="cuda")
+        m = 0.01 * torch.randn((K, A, B), generator=gen, device="cuda")
+        out.append((p, g, m))
+    return out
+
+
+def _step(state, ws):
+    bks = [(p.clone(), g, m.clone()) for p, g, m in state]
+    ma.muon_step(bks, lr=0.02, momentum=0.95, weight_decay=0.1, workspace=ws)
+    torch.cuda.synchronize()
+    return bks
+
+
+def _same(a, b):
+    return all(torch.equal(x[0], y[0]) and torch.equal(x[2], y[2]) for x, y in zip(a, b))
+
+
+@pytest.mark.parametrize("case", sorted(CASES))
+def test_pinned_tiles_are_bitwise_identical(case):
+    shapes = CASES[case]
+    nph, _ = ma.muon_phases(shapes)
+    assert nph == 1
+    state = _state(shapes, 7)
+    ws = torch.empty(ma.muon_workspace_bytes(shapes), dtype=torch.uint8, device="cuda")
+    ma.muon_tune_reset()
+    try:
+        ref = _step(state, ws)
+        options = [(256, 128), (256, 128), (256,) if case == "keeps_xt" else (256, 128)]
+        for tiles in itertools.product(*options):
+            print(f"{case}: pinned {tiles}", flush=True)
+            assert ma.muon_tune(shapes, reps=0, tiles=[list(tiles)]) == [list(tiles)]
+            assert _same(_step(state, ws), ref), tiles
+    finally:
+        ma.muon_tune_reset()
+
+
+@pytest.mark.parametrize("case", ["gpt12", "keeps_xt"])
+def test_tuned_tiles_keep_results(case):
+    shapes = CASES[case]
+    state = _state(shapes, 8)
+    ws = torch.empty(ma.muon_workspace_bytes(shapes), dtype=torch.uint8, device="cuda")
+    ma.muon_tune_reset()
+    try:
+        ref = _step(state, ws)
+        tiles = ma.muon_tune(shapes, reps=2, workspace=ws)
+        print(f"{case}: tuned {tiles}", flush=True)
+        assert len(tiles) == 1 and all(t in (128, 256) for t in tiles[0])
+        if case == "keeps_xt":
+            assert tiles[0][2] == 256
+        assert _same(_step(state, ws), ref)
+    finally:
+        ma.muon_tune_reset()
