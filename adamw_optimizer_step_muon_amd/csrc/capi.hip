@@ -209,8 +209,9 @@ Tiles tuned_tiles(const Phase& ph) {
 }
 
 // Tiles a product of this phase can run: 256 and 128 on a 256-padded phase (the
-// combine of a phase that keeps X^T only its 256-tile configuration), 128 otherwise.
-int tile_candidates(const Phase& ph, int prod, int (&out)[2]) {
+// combine of a phase that keeps X^T only its 256-tile configuration; 192-row combine
+// tiles where every Gram side pads to a multiple of 192), 128 otherwise.
+int tile_candidates(const Phase& ph, int prod, int (&out)[3]) {
   if (ph.tile != 256 || forced_tile()) {
     out[0] = ph.tile;
     return 1;
@@ -218,11 +219,15 @@ int tile_candidates(const Phase& ph, int prod, int (&out)[2]) {
   out[0] = 256;
   if (prod == kProdCombine && ph.plan[0].keeps_xt) return 1;
   out[1] = 128;
-  return 2;
+  if (prod != kProdCombine) return 2;
+  for (int j = 0; j < ph.n; ++j)
+    if (!combine_192_ok(ph.plan[j])) return 2;
+  out[2] = 192;
+  return 3;
 }
 
 bool tile_available(const Phase& ph, int prod, int tile) {
-  int c[2];
+  int c[3];
   const int nc = tile_candidates(ph, prod, c);
   for (int i = 0; i < nc; ++i)
     if (c[i] == tile) return true;
@@ -621,7 +626,7 @@ ma_status ma_muon_tune(const ma_muon_bucket* buckets, int32_t n_buckets,
     };
     Tiles best{0, 0, 0};
     for (int q = 0; q < 3; ++q) {
-      int cand[2];
+      int cand[3];
       const int nc = tile_candidates(ph, q, cand);
       float best_ms = 0.0f;
       for (int i = 0; i < nc; ++i) {

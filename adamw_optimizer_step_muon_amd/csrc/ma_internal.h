@@ -93,8 +93,10 @@ struct NsGroup {
 };
 // GEMM tiles: `tile` (and `tile_choice`) 0 takes the default for the phase; 128 or 256
 // picks that tile (256 only on a 256-padded phase; the combine of a phase that keeps
-// X^T always runs its own 256-tile configuration).  Every choice accumulates each
-// output over the same k order, so results do not depend on it.
+// X^T always runs its own 256-tile configuration), and the combine also takes 192
+// (192 x 256 tiles) where combine_192_ok holds for every bucket.  Every choice
+// accumulates each output over the same k order, so results do not depend on it.
+bool combine_192_ok(const BucketPlan& p);
 // R = X X^T (lower-triangle tiles, mirrored); R *= scale[i][k]^2 where scale[i] is given
 hipError_t launch_gram(const NsGroup* g, int n, const float* const* scale, int tile,
                        hipStream_t s);

@@ -140,6 +140,15 @@ __device__ __forceinline__ int swz(int r, int c) {
 // no swizzle the read runs at about a third of the rate).
 __device__ __forceinline__ int swz_kn(int r, int c) { return c ^ ((r & 3) << 2); }
 
+// 16-byte chunk c of row j of a transposed epilogue tile with N chunks per row: XOR with
+// j for power-of-two N, a rotation by j otherwise (the 24 chunks of 192-row tiles); a
+// permutation of the row's chunks either way.
+template <int N>
+__device__ __forceinline__ int tswz(int c, int j) {
+  if constexpr ((N & (N - 1)) == 0) return c ^ (j % N);
+  else return (c + j) % N;
+}
+
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef short s16x8 __attribute__((ext_vector_type(8)));
 
@@ -587,7 +596,7 @@ __global__ __launch_bounds__(C::kThreads) void ns_gemm_kernel(GemmTable table) {
   }
   if (!need_t) return;
   // transposed tile [BN][BM]: a lane's 4 consecutive rows are one 8-byte write,
-  // chunk c of row j at c ^ (j % kTChunks)
+  // chunk c of row j at tswz(c, j)
   constexpr int kTChunks = C::BM / 8;
   unsigned short* Ts = smem;
 #pragma unroll
@@ -604,7 +613,7 @@ __global__ __launch_bounds__(C::kThreads) void ns_gemm_kernel(GemmTable table) {
         packed[1] = static_cast<unsigned>(f2bf(acc[i][j][q * 4 + 2])) |
                     (static_cast<unsigned>(f2bf(acc[i][j][q * 4 + 3])) << 16);
         const int c = il0 >> 3, half = (il0 >> 2) & 1;
-        *reinterpret_cast<u32x2*>(Ts + jl * C::BM + ((c ^ (jl % kTChunks)) * 8) + half * 4) = packed;
+        *reinterpret_cast<u32x2*>(Ts + jl * C::BM + tswz<kTChunks>(c, jl) * 8 + half * 4) = packed;
       }
     }
   __syncthreads();
@@ -616,7 +625,7 @@ __global__ __launch_bounds__(C::kThreads) void ns_gemm_kernel(GemmTable table) {
     const int idx = tid + it * C::kThreads;
     const int row = idx / kTChunks;  // local column j of the product
     const int c = idx - row * kTChunks;
-    const u32x4 v = *reinterpret_cast<const u32x4*>(Ts + row * C::BM + ((c ^ (row % kTChunks)) * 8));
+    const u32x4 v = *reinterpret_cast<const u32x4*>(Ts + row * C::BM + tswz<kTChunks>(c, row) * 8);
     *reinterpret_cast<u32x4*>(C2 + (n0 + row) * args.ldc2 + m0 + c * 8) = v;
   }
 }
@@ -644,7 +653,11 @@ using Big8K64 = Cfg<256, 256, 64, 2, 4, 3, false, 2>;
 using Big8K64X = Cfg<256, 256, 64, 2, 4, 3, true, 2>;  // combine of Gram sides <= 2048
 using Big8 = Cfg<256, 256, 32, 2, 4, 4, false>;
 using SmallCfg = Cfg<128, 128, 64, 4, 2, 2, true>;
-enum TileCfg { kTileSmall = 0, kTileBig = 1, kTileBigX = 2 };
+// Combine only: 192 x 256 tiles (8 waves of 96 x 64) for Gram sides padded to a multiple
+// of 768, where three-quarter tiles split the work into rounds of the chip with less
+// left over (the 12-layer GPT: 1296 256-tiles are 5.06 rounds, 1728 192-row tiles 6.75).
+using Mid8X = Cfg<192, 256, 64, 2, 4, 3, true, 2>;
+enum TileCfg { kTileSmall = 0, kTileBig = 1, kTileBigX = 2, kTileMidX = 3 };
 
 template <class C>
 hipError_t launch_cfg(int epi, const GemmTable& t, hipStream_t s) {
@@ -682,7 +695,7 @@ void set_tiles(int epi, GemmArgs& a, const BucketPlan& p, int bm, int bn) {
   static const int spread = env_int("MA_NS_SPREAD", -1);
   a.band = epi == kCombine ? (band_combine > 0 ? band_combine : 1) : band_tri;
   a.xcd_remap = xcd;
-  a.spread = spread >= 0 ? spread : (bm == 256 ? 1 : 0);
+  a.spread = spread >= 0 ? spread : (bm >= 192 ? 1 : 0);
   if (epi == kCombine) {
     a.tiles_m = static_cast<int>(p.m_pad / bm);
     a.tiles_n = static_cast<int>(p.n_pad / bn);
@@ -708,6 +721,14 @@ hipError_t launch_table(int epi, GemmTable& t, TileCfg cfg, hipStream_t s) {
   if (cfg == kTileBig)
     return big_variant() == 1 ? launch_cfg<Big8>(epi, t, s) : launch_cfg<Big8K64>(epi, t, s);
   if (cfg == kTileBigX) return launch_cfg<Big8K64X>(epi, t, s);
+  if (cfg == kTileMidX) {
+    if (epi != kCombine) return hipErrorInvalidValue;  // not a symmetric tile
+    const int blocks = t.start[t.ngroups];
+    if (blocks <= 0) return hipSuccess;
+    hipLaunchKernelGGL((ns_gemm_kernel<Mid8X, kCombine>), dim3(static_cast<unsigned>(blocks)),
+                       dim3(Mid8X::kThreads), 0, s, t);
+    return hipGetLastError();
+  }
   return launch_cfg<SmallCfg>(epi, t, s);
 }
 
@@ -719,6 +740,10 @@ int chosen_tile(const BucketPlan& p, int choice) {
 }
 
 }  // namespace
+
+bool combine_192_ok(const BucketPlan& p) {
+  return p.tile == 256 && !p.keeps_xt && p.m_pad % Mid8X::BM == 0;
+}
 
 int64_t tri_tiles_256(int64_t K, int64_t m) {
   const int64_t m256 = (m + 255) / 256;
@@ -803,8 +828,13 @@ hipError_t launch_combine(const NsGroup* g, int n, const float* const* scale, bo
                           int tile, hipStream_t s) {
   // a phase's buckets agree on the tile and on keeping X^T; a 256-tile phase that reads
   // X (no X^T) may also run its combine on 128-tiles
+  bool mid = tile == 192 && !forced_tile();
+  for (int i = 0; i < n && mid; ++i) mid = combine_192_ok(*g[i].plan);
   tile = g[0].plan->keeps_xt ? g[0].plan->tile : chosen_tile(*g[0].plan, tile);
-  const TileCfg cfg = g[0].plan->keeps_xt ? kTileBig : tile == 256 ? kTileBigX : kTileSmall;
+  const TileCfg cfg = g[0].plan->keeps_xt ? kTileBig
+                      : mid                ? kTileMidX
+                      : tile == 256        ? kTileBigX
+                                           : kTileSmall;
   GemmTable t{};
   t.ngroups = n;
   for (int i = 0; i < n; ++i) {
@@ -835,7 +865,7 @@ hipError_t launch_combine(const NsGroup* g, int n, const float* const* scale, bo
     }
     a.scale = scale ? scale[i] : nullptr;
     a.tiles_k = static_cast<int>(p.K);
-    set_tiles(kCombine, a, p, tile, tile);
+    set_tiles(kCombine, a, p, mid ? Mid8X::BM : tile, mid ? Mid8X::BN : tile);
   }
   return launch_table(kCombine, t, cfg, s);
 }

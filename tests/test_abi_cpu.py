@@ -258,7 +258,7 @@ def test_tune_pins_available_tiles(lib):
     if os.environ.get("MA_NS_TILE"):
         pytest.skip("GEMM tile forced")
     try:
-        for t in ([256, 256, 256], [128, 128, 128], [128, 256, 128], [0, 128, 0]):
+        for t in ([256, 256, 256], [128, 128, 128], [128, 256, 128], [0, 128, 0], [256, 128, 192]):
             assert ma.muon_tune(W1, reps=0, tiles=[t]) == [t]
         assert ma.muon_tune(SMALL, reps=0, tiles=[[128, 128, 128]]) == [[128, 128, 128]]
         assert ma.muon_tune(LONG, reps=0, tiles=[[128, 128, 256]]) == [[128, 128, 256]]
@@ -271,7 +271,12 @@ def test_tune_pins_available_tiles(lib):
     (SMALL, [256, 128, 128]),     # 256-tiles on a 128-padded phase
     (SMALL, [128, 128, 256]),
     (LONG, [256, 256, 128]),      # a combine that reads X^T has no 128-tile form
-    (W1, [192, 256, 256]),        # not a tile
+    (W1, [192, 256, 256]),        # 192-row tiles are for the combine only
+    (W1, [256, 192, 256]),
+    (SMALL, [128, 128, 192]),
+    (LONG, [256, 256, 192]),
+    ([(20, 1280, 1280)], [256, 256, 192]),   # 1280 is not a multiple of 192
+    (W1, [256, 256, 64]),         # not a tile
     (W1, [256, -1, 256]),
 ])
 def test_tune_rejects_unavailable_tiles(lib, shapes, tiles):

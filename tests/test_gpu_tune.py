@@ -18,6 +18,8 @@ CASES = {
     "promoted": [(24, 640, 640), (12, 640, 2560), (12, 2560, 640)],
     # a Gram side above 2048: the combine reads the stored X^T (256-tiles only)
     "keeps_xt": [(2, 4096, 4096)],
+    # a 1280-wide Gram side (not a multiple of 192): 256- and 128-tiles only
+    "gpt20": [(20, 1280, 1280), (5, 1280, 5120), (5, 5120, 1280)],
 }
 
 
@@ -53,7 +55,9 @@ def test_pinned_tiles_are_bitwise_identical(case):
     ma.muon_tune_reset()
     try:
         ref = _step(state, ws)
-        options = [(256, 128), (256, 128), (256,) if case == "keeps_xt" else (256, 128)]
+        # the combine of Gram sides padded to 768 also has 192-row tiles
+        combine = {"keeps_xt": (256,), "gpt20": (256, 128)}.get(case, (256, 128, 192))
+        options = [(256, 128), (256, 128), combine]
         for tiles in itertools.product(*options):
             print(f"{case}: pinned {tiles}", flush=True)
             assert ma.muon_tune(shapes, reps=0, tiles=[list(tiles)]) == [list(tiles)]
@@ -72,7 +76,8 @@ def test_tuned_tiles_keep_results(case):
         ref = _step(state, ws)
         tiles = ma.muon_tune(shapes, reps=2, workspace=ws)
         print(f"{case}: tuned {tiles}", flush=True)
-        assert len(tiles) == 1 and all(t in (128, 256) for t in tiles[0])
+        assert len(tiles) == 1 and all(t in (128, 256) for t in tiles[0][:2])
+        assert tiles[0][2] in (128, 192, 256)
         if case == "keeps_xt":
             assert tiles[0][2] == 256
         assert _same(_step(state, ws), ref)
