@@ -46,13 +46,13 @@ class _MuonHParams(ctypes.Structure):
                 ("weight_decay", ctypes.c_float), ("ns_eps", ctypes.c_float),
                 ("nesterov", ctypes.c_int32), ("cautious_wd", ctypes.c_int32),
                 ("ns_steps", ctypes.c_int32), ("scale_mode", ctypes.c_int32),
-                ("ns_coeffs", ctypes.POINTER(ctypes.c_float))]
+                ("ns_coeffs", ctypes.POINTER(ctypes.c_float)), ("ns_mode", ctypes.c_int32)]
 
 
 class _MuonRoute(ctypes.Structure):
     _fields_ = [("transposed", ctypes.c_int32), ("m", ctypes.c_int32), ("n", ctypes.c_int32),
                 ("ns_steps_run", ctypes.c_int32), ("m_pad", ctypes.c_int32),
-                ("n_pad", ctypes.c_int32)]
+                ("n_pad", ctypes.c_int32), ("ns_mode_run", ctypes.c_int32)]
 
 
 class _AdamWHParams(ctypes.Structure):
@@ -72,6 +72,7 @@ class Route:
     ns_steps_run: int
     m_pad: int
     n_pad: int
+    ns_mode_run: int = 0
 
 
 _lib: Optional[ctypes.CDLL] = None
@@ -99,7 +100,7 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
                                             ctypes.POINTER(_MuonHParams)]
     lib.ma_muon_phases.restype = ctypes.c_int32
     lib.ma_muon_phases.argtypes = [ctypes.POINTER(_MuonBucket), ctypes.c_int32,
-                                   ctypes.POINTER(ctypes.c_int32)]
+                                   ctypes.POINTER(_MuonHParams), ctypes.POINTER(ctypes.c_int32)]
     lib.ma_muon_step.restype = ctypes.c_int
     lib.ma_muon_step.argtypes = [ctypes.POINTER(_MuonBucket), ctypes.c_int32,
                                  ctypes.POINTER(_MuonHParams), ctypes.c_void_p, ctypes.c_size_t,
@@ -178,10 +179,11 @@ def _scratch(nbytes: int, device, stream):
 
 
 def _muon_hparams(lr, momentum, weight_decay, nesterov, ns_steps, ns_coeffs, ns_eps,
-                  cautious_wd, scale_mode):
+                  cautious_wd, scale_mode, ns_mode=0):
     hp = _MuonHParams(lr=lr, momentum=momentum, weight_decay=weight_decay, ns_eps=ns_eps,
                       nesterov=int(bool(nesterov)), cautious_wd=int(bool(cautious_wd)),
-                      ns_steps=int(ns_steps), scale_mode=int(scale_mode))
+                      ns_steps=int(ns_steps), scale_mode=int(scale_mode),
+                      ns_mode=int(ns_mode))
     keep = None
     if ns_coeffs is not None:
         flat = [float(x) for row in ns_coeffs for x in (row if hasattr(row, "__len__") else [row])]
@@ -210,7 +212,8 @@ def muon_route_of(A: int, B: int, ns_steps: int = 5) -> Route:
     hp = _MuonHParams(ns_steps=int(ns_steps))
     out = _MuonRoute()
     _check(load().ma_muon_route_of(int(A), int(B), ctypes.byref(hp), ctypes.byref(out)))
-    return Route(bool(out.transposed), out.m, out.n, out.ns_steps_run, out.m_pad, out.n_pad)
+    return Route(bool(out.transposed), out.m, out.n, out.ns_steps_run, out.m_pad, out.n_pad,
+                 out.ns_mode_run)
 
 
 def _bucket_array(buckets):
@@ -221,30 +224,39 @@ def _bucket_array(buckets):
     return arr
 
 
-def muon_workspace_bytes(shapes: Sequence[Sequence[int]]) -> int:
+def _mode_hparams(ns_mode: int):
+    """Hyperparameters that only carry ns_mode (for the shape-only calls)."""
+    hp, _ = _muon_hparams(0.0, 0.0, 0.0, True, 5, None, 1e-7, False, 0, ns_mode)
+    return hp
+
+
+def muon_workspace_bytes(shapes: Sequence[Sequence[int]], ns_mode: int = 0) -> int:
     """Workspace bytes for buckets of these (K, A, B) shapes."""
     arr = (_MuonBucket * max(len(shapes), 1))()
     for i, (K, A, B) in enumerate(shapes):
         arr[i] = _MuonBucket(int(K), int(A), int(B), 0, 0, 0)
-    return int(load().ma_muon_workspace_bytes(arr, len(shapes), None))
+    hp = _mode_hparams(ns_mode)
+    return int(load().ma_muon_workspace_bytes(arr, len(shapes), ctypes.byref(hp)))
 
 
-def muon_phases(shapes: Sequence[Sequence[int]]):
-    """(number of phases, phase index per bucket) for buckets of these (K, A, B) shapes:
-    each phase runs 3 x ns_steps Newton-Schulz GEMM launches (ma_muon_phases)."""
+def muon_phases(shapes: Sequence[Sequence[int]], ns_mode: int = 0):
+    """(number of phases, phase index per bucket) for buckets of these (K, A, B) shapes
+    (ma_muon_phases): each phase runs its own Newton-Schulz GEMM launches, 3 x ns_steps
+    of them for the printed iteration."""
     n = len(shapes)
     arr = (_MuonBucket * max(n, 1))()
     for i, (K, A, B) in enumerate(shapes):
         arr[i] = _MuonBucket(int(K), int(A), int(B), 0, 0, 0)
     out = (ctypes.c_int32 * max(n, 1))()
-    count = int(load().ma_muon_phases(arr, n, out))
+    hp = _mode_hparams(ns_mode)
+    count = int(load().ma_muon_phases(arr, n, ctypes.byref(hp), out))
     if count < 0:
         _check(count)
     return count, [int(out[i]) for i in range(n)]
 
 
 def muon_tune(shapes: Sequence[Sequence[int]], *, reps: int = 3, tiles=None, workspace=None,
-              stream=None, device=None):
+              stream=None, device=None, ns_mode: int = 0):
     """Per-shape Newton-Schulz GEMM tiles (ma_muon_tune) for buckets of these (K, A, B)
     shapes.  reps > 0: time the available tiles on the workspace (scratch; allocated for
     the call when None) and keep the fastest; reps == 0: pin `tiles`.  Returns the tiles
@@ -255,23 +267,24 @@ def muon_tune(shapes: Sequence[Sequence[int]], *, reps: int = 3, tiles=None, wor
     arr = (_MuonBucket * max(n, 1))()
     for i, (K, A, B) in enumerate(shapes):
         arr[i] = _MuonBucket(int(K), int(A), int(B), 0, 0, 0)
-    nph, _ = muon_phases(shapes)
-    out = (ctypes.c_int32 * max(3 * nph, 1))()
+    hp = _mode_hparams(ns_mode)
     lib = load()
+    nph, _ = muon_phases(shapes, ns_mode)
+    out = (ctypes.c_int32 * max(3 * nph, 1))()
     if int(reps) == 0:
         flat = [int(t) for ph in (tiles or []) for t in ph]
         if len(flat) != 3 * nph:
             raise ValueError(f"tiles needs {nph} phases of 3 entries")
         for i, t in enumerate(flat):
             out[i] = t
-        _check(lib.ma_muon_tune(arr, n, None, None, 0, None, 0, out))
+        _check(lib.ma_muon_tune(arr, n, ctypes.byref(hp), None, 0, None, 0, out))
     else:
         device = torch.device("cuda", torch.cuda.current_device()) if device is None else device
-        need = int(lib.ma_muon_workspace_bytes(arr, n, None))
+        need = int(lib.ma_muon_workspace_bytes(arr, n, ctypes.byref(hp)))
         if workspace is None and need > 0:
             workspace = _scratch(need, device, stream)
         ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
-        _check(lib.ma_muon_tune(arr, n, None, _ptr(workspace), ws_bytes,
+        _check(lib.ma_muon_tune(arr, n, ctypes.byref(hp), _ptr(workspace), ws_bytes,
                                 _stream_handle(stream, device), int(reps), out))
     return [[int(out[3 * i + q]) for q in range(3)] for i in range(nph)]
 
@@ -283,9 +296,11 @@ def muon_tune_reset() -> None:
 
 def muon_step(buckets, *, lr: float, momentum: float = 0.95, weight_decay: float = 0.0,
               nesterov: bool = True, ns_steps: int = 5, ns_coeffs=None, ns_eps: float = 1e-7,
-              cautious_wd: bool = False, scale_mode: int = 0, workspace=None, stream=None):
+              cautious_wd: bool = False, scale_mode: int = 0, ns_mode: int = 0, workspace=None,
+              stream=None):
     """One Muon step (ma_muon_step) on (param, grad, momentum) triples of (K, A, B) or
-    (A, B) fp32 GPU tensors.  Returns the routing report of each bucket."""
+    (A, B) fp32 GPU tensors.  ns_mode 1 runs the Gram-space iteration where n >= 2 m.
+    Returns the routing report of each bucket."""
     import torch
 
     stacks = []
@@ -299,7 +314,7 @@ def muon_step(buckets, *, lr: float, momentum: float = 0.95, weight_decay: float
     lib = load()
     arr = _bucket_array(stacks)
     hp, _keep = _muon_hparams(lr, momentum, weight_decay, nesterov, ns_steps, ns_coeffs, ns_eps,
-                              cautious_wd, scale_mode)
+                              cautious_wd, scale_mode, ns_mode)
     need = int(lib.ma_muon_workspace_bytes(arr, len(stacks), ctypes.byref(hp)))
     device = stacks[0][0].device if stacks else None
     if workspace is None and need > 0:
@@ -308,7 +323,7 @@ def muon_step(buckets, *, lr: float, momentum: float = 0.95, weight_decay: float
     ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
     _check(lib.ma_muon_step(arr, len(stacks), ctypes.byref(hp), _ptr(workspace), ws_bytes,
                             _stream_handle(stream, device) if device is not None else 0, routes))
-    return [Route(bool(r.transposed), r.m, r.n, r.ns_steps_run, r.m_pad, r.n_pad)
+    return [Route(bool(r.transposed), r.m, r.n, r.ns_steps_run, r.m_pad, r.n_pad, r.ns_mode_run)
             for r in routes[:len(stacks)]]
 
 
@@ -334,7 +349,7 @@ def newton_schulz_workspace_bytes(K: int, A: int, B: int) -> int:
 
 
 def newton_schulz(inp, out, *, ns_steps: int = 5, ns_coeffs=None, ns_eps: float = 1e-7,
-                  workspace=None, stream=None) -> None:
+                  ns_mode: int = 0, workspace=None, stream=None) -> None:
     """The orthogonalisation alone (ma_newton_schulz): out = NS(inp), (K, A, B) or (A, B)."""
     import torch
 
@@ -344,7 +359,7 @@ def newton_schulz(inp, out, *, ns_steps: int = 5, ns_coeffs=None, ns_eps: float 
     if i3.shape != o3.shape:
         raise ValueError("inp and out shapes differ")
     K, A, B = i3.shape
-    hp, _keep = _muon_hparams(0.0, 0.0, 0.0, True, ns_steps, ns_coeffs, ns_eps, False, 0)
+    hp, _keep = _muon_hparams(0.0, 0.0, 0.0, True, ns_steps, ns_coeffs, ns_eps, False, 0, ns_mode)
     need = newton_schulz_workspace_bytes(K, A, B)
     if workspace is None and need > 0:
         workspace = _scratch(need, inp.device, stream)

@@ -66,6 +66,8 @@ ma_status check_hparams(const ma_muon_hparams* hp) {
     return fail(MA_ERR_INVALID_ARG, "ns_steps %d outside [0, %d]", hp->ns_steps, MA_MAX_NS_STEPS);
   if (hp->scale_mode != 0 && hp->scale_mode != 1)
     return fail(MA_ERR_INVALID_ARG, "scale_mode %d is not 0 or 1", hp->scale_mode);
+  if (hp->ns_mode != 0 && hp->ns_mode != 1)
+    return fail(MA_ERR_INVALID_ARG, "ns_mode %d is not 0 or 1", hp->ns_mode);
   if (hp->ns_coeffs) {
     for (int i = 0; i < 3 * hp->ns_steps; ++i)
       if (!finite(hp->ns_coeffs[i])) return fail(MA_ERR_INVALID_ARG, "non-finite ns_coeffs[%d]", i);
@@ -104,6 +106,7 @@ ma_muon_route route_of(const BucketPlan& p, int ns_steps) {
   r.ns_steps_run = ns_steps;
   r.m_pad = static_cast<int32_t>(p.m_pad);
   r.n_pad = static_cast<int32_t>(p.n_pad);
+  r.ns_mode_run = (p.gram_space && ns_steps > 0) ? 1 : 0;
   return r;
 }
 
@@ -124,7 +127,8 @@ struct Phase {
 
 bool phase_accepts(const Phase& ph, const BucketPlan& p) {
   return ph.n > 0 && ph.n < kMaxGemmGroups && ph.tile == p.tile &&
-         ph.plan[0].keeps_xt == p.keeps_xt && ph.bytes + p.bytes <= kPhaseBytes;
+         ph.plan[0].keeps_xt == p.keeps_xt && ph.plan[0].gram_space == p.gram_space &&
+         ph.bytes + p.bytes <= kPhaseBytes;
 }
 
 void phase_add(Phase& ph, const BucketPlan& p, int bucket) {
@@ -154,20 +158,24 @@ void promote(Phase& ph) {
   if (!fills_256(tri, comb)) return;
   Phase q;
   for (int j = 0; j < ph.n; ++j) {
-    const BucketPlan p = plan_bucket(ph.plan[j].K, ph.plan[j].A, ph.plan[j].B, 256);
+    const BucketPlan p =
+        plan_bucket(ph.plan[j].K, ph.plan[j].A, ph.plan[j].B, 256, ph.plan[j].gram_space);
     if (p.keeps_xt) return;
     phase_add(q, p, ph.bucket[j]);
   }
   if (q.bytes <= kPhaseBytes) ph = q;
 }
 
-// Calls fn(phase) for each phase of the bucket list, in order.
+// Calls fn(phase) for each phase of the bucket list, in order (ns_mode: see
+// ma_muon_hparams; Gram-space buckets form phases of their own).
 template <class Fn>
-ma_status for_each_phase(const ma_muon_bucket* buckets, int32_t n_buckets, Fn&& fn) {
+ma_status for_each_phase(const ma_muon_bucket* buckets, int32_t n_buckets, int32_t ns_mode,
+                         Fn&& fn) {
   Phase ph;
   for (int32_t i = 0; i < n_buckets; ++i) {
     if (buckets[i].K <= 0) continue;
-    const BucketPlan p = plan_bucket(buckets[i].K, buckets[i].A, buckets[i].B);
+    const BucketPlan p = plan_bucket(buckets[i].K, buckets[i].A, buckets[i].B, 0,
+                                     wants_gram_space(ns_mode, buckets[i].A, buckets[i].B));
     if (ph.n > 0 && !phase_accepts(ph, p)) {
       promote(ph);
       const ma_status st = fn(ph);
@@ -197,7 +205,8 @@ std::vector<int64_t> phase_key(const Phase& ph) {
   std::vector<int64_t> k{ph.n};
   for (int j = 0; j < ph.n; ++j) {
     const BucketPlan& p = ph.plan[j];
-    k.insert(k.end(), {p.K, p.m_pad, p.n_pad, p.transposed ? 1 : 0, p.keeps_xt ? 1 : 0});
+    k.insert(k.end(), {p.K, p.m_pad, p.n_pad, p.transposed ? 1 : 0, p.keeps_xt ? 1 : 0,
+                       p.gram_space ? 1 : 0});
   }
   return k;
 }
@@ -260,8 +269,77 @@ void phase_groups(const Phase& ph, char* ws, int cur, NsGroup* g) {
 // inv[k] = 1 / (||U_k|| + eps) are in its workspace.  On
 // return out[j] holds bucket j's result in the matrix's own orientation (row stride
 // ldo[j]) and oscale[j] the per-matrix factor still to apply (inv when no iteration ran).
+// The Gram-space form of the same iteration ("DMuon: Efficient Distributed Muon Training
+// with Near-Adam Overhead", section 2.2, Gram Newton-Schulz), for a phase of buckets
+// planned with gram_space and ns_steps >= 1.  With X_{k+1} = P_k X_k and P_k = a I +
+// b R_k + c R_k^2 (R_k = X_k X_k^T), R_{k+1} = P_k R_k P_k and X_N = Q_N X_0 with
+// Q_N = P_{N-1} ... P_0; every R_k, P_k, Q_k is a polynomial in R_0, so all of them and
+// their products are symmetric and run on lower-triangle tiles.  Launches: the Gram of
+// X_0 (normalised in its epilogue), per step the polynomial, Q <- P Q (from the second
+// step), T = R P and R <- P T (all but the last step), then the combine X = inv Q U.
+// Outputs as run_ns.
+ma_status run_ns_gram_space(const Phase& ph, const ma_muon_hparams* hp, char* ws,
+                            hipStream_t s, const unsigned short** out, int64_t* ldo,
+                            const float** oscale) {
+  NsGroup g[kMaxGemmGroups];
+  SymProd sp[kMaxGemmGroups];
+  const float* inv[kMaxGemmGroups];
+  for (int j = 0; j < ph.n; ++j) inv[j] = at<const float>(ws, ph.base[j] + ph.plan[j].off_inv);
+  const Tiles tiles = tuned_tiles(ph);
+  phase_groups(ph, ws, 0, g);  // X = X_0 (bf16 U), Xn = the output, R = R_0
+  auto buf = [&](int j, size_t off) { return at<unsigned short>(ws + ph.base[j], off); };
+  hipError_t e = launch_gram(g, ph.n, inv, tiles[kProdGram], s);
+  if (e != hipSuccess) return hip_fail(e, "gram launch");
+  int rc = 0, qc = 0;  // current R (off_r / off_r2) and Q (off_q[qc])
+  const int N = hp->ns_steps;
+  for (int it = 0; it < N; ++it) {
+    const NsCoeffs c = coeff_at(hp, it);
+    // P_k; the first one is Q_1 itself (Q_0 = I), so it goes straight into Q[0]
+    for (int j = 0; j < ph.n; ++j) {
+      const BucketPlan& p = ph.plan[j];
+      g[j].R = buf(j, rc ? p.off_r2 : p.off_r);
+      g[j].P = buf(j, it == 0 ? p.off_q[0] : p.off_p);
+    }
+    e = launch_poly(g, ph.n, c.a, c.b, c.c, tiles[kProdPoly], s);
+    if (e != hipSuccess) return hip_fail(e, "poly launch");
+    if (it > 0) {  // Q <- P Q
+      for (int j = 0; j < ph.n; ++j)
+        sp[j] = SymProd{&ph.plan[j], g[j].P, buf(j, ph.plan[j].off_q[qc]),
+                        buf(j, ph.plan[j].off_q[qc ^ 1])};
+      e = launch_sym(sp, ph.n, tiles[kProdPoly], s);
+      if (e != hipSuccess) return hip_fail(e, "Q product launch");
+      qc ^= 1;
+    }
+    if (it + 1 < N) {  // T = R P, then R <- P T
+      for (int j = 0; j < ph.n; ++j)
+        sp[j] = SymProd{&ph.plan[j], g[j].R, g[j].P, buf(j, ph.plan[j].off_t)};
+      e = launch_sym(sp, ph.n, tiles[kProdPoly], s);
+      if (e != hipSuccess) return hip_fail(e, "R P product launch");
+      for (int j = 0; j < ph.n; ++j)
+        sp[j] = SymProd{&ph.plan[j], g[j].P, buf(j, ph.plan[j].off_t),
+                        buf(j, rc ? ph.plan[j].off_r : ph.plan[j].off_r2)};
+      e = launch_sym(sp, ph.n, tiles[kProdPoly], s);
+      if (e != hipSuccess) return hip_fail(e, "R update launch");
+      rc ^= 1;
+    }
+  }
+  // X_N = Q_N X_0 = inv Q_N U, in the parameter's orientation
+  for (int j = 0; j < ph.n; ++j) g[j].P = buf(j, ph.plan[j].off_q[qc]);
+  e = launch_combine(g, ph.n, inv, true, tiles[kProdCombine], s);
+  if (e != hipSuccess) return hip_fail(e, "combine launch");
+  for (int j = 0; j < ph.n; ++j) {
+    const BucketPlan& p = ph.plan[j];
+    out[j] = buf(j, (p.keeps_xt && p.transposed) ? p.off_xt[1] : p.off_x[1]);
+    ldo[j] = p.transposed ? p.m_pad : p.n_pad;
+    oscale[j] = nullptr;
+  }
+  return MA_OK;
+}
+
 ma_status run_ns(const Phase& ph, const ma_muon_hparams* hp, char* ws, hipStream_t s,
                  const unsigned short** out, int64_t* ldo, const float** oscale) {
+  if (ph.plan[0].gram_space && hp->ns_steps > 0)
+    return run_ns_gram_space(ph, hp, ws, s, out, ldo, oscale);
   NsGroup g[kMaxGemmGroups];
   const float* inv[kMaxGemmGroups];
   for (int j = 0; j < ph.n; ++j) inv[j] = at<const float>(ws, ph.base[j] + ph.plan[j].off_inv);
@@ -331,7 +409,12 @@ int forced_tile() {
   return t;
 }
 
-BucketPlan plan_bucket(int64_t K, int64_t A, int64_t B, int tile) {
+bool wants_gram_space(int32_t ns_mode, int64_t A, int64_t B) {
+  const int64_t m = A < B ? A : B, n = A < B ? B : A;
+  return ns_mode == 1 && n >= 2 * m;
+}
+
+BucketPlan plan_bucket(int64_t K, int64_t A, int64_t B, int tile, bool gram_space) {
   BucketPlan p{};
   p.K = K;
   p.A = A;
@@ -358,6 +441,18 @@ BucketPlan plan_bucket(int64_t K, int64_t A, int64_t B, int tile) {
   off = align256(off + rb);
   p.off_p = off;
   off = align256(off + rb);
+  p.gram_space = gram_space;
+  p.off_r2 = p.off_q[0] = p.off_q[1] = p.off_t = 0;
+  if (gram_space) {
+    p.off_r2 = off;
+    off = align256(off + rb);
+    for (int i = 0; i < 2; ++i) {
+      p.off_q[i] = off;
+      off = align256(off + rb);
+    }
+    p.off_t = off;
+    off = align256(off + rb);
+  }
   p.off_part = off;
   off = align256(off + static_cast<size_t>(K * p.nblk) * 4);
   p.off_inv = off;
@@ -399,19 +494,19 @@ ma_status ma_muon_route_of(int64_t A, int64_t B, const ma_muon_hparams* hp, ma_m
 
 size_t ma_muon_workspace_bytes(const ma_muon_bucket* buckets, int32_t n_buckets,
                                const ma_muon_hparams* hp) {
-  (void)hp;
   if (n_buckets <= 0 || !buckets) return 0;
   for (int32_t i = 0; i < n_buckets; ++i)
     if (buckets[i].K > 0 && (buckets[i].A < 1 || buckets[i].B < 1)) return 0;
   size_t need = 0;
-  for_each_phase(buckets, n_buckets, [&](const Phase& ph) {
+  for_each_phase(buckets, n_buckets, hp ? hp->ns_mode : 0, [&](const Phase& ph) {
     if (ph.bytes > need) need = ph.bytes;
     return MA_OK;
   });
   return need;
 }
 
-int32_t ma_muon_phases(const ma_muon_bucket* buckets, int32_t n_buckets, int32_t* phase_of) {
+int32_t ma_muon_phases(const ma_muon_bucket* buckets, int32_t n_buckets,
+                       const ma_muon_hparams* hp, int32_t* phase_of) {
   g_last_error.clear();
   if (n_buckets < 0) return fail(MA_ERR_INVALID_ARG, "n_buckets %d < 0", n_buckets);
   if (n_buckets > 0 && !buckets) return fail(MA_ERR_INVALID_ARG, "buckets is NULL");
@@ -421,7 +516,7 @@ int32_t ma_muon_phases(const ma_muon_bucket* buckets, int32_t n_buckets, int32_t
     if (phase_of) phase_of[i] = -1;
   }
   int32_t count = 0;
-  for_each_phase(buckets, n_buckets, [&](const Phase& ph) {
+  for_each_phase(buckets, n_buckets, hp ? hp->ns_mode : 0, [&](const Phase& ph) {
     if (phase_of)
       for (int j = 0; j < ph.n; ++j) phase_of[ph.bucket[j]] = count;
     ++count;
@@ -476,15 +571,15 @@ ma_status ma_muon_step(const ma_muon_bucket* buckets, int32_t n_buckets,
   }
   if (route_out) {
     // from the plans the phases run (a phase may re-plan its buckets' tile)
-    for (int32_t i = 0; i < n_buckets; ++i) route_out[i] = ma_muon_route{0, 0, 0, 0, 0, 0};
-    for_each_phase(buckets, n_buckets, [&](const Phase& ph) {
+    for (int32_t i = 0; i < n_buckets; ++i) route_out[i] = ma_muon_route{0, 0, 0, 0, 0, 0, 0};
+    for_each_phase(buckets, n_buckets, hp->ns_mode, [&](const Phase& ph) {
       for (int j = 0; j < ph.n; ++j) route_out[ph.bucket[j]] = route_of(ph.plan[j], hp->ns_steps);
       return MA_OK;
     });
   }
   hipStream_t s = static_cast<hipStream_t>(stream);
   char* ws = static_cast<char*>(workspace);
-  return for_each_phase(buckets, n_buckets, [&](const Phase& ph) -> ma_status {
+  return for_each_phase(buckets, n_buckets, hp->ns_mode, [&](const Phase& ph) -> ma_status {
     for (int j = 0; j < ph.n; ++j) {
       const ma_muon_bucket& b = buckets[ph.bucket[j]];
       const ma_status st2 = prep_bucket(ph.plan[j], b.grad, b.momentum, hp, ws + ph.base[j], s);
@@ -513,7 +608,10 @@ ma_status ma_muon_step(const ma_muon_bucket* buckets, int32_t n_buckets,
 
 size_t ma_newton_schulz_workspace_bytes(int64_t K, int64_t A, int64_t B) {
   if (K <= 0 || A < 1 || B < 1) return 0;
-  return plan_bucket(K, A, B).bytes;
+  // enough for either ns_mode (the Gram-space plan adds four m x m buffers)
+  const size_t plain = plan_bucket(K, A, B).bytes;
+  const size_t gs = plan_bucket(K, A, B, 0, wants_gram_space(1, A, B)).bytes;
+  return plain > gs ? plain : gs;
 }
 
 ma_status ma_newton_schulz(const float* in, float* out, int64_t K, int64_t A, int64_t B,
@@ -531,7 +629,7 @@ ma_status ma_newton_schulz(const float* in, float* out, int64_t K, int64_t A, in
   const int64_t bytes = K * A * B * 4;
   if (overlap(range_of(in, bytes), range_of(out, bytes)))
     return fail(MA_ERR_INVALID_ARG, "in and out overlap");
-  const BucketPlan p = plan_bucket(K, A, B);
+  const BucketPlan p = plan_bucket(K, A, B, 0, wants_gram_space(hp->ns_mode, A, B));
   if (!workspace) return fail(MA_ERR_WORKSPACE, "workspace is NULL, %zu bytes needed", p.bytes);
   if (reinterpret_cast<uintptr_t>(workspace) & 255u)
     return fail(MA_ERR_WORKSPACE, "workspace must be 256-byte aligned");
@@ -572,7 +670,7 @@ ma_status ma_muon_tune(const ma_muon_bucket* buckets, int32_t n_buckets,
   if (reps == 0) {
     // pin: check every requested tile first, then store (all zero: back to the rule)
     int phase = 0;
-    ma_status st = for_each_phase(buckets, n_buckets, [&](const Phase& ph) -> ma_status {
+    ma_status st = for_each_phase(buckets, n_buckets, hp ? hp->ns_mode : 0, [&](const Phase& ph) -> ma_status {
       for (int q = 0; q < 3; ++q) {
         const int t = tiles[3 * phase + q];
         if (t != 0 && !tile_available(ph, q, t))
@@ -585,7 +683,7 @@ ma_status ma_muon_tune(const ma_muon_bucket* buckets, int32_t n_buckets,
     if (st != MA_OK) return st;
     phase = 0;
     std::lock_guard<std::mutex> lock(g_tune_mu);
-    return for_each_phase(buckets, n_buckets, [&](const Phase& ph) -> ma_status {
+    return for_each_phase(buckets, n_buckets, hp ? hp->ns_mode : 0, [&](const Phase& ph) -> ma_status {
       const Tiles t{tiles[3 * phase], tiles[3 * phase + 1], tiles[3 * phase + 2]};
       if (t == Tiles{0, 0, 0}) g_tune.erase(phase_key(ph)); else g_tune[phase_key(ph)] = t;
       ++phase;
@@ -601,7 +699,7 @@ ma_status ma_muon_tune(const ma_muon_bucket* buckets, int32_t n_buckets,
       return fail(MA_ERR_WORKSPACE, "workspace has %zu bytes, %zu needed", workspace_bytes, need);
   }
   int phases = 0;
-  for_each_phase(buckets, n_buckets, [&](const Phase&) { ++phases; return MA_OK; });
+  for_each_phase(buckets, n_buckets, hp ? hp->ns_mode : 0, [&](const Phase&) { ++phases; return MA_OK; });
   if (phases == 0) return MA_OK;
   hipStream_t s = static_cast<hipStream_t>(stream);
   char* ws = static_cast<char*>(workspace);
@@ -614,7 +712,7 @@ ma_status ma_muon_tune(const ma_muon_bucket* buckets, int32_t n_buckets,
     return hip_fail(he, "event create");
   }
   int phase = 0;
-  const ma_status st = for_each_phase(buckets, n_buckets, [&](const Phase& ph) -> ma_status {
+  const ma_status st = for_each_phase(buckets, n_buckets, hp ? hp->ns_mode : 0, [&](const Phase& ph) -> ma_status {
     NsGroup g[kMaxGemmGroups];
     phase_groups(ph, ws, 0, g);
     auto launch = [&](int q, int tile) {

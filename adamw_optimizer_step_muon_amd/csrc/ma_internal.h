@@ -43,11 +43,18 @@ struct BucketPlan {
   // which their combine reads
   bool keeps_xt;
   size_t off_xt[2];
+  // Gram-space iteration (n >= 2 m, when asked for): R ping-pong in off_r / off_r2, the
+  // accumulated polynomial Q in off_q[2], the product R P in off_t (m_pad x m_pad bf16)
+  bool gram_space;
+  size_t off_r2, off_q[2], off_t;
 };
 
 // Plan of one bucket on the given GEMM tile (128 or 256), or on pick_tile's choice
 // (tile 0); MA_NS_TILE, when set to 128 or 256, overrides either.
-BucketPlan plan_bucket(int64_t K, int64_t A, int64_t B, int tile = 0);
+BucketPlan plan_bucket(int64_t K, int64_t A, int64_t B, int tile = 0, bool gram_space = false);
+// Whether a bucket runs the Gram-space iteration under ns_mode: 1 asks for it where the
+// long side is at least twice the Gram side.
+bool wants_gram_space(int32_t ns_mode, int64_t A, int64_t B);
 // Whether GEMM launches holding `tri` lower-triangle and `comb` combine tiles of
 // 256 x 256 fill the chip well enough for 256-tiles.
 bool fills_256(int64_t tri, int64_t comb);
@@ -108,6 +115,16 @@ hipError_t launch_poly(const NsGroup* g, int n, float a, float b, float c, int t
 // (X^T when A > B: n_pad x m_pad, into XTn, or into Xn for one-orientation buckets)
 hipError_t launch_combine(const NsGroup* g, int n, const float* const* scale, bool last,
                           int tile, hipStream_t s);
+// One symmetric product per bucket: C = A B^T (= A B for symmetric B) on lower-triangle
+// tiles, mirrored, all m_pad x m_pad; exact only when A B is symmetric (A and B
+// polynomials in one matrix, as in the Gram-space iteration).  Tile as launch_poly's.
+struct SymProd {
+  const BucketPlan* plan;
+  const unsigned short* A;
+  const unsigned short* B;
+  unsigned short* C;
+};
+hipError_t launch_sym(const SymProd* p, int n, int tile_choice, hipStream_t s);
 // param <- param - lr*wd*mask*param - lr*scale*O with O = oscale[k] * (bf16 O) (oscale
 // may be null: 1), row stride ldo
 hipError_t launch_muon_apply(const BucketPlan& p, float* param, const unsigned short* O,

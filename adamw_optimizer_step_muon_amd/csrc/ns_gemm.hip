@@ -71,6 +71,7 @@ struct GemmArgs {
   int band;             // tile rows per L2 band (tile order; 0: plain row-major triangle)
   int xcd_remap;        // 1: renumber blocks XCD by XCD
   int spread;           // 1: spread the next stage's DMAs over the first half-stage
+  int symmetrize;       // gram with A != B: copy each diagonal tile's lower triangle up
 };
 
 // Up to kMaxGroups buckets (same tile shape) share one launch: block b belongs to the
@@ -581,6 +582,21 @@ __global__ __launch_bounds__(C::kThreads) void ns_gemm_kernel(GemmTable table) {
           }
       }
     __syncthreads();
+    if constexpr (kEpi == kGram && C::BM == C::BN) {
+      if (args.symmetrize && ti == tj) {
+        // A B^T with A != B (a product of two commuting symmetric matrices) is symmetric
+        // only up to rounding; the off-diagonal tiles are mirrored whole, and a diagonal
+        // tile takes its upper triangle from its lower one, so the stored matrix is
+        // exactly symmetric (reads below the diagonal, writes above it: no overlap)
+        for (int idx = tid; idx < C::BM * C::BN; idx += C::kThreads) {
+          const int r = idx / C::BN, c = idx - r * C::BN;
+          if (c > r)
+            Cs[r * C::BN + ((((c >> 3) ^ (r % kCChunks)) << 3) | (c & 7))] =
+                Cs[c * C::BN + ((((r >> 3) ^ (c % kCChunks)) << 3) | (r & 7))];
+        }
+        __syncthreads();
+      }
+    }
     unsigned short* Cp = args.C + batch * args.strideC;
     constexpr int kAll = C::BM * kCChunks;
     static_assert(kAll % C::kThreads == 0, "epilogue copy");
@@ -822,6 +838,33 @@ hipError_t launch_poly(const NsGroup* g, int n, float a_coef, float b, float c, 
     set_tiles(kPoly, a, p, tile, tile);
   }
   return launch_table(kPoly, t, tile == 256 ? kTileBig : kTileSmall, s);
+}
+
+hipError_t launch_sym(const SymProd* pr, int n, int tile_choice, hipStream_t s) {
+  // contracts over the Gram side like the polynomial: same tile rule
+  int tile = chosen_tile(*pr[0].plan, tile_choice);
+  if (tile_choice == 0 && tile == 256 && !forced_tile()) {
+    int64_t tri = 0;
+    for (int i = 0; i < n; ++i) tri += tri_tiles_256(pr[i].plan->K, pr[i].plan->m_pad);
+    if (tri < 512) tile = SmallCfg::BM;
+  }
+  GemmTable t{};
+  t.ngroups = n;
+  for (int i = 0; i < n; ++i) {
+    const BucketPlan& p = *pr[i].plan;
+    GemmArgs& a = t.g[i];
+    a.A = pr[i].A; a.B = pr[i].B;
+    a.lda = a.ldb = p.m_pad;
+    a.strideA = a.strideB = p.m_pad * p.m_pad;
+    a.kdim = static_cast<int>(p.m_pad);
+    a.C = pr[i].C; a.C2 = pr[i].C;
+    a.ldc = a.ldc2 = p.m_pad;
+    a.strideC = a.strideC2 = p.m_pad * p.m_pad;
+    a.symmetrize = 1;
+    a.tiles_k = static_cast<int>(p.K);
+    set_tiles(kGram, a, p, tile, tile);
+  }
+  return launch_table(kGram, t, tile == 256 ? kTileBig : kTileSmall, s);
 }
 
 hipError_t launch_combine(const NsGroup* g, int n, const float* const* scale, bool last,

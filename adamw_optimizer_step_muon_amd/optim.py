@@ -21,7 +21,7 @@ from typing import Dict, List
 from . import _lib
 
 MUON_DEFAULTS = dict(lr=0.02, momentum=0.95, weight_decay=0.0, nesterov=True, ns_steps=5,
-                     ns_coeffs=None, ns_eps=1e-7, cautious_wd=False, scale_mode=0)
+                     ns_coeffs=None, ns_eps=1e-7, cautious_wd=False, scale_mode=0, ns_mode=0)
 ADAMW_DEFAULTS = dict(lr=1e-3, betas=(0.9, 0.999), eps=1e-8, weight_decay=0.0,
                       decoupled=True, cautious_wd=False)
 
@@ -68,10 +68,11 @@ class MuonAdamW:
                 b += sum(t.numel() * t.element_size() for t in self.state[id(p)].values())
         return b / n if n else 0.0
 
-    def _muon_workspace(self, stacks, device):
+    def _muon_workspace(self, stacks, device, ns_mode):
         import torch
 
-        need = _lib.muon_workspace_bytes([tuple(_lib._as_stack(p).shape) for p, _, _ in stacks])
+        need = _lib.muon_workspace_bytes([tuple(_lib._as_stack(p).shape) for p, _, _ in stacks],
+                                         ns_mode)
         if need and (self._workspace is None or self._workspace.numel() < need):
             self._workspace = torch.empty(need, dtype=torch.uint8, device=device)
         return self._workspace
@@ -92,12 +93,12 @@ class MuonAdamW:
                                     decoupled=g["decoupled"], cautious_wd=g["cautious_wd"])
             else:
                 stacks = [(p.data, p.grad, self.state[id(p)]["momentum_buffer"]) for p in live]
-                ws = self._muon_workspace(stacks, live[0].device)
+                ws = self._muon_workspace(stacks, live[0].device, g["ns_mode"])
                 _lib.muon_step(stacks, lr=g["lr"], momentum=g["momentum"],
                                weight_decay=g["weight_decay"], nesterov=g["nesterov"],
                                ns_steps=g["ns_steps"], ns_coeffs=g["ns_coeffs"],
                                ns_eps=g["ns_eps"], cautious_wd=g["cautious_wd"],
-                               scale_mode=g["scale_mode"], workspace=ws)
+                               scale_mode=g["scale_mode"], ns_mode=g["ns_mode"], workspace=ws)
 
     def zero_grad(self, set_to_none: bool = True) -> None:
         for g in self.param_groups:

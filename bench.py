@@ -29,14 +29,28 @@ HBM_PEAK_GBS = 8000.0            # MI355X HBM3E
 ADAMW_BYTES_PER_ELEM = 28        # read p, g, m, v; write p, m, v (fp32)
 
 
-def ns_flops(wl, steps=None, symmetric=True):
-    """Algorithmic Newton-Schulz FLOP of one optimizer step: per matrix and iteration
-    3 m^2 n + m^3 with the symmetric Gram and R R^T on one triangle (dense: 4 m^2 n + 2 m^3)."""
+def gram_space(b, ns_mode):
+    m, n = min(b.A, b.B), max(b.A, b.B)
+    return ns_mode == 1 and n >= 2 * m
+
+
+def ns_flops(wl, steps=None, symmetric=True, ns_mode=0):
+    """Algorithmic Newton-Schulz FLOP of one optimizer step.  Printed iteration, per matrix
+    and iteration: 3 m^2 n + m^3 with the symmetric Gram and R R^T on one triangle (dense:
+    4 m^2 n + 2 m^3).  Gram-space route (ns_mode 1, n >= 2 m), per matrix for N steps:
+    the Gram m^2 n, N polynomials, N - 1 products P Q, 2 (N - 1) products for R <- P R P
+    (m^3 each on one triangle), and the final Q X0, 2 m^2 n: 3 m^2 n + (4 N - 3) m^3
+    (dense: 4 m^2 n + (8 N - 6) m^3)."""
+    N = wl.muon_hp.ns_steps if steps is None else steps
     total = 0
     for b in wl.muon:
         m, n = min(b.A, b.B), max(b.A, b.B)
-        per = (3 * m * m * n + m ** 3) if symmetric else (4 * m * m * n + 2 * m ** 3)
-        total += b.K * per * (wl.muon_hp.ns_steps if steps is None else steps)
+        if gram_space(b, ns_mode) and N > 0:
+            per = (3 * m * m * n + (4 * N - 3) * m ** 3) if symmetric else (
+                4 * m * m * n + (8 * N - 6) * m ** 3)
+        else:
+            per = N * ((3 * m * m * n + m ** 3) if symmetric else (4 * m * m * n + 2 * m ** 3))
+        total += b.K * per
     return total
 
 
@@ -47,6 +61,9 @@ def parse():
     ap.add_argument("--warmup", type=int, default=2)
     ap.add_argument("--workload", type=int, default=1)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--ns-mode", type=int, default=0, choices=(0, 1),
+                    help="1: Gram-space Newton-Schulz for buckets with n >= 2 m (opt-in; its "
+                         "bf16 error is input-dependent)")
     ap.add_argument("--no-tune", action="store_true",
                     help="keep the default GEMM tile rules instead of timing the tiles of each "
                          "Newton-Schulz product once before the warm-up (ma_muon_tune)")
@@ -194,14 +211,16 @@ def main():
     gen.torch_adamw_flat(torch, wl, 0, ap_)
     gen.torch_adamw_flat(torch, wl, 1, ag)
     am, av = torch.zeros_like(ap_), torch.zeros_like(ap_)
-    ws = torch.empty(max(ma.muon_workspace_bytes([tuple(b[0].shape) for b in buckets]), 1),
+    ws = torch.empty(max(ma.muon_workspace_bytes([tuple(b[0].shape) for b in buckets],
+                                                 args.ns_mode), 1),
                      dtype=torch.uint8, device=dev)
     stream = torch.cuda.current_stream(dev)
     state = {"t": 0}
     shapes = [(b.K, b.A, b.B) for b in wl.muon]
     # per-shape GEMM tiles, timed once on the workspace (untimed set-up, like the warm-up)
-    ns_tiles = (ma.muon_phases(shapes)[0] * [[0, 0, 0]] if args.no_tune
-                else ma.muon_tune(shapes, reps=3, workspace=ws, stream=stream))
+    ns_tiles = (ma.muon_phases(shapes, args.ns_mode)[0] * [[0, 0, 0]] if args.no_tune
+                else ma.muon_tune(shapes, reps=3, workspace=ws, stream=stream,
+                                  ns_mode=args.ns_mode))
 
     def adamw():
         ma.adamw_step(ap_, ag, am, av, step=state["t"], lr=ah.lr, beta1=ah.beta1, beta2=ah.beta2,
@@ -211,8 +230,8 @@ def main():
     def muon(ns_steps):
         ma.muon_step(buckets, lr=mh.lr, momentum=mh.momentum, weight_decay=mh.weight_decay,
                      nesterov=mh.nesterov, ns_steps=ns_steps, ns_eps=mh.ns_eps,
-                     cautious_wd=mh.cautious_wd, scale_mode=mh.scale_mode, workspace=ws,
-                     stream=stream)
+                     cautious_wd=mh.cautious_wd, scale_mode=mh.scale_mode, ns_mode=args.ns_mode,
+                     workspace=ws, stream=stream)
 
     def step():
         state["t"] += 1
@@ -241,10 +260,15 @@ def main():
     muon_ms = timed(lambda: muon(mh.ns_steps), reps)
     muon0_ms = timed(lambda: muon(0), reps)
     ns_ms = max(muon_ms - muon0_ms, 1e-9)          # exactly the Newton-Schulz GEMM launches
-    # same-tile buckets share launches: 3 x ns_steps per phase of the bucket list
-    phases, _ = ma.muon_phases([(b.K, b.A, b.B) for b in wl.muon])
-    launches = 3 * mh.ns_steps * phases
-    flops = ns_flops(wl)
+    # same-tile buckets share launches: 3 x ns_steps per phase of the printed iteration,
+    # 4 ns_steps - 1 per Gram-space phase (Gram, polynomials, products, final product)
+    phases, phase_of = ma.muon_phases(shapes, args.ns_mode)
+    N = mh.ns_steps
+    launches = 0
+    for ph in range(phases):
+        b = wl.muon[phase_of.index(ph)]
+        launches += (4 * N - 1) if (gram_space(b, args.ns_mode) and N > 0) else 3 * N
+    flops = ns_flops(wl, ns_mode=args.ns_mode)
     ns_tflops = flops / (ns_ms * 1e-3) / 1e12
     state["t"] = 1
     adamw_ms = timed(adamw, reps)
@@ -265,7 +289,7 @@ def main():
         "dtype_detail": "bf16 MFMA operands, fp32 accumulation; fp32 elementwise state",
         "data": "synthetic (seeded device-generated gradients and N(0,1) parameters)",
         "config": {"workload": wl.name, "muon_buckets": [[b.K, b.A, b.B] for b in wl.muon],
-                   "adamw_elements": n, "ns_steps": mh.ns_steps,
+                   "adamw_elements": n, "ns_steps": mh.ns_steps, "ns_mode": args.ns_mode,
                    "cautious_wd": mh.cautious_wd},
         "ns_tiles": ns_tiles,
         "ns_tflops": round(ns_tflops, 2),

@@ -134,6 +134,8 @@ FAKE = 0x10000000  # never dereferenced: every call below fails validation first
     ("neg_steps", _lib.MA_ERR_INVALID_ARG),
     ("big_steps", _lib.MA_ERR_INVALID_ARG),
     ("bad_scale", _lib.MA_ERR_INVALID_ARG),
+    ("bad_ns_mode", _lib.MA_ERR_INVALID_ARG),
+    ("small_gram_space_workspace", _lib.MA_ERR_WORKSPACE),
     ("nan_lr", _lib.MA_ERR_INVALID_ARG),
     ("neg_K", _lib.MA_ERR_INVALID_ARG),
     ("zero_A", _lib.MA_ERR_INVALID_ARG),
@@ -160,6 +162,13 @@ def test_muon_step_rejects_before_launch(lib, case, status):
         hp.ns_steps = _lib.MA_MAX_NS_STEPS + 1
     elif case == "bad_scale":
         hp.scale_mode = 2
+    elif case == "bad_ns_mode":
+        hp.ns_mode = 2
+    elif case == "small_gram_space_workspace":
+        # 64 x 96 is not 2:1, so 64 x 160 is used: its Gram-space plan needs more
+        bucket.B = 160
+        hp.ns_mode = 1
+        ws_bytes = lib.ma_muon_workspace_bytes(ctypes.byref(bucket), 1, None)
     elif case == "nan_lr":
         hp.lr = float("nan")
     elif case == "neg_K":
@@ -297,3 +306,21 @@ def test_tune_rejects_bad_arguments_before_launch(lib):
     with pytest.raises(ValueError):
         ma.muon_tune(W1, reps=0, tiles=[[256, 256, 256], [256, 256, 256]])
     assert _tune_raw(lib, [], 3, None) == _lib.MA_OK                   # no phase: no-op
+
+
+def test_gram_space_routing_and_workspace(lib):
+    """ns_mode 1 routes buckets whose long side is at least twice the Gram side through
+    the Gram-space iteration, in phases of their own, with four more m x m buffers."""
+    mlp, sq = (12, 768, 3072), (48, 768, 768)
+    assert ma.muon_phases([sq, mlp, (12, 3072, 768)]) == (1, [0, 0, 0])
+    assert ma.muon_phases([sq, mlp, (12, 3072, 768)], ns_mode=1) == (2, [0, 1, 1])
+    m_pad = 768 if not os.environ.get("MA_NS_TILE") else None
+    extra = ma.muon_workspace_bytes([mlp], ns_mode=1) - ma.muon_workspace_bytes([mlp])
+    if m_pad:
+        assert extra == 4 * 12 * m_pad * m_pad * 2
+    assert ma.muon_workspace_bytes([sq], ns_mode=1) == ma.muon_workspace_bytes([sq])
+    assert ma.muon_workspace_bytes([(3, 100, 199)], ns_mode=1) == ma.muon_workspace_bytes(
+        [(3, 100, 199)])
+    # ma_newton_schulz's workspace serves either mode
+    assert ma.newton_schulz_workspace_bytes(12, 768, 3072) == ma.muon_workspace_bytes(
+        [mlp], ns_mode=1)
