@@ -88,9 +88,10 @@ typedef struct {
                              in real arithmetic; in bf16 its error depends on the input
                              (R holds squared singular values and the recurrence amplifies
                              rounding): within 2e-2 of the printed iteration on Gaussian
-                             and low-rank gradients and on row-scaled gradients of wide
-                             matrices, 2.3e-2 to 4.4e-2 on row-scaled tall ones and 2.5e-2
-                             to 3.5e-2 at condition numbers near 1e4.  Opt-in. */
+                             gradients, on low-rank ones up to Gram sides near 1024 and on
+                             row-scaled gradients of wide matrices; 2e-2 to 5e-2 on
+                             row-scaled tall matrices, low-rank ones with Gram sides of
+                             2560 and condition numbers near 1e4.  Opt-in. */
 } ma_muon_hparams;
 
 #define MA_MAX_NS_STEPS 64

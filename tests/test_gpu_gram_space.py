@@ -95,3 +95,17 @@ def test_gram_space_full_size_mlp_buckets():
     hist, routes = _muon_run(P0, grads, lr=LR, momentum=MU, weight_decay=WD, ns_mode=1)
     assert [r.ns_mode_run for r in routes] == [1, 1]
     _check_muon(P0, grads, hist, routes, only=[[0, 11], [0, 11]])
+
+
+def test_gram_space_bucket_that_keeps_xt():
+    """Gram sides above 2048 on 256-tiles keep X^T, so the final product reads X_0^T:
+    both orientations (6 x 2560 x 5120 and its transpose, one phase), first matrix of each
+    against the oracle for one step on Gaussian gradients (at this Gram side the route's
+    error on low-rank gradients is 3.8e-2, bit for bit what a CPU bf16 emulation of the
+    same scheme gives: outside the tolerance, so not a parity case)."""
+    shapes = [(6, 2560, 5120), (6, 5120, 2560)]
+    assert ma.muon_phases(shapes, ns_mode=1) == (1, [0, 0])
+    P0, grads = _buckets(shapes, 51, 1, recipe="gauss")
+    hist, routes = _muon_run(P0, grads, lr=LR, momentum=MU, weight_decay=WD, ns_mode=1)
+    assert [(r.ns_mode_run, r.m_pad) for r in routes] == [(1, 2560), (1, 2560)]
+    _check_muon(P0, grads, hist, routes, only=[[0], [0]])
