@@ -22,12 +22,14 @@ def _state(seed):
     return ps, gs, ms
 
 
-def test_muon_step_graph_replays_match_eager():
+@pytest.mark.parametrize("ns_mode", [0, 1])
+def test_muon_step_graph_replays_match_eager(ns_mode):
+    """ns_mode 1 routes the 390 x 130 bucket through the Gram-space launches."""
     ps, gs, ms = _state(5)
     ps_e, ms_e = [p.clone() for p in ps], [m.clone() for m in ms]
-    ws = torch.empty(ma.muon_workspace_bytes(SHAPES), dtype=torch.uint8, device=DEV)
+    ws = torch.empty(ma.muon_workspace_bytes(SHAPES, ns_mode), dtype=torch.uint8, device=DEV)
     ws_e = torch.empty_like(ws)
-    hp = dict(lr=0.02, momentum=0.95, weight_decay=0.1, cautious_wd=True)
+    hp = dict(lr=0.02, momentum=0.95, weight_decay=0.1, cautious_wd=True, ns_mode=ns_mode)
     torch.cuda.synchronize()
     graph = torch.cuda.CUDAGraph()
     with torch.cuda.graph(graph):
