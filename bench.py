@@ -54,6 +54,26 @@ def ns_flops(wl, steps=None, symmetric=True, ns_mode=0):
     return total
 
 
+def ns_bytes(wl, ns_mode=0):
+    """Algorithmic HBM bytes of the Newton-Schulz launches of one step (bf16 operands and
+    results, each read or written once, padding ignored).  Printed iteration, per matrix
+    and iteration: the Gram reads X and writes R (m n + m^2), the polynomial reads R and
+    writes P (2 m^2), the combine reads P and X and writes X' (m^2 + 2 m n): 2 (3 m n +
+    4 m^2) bytes.  Gram-space route: the Gram (m n + m^2), per step a polynomial (2 m^2),
+    then 3 m^2 per symmetric product (two operands, one result) for the 3 (N - 1)
+    products, and the final product (m^2 + 2 m n)."""
+    N = wl.muon_hp.ns_steps
+    total = 0
+    for b in wl.muon:
+        m, n = min(b.A, b.B), max(b.A, b.B)
+        if gram_space(b, ns_mode) and N > 0:
+            per = (m * n + m * m) + N * 2 * m * m + 3 * (N - 1) * 3 * m * m + (m * m + 2 * m * n)
+        else:
+            per = N * (3 * m * n + 4 * m * m)
+        total += 2 * b.K * per
+    return total
+
+
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -269,6 +289,9 @@ def main():
         b = wl.muon[phase_of.index(ph)]
         launches += (4 * N - 1) if (gram_space(b, args.ns_mode) and N > 0) else 3 * N
     flops = ns_flops(wl, ns_mode=args.ns_mode)
+    nbytes = ns_bytes(wl, args.ns_mode)
+    intensity = flops / nbytes
+    attainable = min(MFMA_BF16_PEAK_TFLOPS, intensity * HBM_PEAK_GBS / 1e3)
     ns_tflops = flops / (ns_ms * 1e-3) / 1e12
     state["t"] = 1
     adamw_ms = timed(adamw, reps)
@@ -313,6 +336,12 @@ def main():
                                                  "ns_gemm.hip", key="mfma_busy"),
             "flops_per_launch": flops / launches,
             "avg_launch_ms": ns_ms / launches,
+            # the same launches against both ceilings: algorithmic FLOP per algorithmic HBM
+            # byte, and the roofline's attainable rate min(MFMA peak, intensity x HBM peak)
+            "intensity_flop_per_byte": round(intensity, 1),
+            "achieved_hbm_gbs": round(nbytes / (ns_ms * 1e-3) / 1e9, 1),
+            "attainable_tflops": round(attainable, 1),
+            "frac_of_attainable": round(ns_tflops / attainable, 4),
         },
         "adamw_roofline": {
             "kernel": "adamw_vec_kernel",
