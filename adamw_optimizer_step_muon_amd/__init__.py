@@ -4,12 +4,12 @@ The compute runs in libmuonadamw.so (hand-written HIP kernels behind the C ABI o
 include/muon_adamw.h); this package is its thin Python binding plus the MuonAdamW
 parameter-group wrapper.  PyTorch supplies device memory and streams only.
 """
-from ._lib import (LIB_PATH, MuonAdamWError, Route, abi_version, adamw_step, load,
+from ._lib import (LIB_PATH, MuonAdamWError, Route, abi_version, adamw_step, adamw_step_multi, load,
                    muon_phases, muon_route_of, muon_step, muon_tune, muon_tune_reset,
                    muon_workspace_bytes, newton_schulz, newton_schulz_workspace_bytes)
 from .optim import MuonAdamW
 
-__all__ = ["LIB_PATH", "MuonAdamWError", "Route", "abi_version", "adamw_step", "load",
+__all__ = ["LIB_PATH", "MuonAdamWError", "Route", "abi_version", "adamw_step", "adamw_step_multi", "load",
            "muon_phases", "muon_route_of", "muon_step", "muon_tune", "muon_tune_reset",
            "muon_workspace_bytes", "newton_schulz",
            "newton_schulz_workspace_bytes", "MuonAdamW"]

@@ -26,6 +26,7 @@ EXPORTED = (
     "ma_abi_version", "ma_status_string", "ma_last_error", "ma_muon_route_of",
     "ma_muon_workspace_bytes", "ma_muon_phases", "ma_muon_step", "ma_adamw_step",
     "ma_newton_schulz_workspace_bytes", "ma_newton_schulz", "ma_muon_tune", "ma_muon_tune_reset",
+    "ma_adamw_step_multi",
 )
 
 
@@ -53,6 +54,11 @@ class _MuonRoute(ctypes.Structure):
     _fields_ = [("transposed", ctypes.c_int32), ("m", ctypes.c_int32), ("n", ctypes.c_int32),
                 ("ns_steps_run", ctypes.c_int32), ("m_pad", ctypes.c_int32),
                 ("n_pad", ctypes.c_int32), ("ns_mode_run", ctypes.c_int32)]
+
+
+class _AdamWSegment(ctypes.Structure):
+    _fields_ = [("param", ctypes.c_void_p), ("grad", ctypes.c_void_p), ("exp_avg", ctypes.c_void_p),
+                ("exp_avg_sq", ctypes.c_void_p), ("n", ctypes.c_int64)]
 
 
 class _AdamWHParams(ctypes.Structure):
@@ -120,6 +126,9 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.ma_muon_tune.argtypes = [ctypes.POINTER(_MuonBucket), ctypes.c_int32,
                                  ctypes.POINTER(_MuonHParams), ctypes.c_void_p, ctypes.c_size_t,
                                  ctypes.c_void_p, ctypes.c_int32, ctypes.POINTER(ctypes.c_int32)]
+    lib.ma_adamw_step_multi.restype = ctypes.c_int
+    lib.ma_adamw_step_multi.argtypes = [ctypes.POINTER(_AdamWSegment), ctypes.c_int32,
+                                        ctypes.POINTER(_AdamWHParams), ctypes.c_void_p]
     lib.ma_muon_tune_reset.restype = None
     lib.ma_muon_tune_reset.argtypes = []
     _lib = lib
@@ -342,6 +351,31 @@ def adamw_step(param, grad, exp_avg, exp_avg_sq, *, step: int, lr: float, beta1:
                        cautious_wd=int(bool(cautious_wd)))
     _check(load().ma_adamw_step(_ptr(param), _ptr(grad), _ptr(exp_avg), _ptr(exp_avg_sq), n,
                                 ctypes.byref(hp), _stream_handle(stream, param.device)))
+
+
+def adamw_step_multi(segments, *, step: int, lr: float, beta1: float = 0.9, beta2: float = 0.999,
+                     eps: float = 1e-8, weight_decay: float = 0.0, decoupled: bool = True,
+                     cautious_wd: bool = False, stream=None) -> None:
+    """One AdamW step (ma_adamw_step_multi) over (param, grad, exp_avg, exp_avg_sq) tuples of
+    contiguous fp32 GPU tensors, each tuple of one size: one launch per 48 tensors."""
+    segs = list(segments)
+    arr = (_AdamWSegment * max(len(segs), 1))()
+    device = None
+    for i, (p, g, m, v) in enumerate(segs):
+        for name, t in (("param", p), ("grad", g), ("exp_avg", m), ("exp_avg_sq", v)):
+            _require_f32_cuda(f"segment {i} {name}", t)
+        n = p.numel()
+        if not (g.numel() == m.numel() == v.numel() == n):
+            raise ValueError(f"segment {i}: param, grad, exp_avg and exp_avg_sq differ in size")
+        arr[i] = _AdamWSegment(_ptr(p), _ptr(g), _ptr(m), _ptr(v), n)
+        device = p.device
+    if not segs:
+        return
+    hp = _AdamWHParams(lr=lr, beta1=beta1, beta2=beta2, eps=eps, weight_decay=weight_decay,
+                       step=int(step), decoupled=int(bool(decoupled)),
+                       cautious_wd=int(bool(cautious_wd)))
+    _check(load().ma_adamw_step_multi(arr, len(segs), ctypes.byref(hp),
+                                      _stream_handle(stream, device)))
 
 
 def newton_schulz_workspace_bytes(K: int, A: int, B: int) -> int:

@@ -22,12 +22,18 @@ constexpr int kThreads = 256;
 // Decay variants, fixed per launch so the vector kernel's body has no branches.
 enum DecayMode { kDecoupled = 0, kDecoupledCautious = 1, kCoupled = 2 };
 
+// The multiply-adds are explicit (fmaf) and nothing else is contracted: every kernel
+// (flat vector, flat scalar, multi-tensor) rounds the same operations, so an element's
+// result does not depend on which kernel updated it (left to the compiler, p keep -
+// lr upd was fused differently in different kernels).  g + wd p (coupled decay) keeps a
+// single rounding, which matters where the two terms cancel.
 template <int kMode>
 __device__ __forceinline__ void adamw_elem_t(float& p, float g, float& m, float& v,
                                              const AdamWConst& c) {
-  if (kMode == kCoupled) g = g + c.wd * p;
-  m = c.beta1 * m + c.one_m_beta1 * g;
-  v = c.beta2 * v + c.one_m_beta2 * (g * g);
+#pragma clang fp contract(off)
+  if (kMode == kCoupled) g = __builtin_fmaf(c.wd, p, g);
+  m = __builtin_fmaf(c.beta1, m, c.one_m_beta1 * g);
+  v = __builtin_fmaf(c.beta2, v, c.one_m_beta2 * (g * g));
   const float mhat = m * c.inv_bc1;
   const float vhat = v * c.inv_bc2;
   const float upd = mhat / (__builtin_sqrtf(vhat) + c.eps);
@@ -35,7 +41,7 @@ __device__ __forceinline__ void adamw_elem_t(float& p, float g, float& m, float&
     const float keep = 1.0f - c.lr * c.wd;
     p = p * ((kMode == kDecoupledCautious && !(upd * p > 0.0f)) ? 1.0f : keep);
   }
-  p = p - c.lr * upd;
+  p = __builtin_fmaf(-c.lr, upd, p);
 }
 
 __device__ __forceinline__ void adamw_elem(float& p, float g, float& m, float& v,
@@ -152,7 +158,107 @@ int adamw_variant() {
   return v;
 }
 
+// Many tensors in one launch: each block belongs to one segment of the table (read in
+// place from the kernel-argument segment) and covers kMultiChunk of its elements, as
+// float4 groups where the segment's four pointers are 16-byte aligned (the last block
+// also takes the n % 4 tail) and element by element otherwise.  The same element
+// function as the flat kernels, so every element's result is bitwise the same.
+constexpr int kMultiGroups = 4;                               // float4 groups per thread
+constexpr int kMultiChunk = kThreads * kMultiGroups * 4;      // elements per block
+
+template <int kMode>
+__global__ __launch_bounds__(kThreads) void adamw_multi_kernel(AdamWSegTable table) {
+  const AdamWSegTable* kt = (const AdamWSegTable*)__builtin_amdgcn_kernarg_segment_ptr();
+  (void)table;
+  const int64_t b = blockIdx.x;
+  int s = 0;
+  for (int i = 1; i < kt->nseg; ++i)
+    if (b >= kt->block_start[i]) s = i;
+  const AdamWConst& c = kt->c;
+  const int64_t n = kt->n[s];
+  const int64_t lb = b - kt->block_start[s];
+  float* p = kt->p[s];
+  const float* g = kt->g[s];
+  float* m = kt->m[s];
+  float* v = kt->v[s];
+  const int tid = threadIdx.x;
+  if (kt->vec[s]) {
+    const int64_t n4 = n / 4;
+    f32x4* p4 = reinterpret_cast<f32x4*>(p);
+    const f32x4* g4 = reinterpret_cast<const f32x4*>(g);
+    f32x4* m4 = reinterpret_cast<f32x4*>(m);
+    f32x4* v4 = reinterpret_cast<f32x4*>(v);
+    const int64_t base = lb * (kThreads * kMultiGroups) + tid;
+    f32x4 P[kMultiGroups], G[kMultiGroups], M[kMultiGroups], V[kMultiGroups];
+#pragma unroll
+    for (int u = 0; u < kMultiGroups; ++u) {
+      const int64_t i = base + static_cast<int64_t>(u) * kThreads;
+      if (i < n4) {
+        P[u] = ld<true>(&p4[i]);
+        G[u] = ld<true>(&g4[i]);
+        M[u] = ld<true>(&m4[i]);
+        V[u] = ld<true>(&v4[i]);
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < kMultiGroups; ++u) {
+      const int64_t i = base + static_cast<int64_t>(u) * kThreads;
+      if (i < n4) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          float pe = P[u][e], me = M[u][e], ve = V[u][e];
+          adamw_elem_t<kMode>(pe, G[u][e], me, ve, c);
+          P[u][e] = pe;
+          M[u][e] = me;
+          V[u][e] = ve;
+        }
+        st<true>(&p4[i], P[u]);
+        st<true>(&m4[i], M[u]);
+        st<true>(&v4[i], V[u]);
+      }
+    }
+    // the n % 4 tail, in the segment's last block
+    const int64_t tail0 = n4 * 4;
+    if ((lb + 1) * kMultiChunk >= n && tid < n - tail0) {
+      const int64_t i = tail0 + tid;
+      float P1 = p[i], M1 = m[i], V1 = v[i];
+      adamw_elem_t<kMode>(P1, g[i], M1, V1, c);
+      p[i] = P1;
+      m[i] = M1;
+      v[i] = V1;
+    }
+  } else {
+#pragma unroll
+    for (int k = 0; k < kMultiChunk / kThreads; ++k) {
+      const int64_t i = lb * kMultiChunk + static_cast<int64_t>(k) * kThreads + tid;
+      if (i < n) {
+        float P1 = p[i], M1 = m[i], V1 = v[i];
+        adamw_elem_t<kMode>(P1, g[i], M1, V1, c);
+        p[i] = P1;
+        m[i] = M1;
+        v[i] = V1;
+      }
+    }
+  }
+}
+
 }  // namespace
+
+int64_t adamw_multi_blocks(int64_t n) { return (n + kMultiChunk - 1) / kMultiChunk; }
+
+hipError_t launch_adamw_multi(const AdamWSegTable& t, hipStream_t s) {
+  const int64_t blocks = t.block_start[t.nseg];
+  if (blocks <= 0) return hipSuccess;
+  const dim3 grid(static_cast<unsigned>(blocks));
+  switch (decay_mode(t.c)) {
+    case kCoupled: hipLaunchKernelGGL(adamw_multi_kernel<kCoupled>, grid, dim3(kThreads), 0, s, t); break;
+    case kDecoupledCautious:
+      hipLaunchKernelGGL(adamw_multi_kernel<kDecoupledCautious>, grid, dim3(kThreads), 0, s, t);
+      break;
+    default: hipLaunchKernelGGL(adamw_multi_kernel<kDecoupled>, grid, dim3(kThreads), 0, s, t); break;
+  }
+  return hipGetLastError();
+}
 
 hipError_t launch_adamw(float* p, const float* g, float* m, float* v, int64_t n,
                         const AdamWConst& c, hipStream_t s) {

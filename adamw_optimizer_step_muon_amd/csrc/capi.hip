@@ -1,6 +1,7 @@
 // Exported C ABI (include/muon_adamw.h): argument checks, routing, workspace layout
 // and the launch sequence of one optimizer step.  Host code only; the arithmetic is
 // in the kernels of adamw.hip, muon_elementwise.hip and ns_gemm.hip.
+#include <algorithm>
 #include <array>
 #include <cmath>
 #include <cstdarg>
@@ -398,6 +399,33 @@ ma_status prep_bucket(const BucketPlan& p, const float* grad, float* momentum,
   return MA_OK;
 }
 
+// AdamW hyperparameter checks and the per-step constants of the kernels.
+ma_status adamw_const(const ma_adamw_hparams* hp, AdamWConst* c) {
+  if (!hp) return fail(MA_ERR_INVALID_ARG, "hparams is NULL");
+  if (hp->step < 1) return fail(MA_ERR_INVALID_ARG, "step %lld < 1", (long long)hp->step);
+  if (!finite(hp->lr) || !finite(hp->beta1) || !finite(hp->beta2) || !finite(hp->eps) ||
+      !finite(hp->weight_decay))
+    return fail(MA_ERR_INVALID_ARG, "non-finite AdamW hyperparameter");
+  if (!(hp->beta1 >= 0.0f && hp->beta1 < 1.0f && hp->beta2 >= 0.0f && hp->beta2 < 1.0f))
+    return fail(MA_ERR_INVALID_ARG, "betas must lie in [0, 1)");
+  c->lr = hp->lr;
+  c->beta1 = hp->beta1;
+  c->beta2 = hp->beta2;
+  c->one_m_beta1 = static_cast<float>(1.0 - static_cast<double>(hp->beta1));
+  c->one_m_beta2 = static_cast<float>(1.0 - static_cast<double>(hp->beta2));
+  c->eps = hp->eps;
+  c->wd = hp->weight_decay;
+  const double t = static_cast<double>(hp->step);
+  c->inv_bc1 = static_cast<float>(1.0 / (1.0 - std::pow(static_cast<double>(hp->beta1), t)));
+  c->inv_bc2 = static_cast<float>(1.0 / (1.0 - std::pow(static_cast<double>(hp->beta2), t)));
+  c->decoupled = hp->decoupled ? 1 : 0;
+  c->cautious = hp->cautious_wd ? 1 : 0;
+  return MA_OK;
+}
+
+// Grid size limit of one launch (blocks), with the room the block-count arithmetic needs.
+constexpr int64_t kMaxGridBlocks = (int64_t(1) << 31) - 4096;
+
 }  // namespace
 
 int forced_tile() {
@@ -763,14 +791,10 @@ void ma_muon_tune_reset(void) {
 ma_status ma_adamw_step(float* param, const float* grad, float* exp_avg, float* exp_avg_sq,
                         int64_t n, const ma_adamw_hparams* hp, void* stream) {
   g_last_error.clear();
-  if (!hp) return fail(MA_ERR_INVALID_ARG, "hparams is NULL");
+  AdamWConst c;
+  const ma_status st = adamw_const(hp, &c);
+  if (st != MA_OK) return st;
   if (n < 0) return fail(MA_ERR_INVALID_ARG, "n = %lld < 0", (long long)n);
-  if (hp->step < 1) return fail(MA_ERR_INVALID_ARG, "step %lld < 1", (long long)hp->step);
-  if (!finite(hp->lr) || !finite(hp->beta1) || !finite(hp->beta2) || !finite(hp->eps) ||
-      !finite(hp->weight_decay))
-    return fail(MA_ERR_INVALID_ARG, "non-finite AdamW hyperparameter");
-  if (!(hp->beta1 >= 0.0f && hp->beta1 < 1.0f && hp->beta2 >= 0.0f && hp->beta2 < 1.0f))
-    return fail(MA_ERR_INVALID_ARG, "betas must lie in [0, 1)");
   if (n == 0) return MA_OK;
   if (!param || !grad || !exp_avg || !exp_avg_sq)
     return fail(MA_ERR_INVALID_ARG, "NULL param, grad, exp_avg or exp_avg_sq");
@@ -782,23 +806,87 @@ ma_status ma_adamw_step(float* param, const float* grad, float* exp_avg, float* 
   for (int i = 0; i < 4; ++i)
     for (int j = i + 1; j < 4; ++j)
       if (overlap(r[i], r[j])) return fail(MA_ERR_INVALID_ARG, "param/grad/exp_avg/exp_avg_sq overlap");
-  AdamWConst c;
-  c.lr = hp->lr;
-  c.beta1 = hp->beta1;
-  c.beta2 = hp->beta2;
-  c.one_m_beta1 = static_cast<float>(1.0 - static_cast<double>(hp->beta1));
-  c.one_m_beta2 = static_cast<float>(1.0 - static_cast<double>(hp->beta2));
-  c.eps = hp->eps;
-  c.wd = hp->weight_decay;
-  const double t = static_cast<double>(hp->step);
-  c.inv_bc1 = static_cast<float>(1.0 / (1.0 - std::pow(static_cast<double>(hp->beta1), t)));
-  c.inv_bc2 = static_cast<float>(1.0 / (1.0 - std::pow(static_cast<double>(hp->beta2), t)));
-  c.decoupled = hp->decoupled ? 1 : 0;
-  c.cautious = hp->cautious_wd ? 1 : 0;
   const hipError_t e = launch_adamw(param, grad, exp_avg, exp_avg_sq, n, c,
                                     static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail(e, "adamw launch");
   return MA_OK;
+}
+
+ma_status ma_adamw_step_multi(const ma_adamw_segment* segs, int32_t n_segs,
+                              const ma_adamw_hparams* hp, void* stream) {
+  g_last_error.clear();
+  AdamWConst c;
+  ma_status st = adamw_const(hp, &c);
+  if (st != MA_OK) return st;
+  if (n_segs < 0) return fail(MA_ERR_INVALID_ARG, "n_segs %d < 0", n_segs);
+  if (n_segs > 0 && !segs) return fail(MA_ERR_INVALID_ARG, "segs is NULL");
+  // every segment on its own, then no write range may overlap any other range (a sweep
+  // over the ranges sorted by start: a range overlaps an earlier one iff it starts
+  // before the largest end seen so far)
+  struct Span {
+    uintptr_t lo, hi;
+    bool write;
+  };
+  std::vector<Span> spans;
+  spans.reserve(static_cast<size_t>(n_segs) * 4);
+  for (int32_t i = 0; i < n_segs; ++i) {
+    const ma_adamw_segment& g = segs[i];
+    if (g.n < 0) return fail(MA_ERR_INVALID_ARG, "segment %d: n = %lld < 0", i, (long long)g.n);
+    if (g.n == 0) continue;
+    if (!g.param || !g.grad || !g.exp_avg || !g.exp_avg_sq)
+      return fail(MA_ERR_INVALID_ARG, "segment %d: NULL pointer", i);
+    if ((reinterpret_cast<uintptr_t>(g.param) | reinterpret_cast<uintptr_t>(g.grad) |
+         reinterpret_cast<uintptr_t>(g.exp_avg) | reinterpret_cast<uintptr_t>(g.exp_avg_sq)) & 3u)
+      return fail(MA_ERR_INVALID_ARG, "segment %d: pointers must be 4-byte aligned", i);
+    const int64_t b = g.n * 4;
+    spans.push_back({range_of(g.param, b).lo, range_of(g.param, b).hi, true});
+    spans.push_back({range_of(g.grad, b).lo, range_of(g.grad, b).hi, false});
+    spans.push_back({range_of(g.exp_avg, b).lo, range_of(g.exp_avg, b).hi, true});
+    spans.push_back({range_of(g.exp_avg_sq, b).lo, range_of(g.exp_avg_sq, b).hi, true});
+  }
+  std::sort(spans.begin(), spans.end(), [](const Span& a, const Span& b) { return a.lo < b.lo; });
+  uintptr_t end_any = 0, end_write = 0;
+  for (const Span& x : spans) {
+    if (x.lo < (x.write ? end_any : end_write))
+      return fail(MA_ERR_INVALID_ARG, "segments overlap (a written range meets another range)");
+    end_any = std::max(end_any, x.hi);
+    if (x.write) end_write = std::max(end_write, x.hi);
+  }
+  // launches of up to kMaxAdamWSegs segments, in order
+  AdamWSegTable t{};
+  t.c = c;
+  auto flush = [&]() -> ma_status {
+    if (t.nseg == 0) return MA_OK;
+    const hipError_t e = launch_adamw_multi(t, static_cast<hipStream_t>(stream));
+    t.nseg = 0;
+    t.block_start[0] = 0;
+    if (e != hipSuccess) return hip_fail(e, "adamw multi launch");
+    return MA_OK;
+  };
+  for (int32_t i = 0; i < n_segs; ++i) {
+    const ma_adamw_segment& g = segs[i];
+    if (g.n == 0) continue;
+    const int64_t nb = adamw_multi_blocks(g.n);
+    if (t.nseg == kMaxAdamWSegs || t.block_start[t.nseg] + nb > kMaxGridBlocks) {
+      st = flush();
+      if (st != MA_OK) return st;
+    }
+    if (nb > kMaxGridBlocks)
+      return fail(MA_ERR_UNSUPPORTED, "segment %d: %lld elements exceed one launch", i,
+                  (long long)g.n);
+    const int k = t.nseg;
+    t.p[k] = g.param;
+    t.g[k] = g.grad;
+    t.m[k] = g.exp_avg;
+    t.v[k] = g.exp_avg_sq;
+    t.n[k] = g.n;
+    t.vec[k] = ((reinterpret_cast<uintptr_t>(g.param) | reinterpret_cast<uintptr_t>(g.grad) |
+                 reinterpret_cast<uintptr_t>(g.exp_avg) | reinterpret_cast<uintptr_t>(g.exp_avg_sq)) &
+                15u) == 0;
+    t.block_start[k + 1] = t.block_start[k] + nb;
+    t.nseg = k + 1;
+  }
+  return flush();
 }
 
 }  // extern "C"

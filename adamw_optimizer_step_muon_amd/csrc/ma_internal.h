@@ -140,5 +140,22 @@ struct AdamWConst {
 };
 hipError_t launch_adamw(float* p, const float* g, float* m, float* v, int64_t n,
                         const AdamWConst& c, hipStream_t s);
+// Up to kMaxAdamWSegs tensors in one launch (ma_adamw_step_multi): segment i covers
+// blocks [block_start[i], block_start[i + 1]) of the grid, adamw_multi_blocks(n[i]) of them
+// (n[i] >= 1); vec[i] = 1 when its four pointers are 16-byte aligned.
+constexpr int kMaxAdamWSegs = 48;
+struct AdamWSegTable {
+  float* p[kMaxAdamWSegs];
+  const float* g[kMaxAdamWSegs];
+  float* m[kMaxAdamWSegs];
+  float* v[kMaxAdamWSegs];
+  int64_t n[kMaxAdamWSegs];
+  int64_t block_start[kMaxAdamWSegs + 1];
+  int32_t vec[kMaxAdamWSegs];
+  int32_t nseg;
+  AdamWConst c;
+};
+int64_t adamw_multi_blocks(int64_t n);
+hipError_t launch_adamw_multi(const AdamWSegTable& t, hipStream_t s);
 
 }  // namespace ma

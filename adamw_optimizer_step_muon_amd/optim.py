@@ -8,7 +8,7 @@ the distributed optimizer", section "Muon: orthogonalising the update": Muon for
 hidden 2-D matrices, AdamW for embeddings, the output layer and vectors.
 
 Host bookkeeping only: each group is marshalled to the C ABI (ma_muon_step over its
-stacks, ma_adamw_step per tensor).  Muon parameters are 3-D (K, A, B) stacks of
+stacks, ma_adamw_step_multi over its tensors).  Muon parameters are 3-D (K, A, B) stacks of
 same-shape matrices (a 2-D matrix counts as K = 1); stacking a model's matrices into
 such buffers is the caller's layout choice.  State is fp32 and zero-initialised:
 ``momentum_buffer`` (4 bytes per Muon parameter), ``exp_avg`` and ``exp_avg_sq``
@@ -84,13 +84,13 @@ class MuonAdamW:
                 continue
             g["step"] += 1
             if g["kind"] == "adamw":
+                # the group's tensors in one fused pass (one launch per 48 tensors)
                 b1, b2 = g["betas"]
-                for p in live:
-                    st = self.state[id(p)]
-                    _lib.adamw_step(p.data, p.grad, st["exp_avg"], st["exp_avg_sq"],
-                                    step=g["step"], lr=g["lr"], beta1=b1, beta2=b2,
-                                    eps=g["eps"], weight_decay=g["weight_decay"],
-                                    decoupled=g["decoupled"], cautious_wd=g["cautious_wd"])
+                segs = [(p.data, p.grad, self.state[id(p)]["exp_avg"],
+                         self.state[id(p)]["exp_avg_sq"]) for p in live]
+                _lib.adamw_step_multi(segs, step=g["step"], lr=g["lr"], beta1=b1, beta2=b2,
+                                      eps=g["eps"], weight_decay=g["weight_decay"],
+                                      decoupled=g["decoupled"], cautious_wd=g["cautious_wd"])
             else:
                 stacks = [(p.data, p.grad, self.state[id(p)]["momentum_buffer"]) for p in live]
                 ws = self._muon_workspace(stacks, live[0].device, g["ns_mode"])

@@ -180,6 +180,26 @@ ma_status ma_muon_step(const ma_muon_bucket* buckets, int32_t n_buckets,
 ma_status ma_adamw_step(float* param, const float* grad, float* exp_avg, float* exp_avg_sq,
                         int64_t n, const ma_adamw_hparams* hp, void* stream);
 
+/* One AdamW tensor of ma_adamw_step_multi: n fp32 elements at each pointer (device). */
+typedef struct {
+  float* param;
+  const float* grad;
+  float* exp_avg;
+  float* exp_avg_sq;
+  int64_t n;
+} ma_adamw_segment;
+
+/* ma_adamw_step over many tensors at once ([NC]: one fused AdamW over the optimizer's
+ * AdamW parameters): segs is a host array of n_segs segments, each updated exactly as
+ * ma_adamw_step would (bitwise the same results), in one launch per 48 segments instead of
+ * one per tensor.  Segments with n == 0 are skipped.  No written range (param, exp_avg,
+ * exp_avg_sq) may overlap any other range of any segment; gradients may be shared.
+ * Errors: MA_ERR_INVALID_ARG (as ma_adamw_step, per segment, plus n_segs < 0, segs NULL
+ * with n_segs > 0, overlap between segments), MA_ERR_UNSUPPORTED (a segment above 2^31
+ * blocks of 4096 elements), MA_ERR_HIP. */
+ma_status ma_adamw_step_multi(const ma_adamw_segment* segs, int32_t n_segs,
+                              const ma_adamw_hparams* hp, void* stream);
+
 /* Host only: workspace bytes ma_newton_schulz needs for a (K, A, B) stack. */
 size_t ma_newton_schulz_workspace_bytes(int64_t K, int64_t A, int64_t B);
 

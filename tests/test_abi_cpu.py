@@ -324,3 +324,35 @@ def test_gram_space_routing_and_workspace(lib):
     # ma_newton_schulz's workspace serves either mode
     assert ma.newton_schulz_workspace_bytes(12, 768, 3072) == ma.muon_workspace_bytes(
         [mlp], ns_mode=1)
+
+
+@pytest.mark.parametrize("case", ["null_segs", "neg_count", "neg_n", "null_ptr", "misaligned",
+                                  "overlap_across", "overlap_within", "bad_hp"])
+def test_adamw_step_multi_rejects_before_launch(lib, case):
+    n = 1000
+    segs = (_lib._AdamWSegment * 2)()
+    for i in range(2):
+        base = FAKE + i * 16 * n
+        segs[i] = _lib._AdamWSegment(base, base + 4 * n, base + 8 * n, base + 12 * n, n)
+    hp = _lib._AdamWHParams(lr=1e-3, beta1=0.9, beta2=0.95, eps=1e-8, weight_decay=0.1, step=1,
+                            decoupled=1, cautious_wd=0)
+    arr, count = segs, 2
+    if case == "null_segs":
+        arr = None
+    elif case == "neg_count":
+        count = -1
+    elif case == "neg_n":
+        segs[1].n = -5
+    elif case == "null_ptr":
+        segs[1].exp_avg = None
+    elif case == "misaligned":
+        segs[0].grad = FAKE + 4 * n + 2
+    elif case == "overlap_across":
+        segs[1].param = FAKE + 8 * n + 400          # inside segment 0's exp_avg
+    elif case == "overlap_within":
+        segs[0].exp_avg_sq = FAKE + 8 * n + 4        # overlaps its own exp_avg
+    elif case == "bad_hp":
+        hp.beta2 = 1.0
+    got = lib.ma_adamw_step_multi(arr, count, ctypes.byref(hp), None)
+    assert got == _lib.MA_ERR_INVALID_ARG, (case, lib.ma_last_error())
+    assert lib.ma_last_error()

@@ -174,3 +174,34 @@ def test_adamw_full_size_sampled(index):
         torch.cuda.synchronize()
         got.append((p[tidx].cpu().numpy(), m[tidx].cpu().numpy(), v[tidx].cpu().numpy()))
     _check(got, p0, gs, hp, _oracle(p0, gs, hp))
+
+
+@pytest.mark.parametrize("variant", [dict(), dict(decoupled=False), dict(cautious_wd=True)])
+def test_adamw_multi_matches_per_tensor_bitwise(variant):
+    """ma_adamw_step_multi over 130 tensors (three launches of at most 48): ragged sizes,
+    starts misaligned for the vector path, a gradient shared by two tensors, an empty
+    tensor; every element bitwise equal to ma_adamw_step on the same tensor."""
+    rng = np.random.default_rng(11)
+    sizes = [int(x) for x in rng.integers(1, 9000, size=126)] + [0, 4096, 4097, 100_003]
+    store = torch.randn(sum(sizes) + 8, device="cuda")
+    shared = torch.randn(4097, device="cuda") * 1e-3
+    segs, segs_ref = [], []
+    off = 0
+    for i, n in enumerate(sizes):
+        lo = off + (i % 3)                           # odd starts: scalar path
+        p = store[lo:lo + n].clone() if i % 5 else store[lo:lo + n].clone()[0:n]
+        g = shared[:n] if (n <= 4097 and i in (3, 7)) else torch.randn(n, device="cuda") * 1e-3
+        m = torch.randn(n, device="cuda").abs() * 1e-4
+        v = torch.randn(n, device="cuda").abs() * 1e-6
+        if i % 3:                                     # misaligned views of fresh buffers
+            big = torch.empty(n + 1, device="cuda"); big[1:].copy_(p); p = big[1:]
+        segs.append((p, g, m, v))
+        segs_ref.append((p.clone(), g, m.clone(), v.clone()))
+        off += n
+    hp = dict(step=3, lr=3e-3, beta1=0.9, beta2=0.95, eps=1e-8, weight_decay=0.1, **variant)
+    ma.adamw_step_multi(segs, **hp)
+    for p, g, m, v in segs_ref:
+        ma.adamw_step(p, g, m, v, **hp)
+    torch.cuda.synchronize()
+    for (a, _, am, av), (b, _, bm, bv) in zip(segs, segs_ref):
+        assert torch.equal(a, b) and torch.equal(am, bm) and torch.equal(av, bv)
