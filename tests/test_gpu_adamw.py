@@ -205,3 +205,22 @@ def test_adamw_multi_matches_per_tensor_bitwise(variant):
     torch.cuda.synchronize()
     for (a, _, am, av), (b, _, bm, bv) in zip(segs, segs_ref):
         assert torch.equal(a, b) and torch.equal(am, bm) and torch.equal(av, bv)
+
+
+def test_adamw_non_finite_gradient_stays_in_its_element():
+    """No scrubbing: a NaN gradient element makes that element's parameter and moments
+    NaN; every other element is bitwise as in a clean step (vector and tail paths)."""
+    n = 4099
+    rng = np.random.default_rng(12)
+    p0 = rng.standard_normal(n).astype(np.float32)
+    g = (1e-3 * rng.standard_normal(n)).astype(np.float32)
+    g_bad = g.copy()
+    g_bad[[10, 4097]] = np.nan          # one in the float4 body, one in the scalar tail
+    hp = _hp()
+    got = _run(p0, [g_bad], hp)[0]
+    clean = _run(p0, [g], hp)[0]
+    mask = np.zeros(n, bool)
+    mask[[10, 4097]] = True
+    for a, b in zip(got, clean):
+        assert np.isnan(a[mask]).all()
+        assert np.array_equal(a[~mask], b[~mask])

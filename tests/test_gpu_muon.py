@@ -338,3 +338,28 @@ def test_muon_full_size_sampled(index):
             err = rel_fro(prev * keep - got, prev * keep - ref.param)
         assert err <= MUON_RTOL, (bi, k, err)
         assert rel_err_floor(ms[bi][k].cpu().numpy(), ref.momentum) <= MOMENTUM_RTOL
+
+
+@pytest.mark.parametrize("bad", [float("nan"), float("inf")])
+def test_muon_non_finite_gradient_propagates_to_its_matrix_only(bad):
+    """Non-finite gradients are not scrubbed: one NaN or Inf entry in matrix 1's gradient
+    makes its whole update non-finite (its Frobenius norm is, and the orthogonalisation
+    mixes every entry, as in the oracle), its momentum only at that entry, and leaves the
+    bucket's other matrices bitwise as in a clean run."""
+    shape = (3, 96, 200)
+    P0 = [np.random.default_rng(9).standard_normal(shape).astype(np.float32)]
+    g = np.stack([_grad(shape[1:], 60 + k) for k in range(3)])
+    g_bad = g.copy()
+    g_bad[1, 5, 7] = bad
+    hist, _ = _muon_run(P0, [[g_bad]], lr=LR, momentum=MU, weight_decay=WD)
+    clean, _ = _muon_run(P0, [[g]], lr=LR, momentum=MU, weight_decay=WD)
+    p, m = hist[0][0]
+    pc, mc = clean[0][0]
+    assert not np.isfinite(p[1]).any()
+    ref = oracle.muon_step(P0[0][1], g_bad[1], np.zeros(shape[1:]), lr=f32(LR), mu=f32(MU),
+                           weight_decay=f32(WD))
+    assert not np.isfinite(ref.param).any()
+    bad_m = ~np.isfinite(m[1])
+    assert bad_m.sum() == 1 and bad_m[5, 7]
+    for k in (0, 2):
+        assert np.array_equal(p[k], pc[k]) and np.array_equal(m[k], mc[k])
