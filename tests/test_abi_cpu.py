@@ -356,3 +356,15 @@ def test_adamw_step_multi_rejects_before_launch(lib, case):
     got = lib.ma_adamw_step_multi(arr, count, ctypes.byref(hp), None)
     assert got == _lib.MA_ERR_INVALID_ARG, (case, lib.ma_last_error())
     assert lib.ma_last_error()
+
+
+def test_adamw_step_multi_empty_calls_are_no_ops(lib):
+    """No segments, or only empty ones: nothing to launch, MA_OK (no GPU needed)."""
+    hp = _lib._AdamWHParams(lr=1e-3, beta1=0.9, beta2=0.95, eps=1e-8, weight_decay=0.1, step=1,
+                            decoupled=1, cautious_wd=0)
+    assert lib.ma_adamw_step_multi(None, 0, ctypes.byref(hp), None) == _lib.MA_OK
+    segs = (_lib._AdamWSegment * 3)()
+    for i in range(3):
+        segs[i] = _lib._AdamWSegment(None, None, None, None, 0)
+    assert lib.ma_adamw_step_multi(segs, 3, ctypes.byref(hp), None) == _lib.MA_OK
+    ma.adamw_step_multi([], step=1, lr=1e-3)
