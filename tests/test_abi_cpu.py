@@ -6,6 +6,7 @@ import ctypes
 import os
 import re
 
+import numpy as np
 import pytest
 
 import oracle
@@ -368,3 +369,31 @@ def test_adamw_step_multi_empty_calls_are_no_ops(lib):
         segs[i] = _lib._AdamWSegment(None, None, None, None, 0)
     assert lib.ma_adamw_step_multi(segs, 3, ctypes.byref(hp), None) == _lib.MA_OK
     ma.adamw_step_multi([], step=1, lr=1e-3)
+
+
+def test_adamw_step_multi_overlap_sweep_matches_brute_force(lib):
+    """Random layouts of 3-12 segments packed into a small address window: wherever a
+    brute-force pairwise check finds a written range (param, exp_avg, exp_avg_sq) meeting
+    any other range, the call is rejected before launch.  Only such layouts are tried,
+    so nothing here can reach a kernel."""
+    rng = np.random.default_rng(21)
+    hp = _lib._AdamWHParams(lr=1e-3, beta1=0.9, beta2=0.95, eps=1e-8, weight_decay=0.1, step=1,
+                            decoupled=1, cautious_wd=0)
+    tried = 0
+    while tried < 60:
+        k = int(rng.integers(3, 13))
+        segs = (_lib._AdamWSegment * k)()
+        spans = []
+        for i in range(k):
+            n = int(rng.integers(1, 64))
+            ptrs = [FAKE + 4 * int(rng.integers(0, 4000)) for _ in range(4)]
+            segs[i] = _lib._AdamWSegment(*ptrs, n)
+            for j, q in enumerate(ptrs):
+                spans.append((q, q + 4 * n, j != 1))     # grad (index 1) is read only
+        clash = any((a[2] or b[2]) and a[0] < b[1] and b[0] < a[1]
+                    for x, a in enumerate(spans) for b in spans[x + 1:])
+        if not clash:
+            continue
+        tried += 1
+        assert lib.ma_adamw_step_multi(segs, k, ctypes.byref(hp), None) == _lib.MA_ERR_INVALID_ARG
+        assert b"overlap" in lib.ma_last_error()
