@@ -5,11 +5,14 @@ against: only ``tests/``, ``__graft_entry__.smoke()`` and the benchmark's
 ``cpu_baseline`` leg may import it.  It shares no code with the HIP path (the
 package ``adamw_optimizer_step_muon_amd``) and imports nothing from it.
 
-Each function follows the pages' definitions step by step and cites them;
+Each function writes out the pages' definitions and cites them;
 ``tests/test_oracle_*.py`` pins every function to values printed on the pages,
-closed forms and special cases.  Parity status per function:
+closed forms, independent formulations and special cases.  Parity status per
+function:
 
-* newton_schulz, route, update_scale     pinned (SVD closed form, printed spectra)
+* newton_schulz, route, update_scale     pinned (the printed matrix iteration and
+                                         the SVD form, each restated in the tests;
+                                         printed spectra; invariant band)
 * muon_step                              pinned (composition of pinned parts,
                                          zero-gradient decay, momentum closed form)
 * muon_step with cautious_wd             special cases only; beyond them the

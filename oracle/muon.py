@@ -14,8 +14,9 @@ Sources (page titles as published):
   options": Nesterov switch, cautious weight decay (decay only where the
   update and the parameter have the same sign).
 
-Each step below is the pages' definition written out in float64 with numpy.
-The only library primitive is the matrix product.  Pins: tests/test_oracle_muon.py.
+Each function is the pages' definition written out in float64 with numpy; the
+library primitives are the matrix product and the symmetric eigendecomposition.
+Pins: tests/test_oracle_muon.py.
 """
 from __future__ import annotations
 
@@ -58,27 +59,54 @@ def _coeff_table(coeffs, steps: int) -> Sequence[Tuple[float, float, float]]:
     return [tuple(r) for r in c]
 
 
-def newton_schulz(G: np.ndarray, steps: int = 5, coeffs=QUINTIC, eps: float = 1e-7) -> np.ndarray:
-    """Approximate orthogonal polar factor of G by the quintic Newton-Schulz iteration.
+def _spectral_factor(t: np.ndarray, table) -> np.ndarray:
+    """h(t) = f(s) / s for the squared normalised singular values t = s^2, where f is the
+    composition of the scalar polynomials p_k(s) = a_k s + b_k s^3 + c_k s^5.
 
-    [HB] newton_schulz listing, in its order:
-      1. X = G / (||G||_F + eps)            (spectral norm <= 1)
-      2. transpose when rows > cols         (smaller Gram side)
-      3. repeat: R = X X^T;  X = a X + (b R + c R R) X
-      4. transpose back
+    Each p_k(s) = s q_k(s^2) with q_k(t) = a_k + b_k t + c_k t^2, so along the orbit
+    s_{k+1} = s_k q_k(t_k) of one singular value, t_{k+1} = t_k q_k(t_k)^2 and
+    f(s) / s = q_1(t_1) q_2(t_2) ... : no division by s (zero singular values included).
+    """
+    h = np.ones_like(t)
+    for a, b, c in table:
+        q = a + b * t + c * t * t
+        h = h * q
+        t = t * q * q
+    return h
+
+
+def newton_schulz(G: np.ndarray, steps: int = 5, coeffs=QUINTIC, eps: float = 1e-7) -> np.ndarray:
+    """The matrix the quintic Newton-Schulz iteration produces from G, in float64.
+
+    [HB] Muon section: G is divided by its Frobenius norm plus eps, then each of the
+    ``steps`` iterations replaces X by a X + b (X X^T) X + c (X X^T)^2 X.  Every term is
+    a polynomial in X X^T times X, so with the singular value decomposition
+    X = U diag(s) V^T one iteration gives U diag(a s + b s^3 + c s^5) V^T: the singular
+    vectors are kept and each singular value follows the scalar polynomial on its own
+    (the section's point: all of them are pushed toward 1).  The oracle evaluates that
+    result directly instead of repeating the matrix products: with the smaller Gram
+    matrix X X^T = Q diag(t) Q^T (t = s^2; eigendecomposition in float64), U = Q and
+    diag(s) V^T = Q^T X, so the result is Q diag(h(t)) Q^T X with h(t) = f(s) / s
+    (_spectral_factor).  For a matrix with more rows than columns the Gram matrix of the
+    transpose is the smaller one: the result is computed for G^T and transposed back
+    (the value is the same either way; [HB] transposes for the same reason, cost).
     ``coeffs`` is one (a, b, c) triple or a per-iteration (steps, 3) table.
     """
     X = np.array(G, dtype=np.float64, copy=True)
     if X.ndim != 2:
         raise ValueError("newton_schulz takes one 2-D matrix")
     X = X / (np.linalg.norm(X) + eps)
+    if not np.all(np.isfinite(X)):
+        # a NaN or Inf anywhere reaches every entry through the products X X^T and
+        # (X X^T)^2 of the first iteration
+        return np.full(X.shape, np.nan)
     transposed = X.shape[0] > X.shape[1]
     if transposed:
-        X = X.T
-    for a, b, c in _coeff_table(coeffs, steps):
-        R = X @ X.T
-        X = a * X + (b * R + c * (R @ R)) @ X
-    return X.T if transposed else X
+        X = np.ascontiguousarray(X.T)
+    t, Q = np.linalg.eigh(X @ X.T)
+    h = _spectral_factor(t, _coeff_table(coeffs, steps))
+    O = (Q * h) @ (Q.T @ X)
+    return O.T if transposed else O
 
 
 def update_scale(A: int, B: int, scale_mode: int = 0) -> float:
@@ -108,14 +136,13 @@ def muon_step(param: np.ndarray, grad: np.ndarray, momentum: np.ndarray, *, lr: 
               cautious_wd: bool = False, scale_mode: int = 0) -> MuonResult:
     """One Muon step on one A x B matrix, in float64.
 
-    [HB] update steps and Muon listing:
-      1. M <- mu M + G                              (sum-form momentum, M starts at 0)
-      2. U <- G + mu M  (Nesterov, new M)   or  U <- M
-      3. O <- newton_schulz(U)
-      4. P <- P (1 - lr wd)                         (decoupled decay, old P)
-      5. P <- P - lr * s * O,   s = update_scale(A, B)
-    [DM] cautious weight decay: the decay of step 4 applies only where the
-    update u = s O and the old parameter have the same sign (u * p > 0).
+    [HB] the update's three steps: the momentum is the running sum M <- mu M + G
+    (M starts at zero); the matrix that is orthogonalised is the Nesterov look-ahead
+    G + mu M with the new M (or M itself without Nesterov); the parameter takes the
+    orthogonalised matrix O scaled by s = update_scale(A, B) and the learning rate,
+    after the decoupled decay P (1 - lr wd) of the old parameter.
+    [DM] cautious weight decay: the decay applies only where the update u = s O and
+    the old parameter have the same sign (u * p > 0, strict).
     """
     P = np.asarray(param, dtype=np.float64)
     G = np.asarray(grad, dtype=np.float64)

@@ -1,7 +1,15 @@
 """Pins of the Muon oracle against values and facts fixed outside of it.
 
-* the closed form of the iteration through the SVD (Newton-Schulz acts on the
-  singular values only, through the scalar quintic p(x) = a x + b x^3 + c x^5);
+The oracle evaluates the Newton-Schulz result through the eigendecomposition of the
+Gram matrix; it is pinned here against two other formulations of the same thing:
+
+* the iteration as the handbook prints it, matrix products repeated in float64
+  (normalise, transpose a tall matrix, X <- a X + (b R + c R R) X with R = X X^T,
+  transpose back);
+* the closed form through numpy's SVD (Newton-Schulz acts on the singular values
+  only, through the scalar quintic p(x) = a x + b x^3 + c x^5);
+
+and against
 * the cubic (1.5, -0.5, 0) iteration, which converges to the exact polar factor
   U V^T that numpy's SVD gives;
 * the spectra, energy and RMS printed by the handbook's orthogonalize.py run;
@@ -39,13 +47,62 @@ def _svd_closed_form(G, steps, coeffs=QUINTIC, eps=1e-7):
     return (U * f) @ Vt
 
 
+def _printed_iteration(G, steps, coeffs=QUINTIC, eps=1e-7):
+    """The handbook's newton_schulz, as matrix products in float64."""
+    table = [coeffs] * steps if np.ndim(coeffs) == 1 else [tuple(r) for r in coeffs]
+    X = G / (np.linalg.norm(G) + eps)
+    tall = X.shape[0] > X.shape[1]
+    if tall:
+        X = X.T
+    for a, b, c in table:
+        R = X @ X.T
+        X = a * X + (b * R + c * R @ R) @ X
+    return X.T if tall else X
+
+
+@pytest.mark.parametrize("shape,seed", [((64, 128), 0), ((128, 64), 1), ((96, 96), 2),
+                                        ((40, 130), 3), ((1, 9), 4), ((9, 1), 5)])
+@pytest.mark.parametrize("steps", [0, 1, 2, 5, 7])
+@pytest.mark.parametrize("coeffs", [QUINTIC, (2.0, -1.5, 0.5), (1.5, -0.5, 0.0),
+                                    (0.0, 1.0, 0.0), (0.0, 0.0, 1.0), (1.0, 0.0, 0.0)])
+def test_ns_matches_printed_iteration(shape, seed, steps, coeffs):
+    """Term by term: (0, 1, 0) is the b R X term alone, (0, 0, 1) the c R^2 X term,
+    (1, 0, 0) the a X term (normalisation only).  The repeated products carry their own
+    float64 rounding, which each iteration amplifies at most by the polynomial's slope
+    (a = 3.4445 near zero): the bound grows with it."""
+    G = _rand(shape, seed, row_scale=1.0)
+    got = newton_schulz(G, steps, coeffs)
+    ref = _printed_iteration(G, steps, coeffs)
+    tol = 1e-14 * 3.5 ** steps
+    assert np.max(np.abs(got - ref)) <= tol * max(1.0, np.max(np.abs(ref)))
+
+
+def test_ns_per_iteration_table_matches_printed_iteration():
+    G = _rand((70, 45), 8, row_scale=1.0)
+    table = np.array([[3.4445, -4.7750, 2.0315], [2.0, -1.5, 0.5], [1.5, -0.5, 0.0]])
+    assert np.max(np.abs(newton_schulz(G, 3, table) - _printed_iteration(G, 3, table))) < 1e-12
+
+
+def test_ns_zero_and_non_finite_inputs():
+    assert np.array_equal(newton_schulz(np.zeros((6, 9))), np.zeros((6, 9)))
+    for bad in (np.nan, np.inf):
+        G = _rand((6, 9), 1)
+        G[2, 3] = bad
+        with np.errstate(invalid="ignore"):
+            ref = _printed_iteration(G, 1)
+            got = newton_schulz(G, 1)
+        assert np.all(np.isnan(ref)) and np.all(np.isnan(got))
+
+
 @pytest.mark.parametrize("shape,seed", [((64, 128), 0), ((128, 64), 1), ((96, 96), 2), ((40, 130), 3)])
 @pytest.mark.parametrize("steps", [0, 1, 5, 7])
 def test_ns_matches_svd_closed_form(shape, seed, steps):
     G = _rand(shape, seed, row_scale=1.0)
     got = newton_schulz(G, steps)
     ref = _svd_closed_form(G, steps)
-    assert np.max(np.abs(got - ref)) < 1e-12
+    # the oracle decomposes X X^T, whose small eigenvalues carry absolute (not relative)
+    # float64 errors; the polynomial's slope near zero (a per step) scales them
+    assert np.max(np.abs(got - ref)) < 1e-14 * 3.5 ** steps
 
 
 def test_ns_per_iteration_table_matches_closed_form():
