@@ -20,13 +20,14 @@ MA_ERR_INVALID_ARG = -1
 MA_ERR_UNSUPPORTED = -2
 MA_ERR_WORKSPACE = -3
 MA_ERR_HIP = -4
+MA_ERR_INTERNAL = -5
 MA_MAX_NS_STEPS = 64
 
 EXPORTED = (
     "ma_abi_version", "ma_status_string", "ma_last_error", "ma_muon_route_of",
     "ma_muon_workspace_bytes", "ma_muon_phases", "ma_muon_step", "ma_adamw_step",
     "ma_newton_schulz_workspace_bytes", "ma_newton_schulz", "ma_muon_tune", "ma_muon_tune_reset",
-    "ma_adamw_step_multi",
+    "ma_adamw_step_multi", "ma_muon_check_plan", "ma_muon_ns_time",
 )
 
 
@@ -54,6 +55,11 @@ class _MuonRoute(ctypes.Structure):
     _fields_ = [("transposed", ctypes.c_int32), ("m", ctypes.c_int32), ("n", ctypes.c_int32),
                 ("ns_steps_run", ctypes.c_int32), ("m_pad", ctypes.c_int32),
                 ("n_pad", ctypes.c_int32), ("ns_mode_run", ctypes.c_int32)]
+
+
+class _PlanReport(ctypes.Structure):
+    _fields_ = [("launches", ctypes.c_int64), ("gemm_blocks", ctypes.c_int64),
+                ("gemm_tiles", ctypes.c_int64)]
 
 
 class _AdamWSegment(ctypes.Structure):
@@ -131,6 +137,15 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
                                         ctypes.POINTER(_AdamWHParams), ctypes.c_void_p]
     lib.ma_muon_tune_reset.restype = None
     lib.ma_muon_tune_reset.argtypes = []
+    lib.ma_muon_check_plan.restype = ctypes.c_int
+    lib.ma_muon_check_plan.argtypes = [ctypes.POINTER(_MuonBucket), ctypes.c_int32,
+                                       ctypes.POINTER(_MuonHParams), ctypes.c_int32,
+                                       ctypes.POINTER(_PlanReport)]
+    lib.ma_muon_ns_time.restype = ctypes.c_int
+    lib.ma_muon_ns_time.argtypes = [ctypes.POINTER(_MuonBucket), ctypes.c_int32,
+                                    ctypes.POINTER(_MuonHParams), ctypes.c_void_p,
+                                    ctypes.c_size_t, ctypes.c_void_p, ctypes.c_int32,
+                                    ctypes.POINTER(ctypes.c_float)]
     _lib = lib
     return lib
 
@@ -217,8 +232,8 @@ def _as_stack(t):
 # --------------------------------------------------------------------------
 # entry points (names of the C ABI without the ma_ prefix)
 # --------------------------------------------------------------------------
-def muon_route_of(A: int, B: int, ns_steps: int = 5) -> Route:
-    hp = _MuonHParams(ns_steps=int(ns_steps))
+def muon_route_of(A: int, B: int, ns_steps: int = 5, ns_mode: int = 0) -> Route:
+    hp = _MuonHParams(ns_steps=int(ns_steps), ns_mode=int(ns_mode))
     out = _MuonRoute()
     _check(load().ma_muon_route_of(int(A), int(B), ctypes.byref(hp), ctypes.byref(out)))
     return Route(bool(out.transposed), out.m, out.n, out.ns_steps_run, out.m_pad, out.n_pad,
@@ -400,3 +415,48 @@ def newton_schulz(inp, out, *, ns_steps: int = 5, ns_coeffs=None, ns_eps: float 
     ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
     _check(load().ma_newton_schulz(_ptr(i3), _ptr(o3), K, A, B, ctypes.byref(hp), _ptr(workspace),
                                    ws_bytes, _stream_handle(stream, inp.device)))
+
+
+def muon_check_plan(shapes: Sequence[Sequence[int]], *, what: int = 0, ns_steps: int = 5,
+                    ns_mode: int = 0, ns_coeffs=None) -> dict:
+    """Dry run of the launches of ma_muon_step (what 0) or ma_newton_schulz (what 1, first
+    shape) for buckets of these (K, A, B) shapes (ma_muon_check_plan): raises
+    MuonAdamWError if a launch reads or writes outside its buffers or misses / repeats an
+    output tile; returns the counts of what was checked."""
+    n = len(shapes)
+    arr = (_MuonBucket * max(n, 1))()
+    for i, (K, A, B) in enumerate(shapes):
+        arr[i] = _MuonBucket(int(K), int(A), int(B), 0, 0, 0)
+    hp, _keep = _muon_hparams(0.02, 0.95, 0.1, True, ns_steps, ns_coeffs, 1e-7, False, 0, ns_mode)
+    rep = _PlanReport()
+    _check(load().ma_muon_check_plan(arr, n, ctypes.byref(hp), int(what), ctypes.byref(rep)))
+    return {"launches": rep.launches, "gemm_blocks": rep.gemm_blocks, "gemm_tiles": rep.gemm_tiles}
+
+
+def muon_ns_time(grads, *, reps: int = 3, ns_steps: int = 5, ns_coeffs=None, ns_eps: float = 1e-7,
+                 ns_mode: int = 0, workspace=None, stream=None):
+    """Milliseconds per phase of the Newton-Schulz GEMM launches of ma_muon_step on these
+    (K, A, B) gradient stacks (ma_muon_ns_time; synchronises).  Each repetition first casts
+    the gradients into the workspace (untimed), then times the phase's launches."""
+    stacks = []
+    for i, g in enumerate(grads):
+        _require_f32_cuda(f"gradient {i}", g)
+        stacks.append(_as_stack(g))
+    n = len(stacks)
+    arr = (_MuonBucket * max(n, 1))()
+    for i, g in enumerate(stacks):
+        K, A, B = g.shape
+        arr[i] = _MuonBucket(K, A, B, 0, _ptr(g), 0)
+    hp, _keep = _muon_hparams(0.0, 0.0, 0.0, True, ns_steps, ns_coeffs, ns_eps, False, 0, ns_mode)
+    lib = load()
+    need = int(lib.ma_muon_workspace_bytes(arr, n, ctypes.byref(hp)))
+    device = stacks[0].device if stacks else None
+    if workspace is None and need > 0:
+        workspace = _scratch(need, device, stream)
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    nph = muon_phases([tuple(g.shape) for g in stacks], ns_mode)[0]
+    out = (ctypes.c_float * max(nph, 1))()
+    _check(lib.ma_muon_ns_time(arr, n, ctypes.byref(hp), _ptr(workspace), ws_bytes,
+                               _stream_handle(stream, device) if device is not None else 0,
+                               int(reps), out))
+    return [float(out[i]) for i in range(nph)]

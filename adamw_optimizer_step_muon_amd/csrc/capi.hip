@@ -389,13 +389,100 @@ ma_status prep_bucket(const BucketPlan& p, const float* grad, float* momentum,
                         : (hp->ns_steps == 0 ? at<unsigned short>(w, p.off_x[1]) : nullptr);
   unsigned short* S = p.transposed ? own : X0;   // the matrix's own orientation
   unsigned short* T = p.transposed ? X0 : XT0;   // its transpose
-  float* partials = at<float>(w, p.off_part);
+  double* partials = at<double>(w, p.off_part);
   float* inv = at<float>(w, p.off_inv);
+  int* shift = at<int>(w, p.off_shift);
   hipError_t e = launch_muon_prep(p, grad, momentum, momentum ? hp->momentum : 0.0f,
                                   momentum ? hp->nesterov : 0, partials, S, T, s);
   if (e != hipSuccess) return hip_fail(e, "momentum/cast launch");
-  e = launch_norm_finalize(p, partials, hp->ns_eps, inv, s);
+  e = launch_norm_finalize(p, partials, hp->ns_eps, inv, shift, s);
   if (e != hipSuccess) return hip_fail(e, "norm launch");
+  e = launch_rescale(p, S, T, shift, s);
+  if (e != hipSuccess) return hip_fail(e, "rescale launch");
+  return MA_OK;
+}
+
+// One phase of ma_muon_step: momentum, cast and norm of each bucket, the Newton-Schulz
+// launches shared by the phase's buckets, then each bucket's update.
+ma_status run_phase(const Phase& ph, const ma_muon_bucket* buckets, const ma_muon_hparams* hp,
+                    char* ws, hipStream_t s) {
+  for (int j = 0; j < ph.n; ++j) {
+    const ma_muon_bucket& b = buckets[ph.bucket[j]];
+    const ma_status st = prep_bucket(ph.plan[j], b.grad, b.momentum, hp, ws + ph.base[j], s);
+    if (st != MA_OK) return st;
+  }
+  const unsigned short* O[kMaxGemmGroups];
+  int64_t ldo[kMaxGemmGroups];
+  const float* oscale[kMaxGemmGroups];
+  const ma_status st = run_ns(ph, hp, ws, s, O, ldo, oscale);
+  if (st != MA_OK) return st;
+  for (int j = 0; j < ph.n; ++j) {
+    const ma_muon_bucket& b = buckets[ph.bucket[j]];
+    const double big = static_cast<double>(b.A > b.B ? b.A : b.B);
+    const double scale =
+        hp->scale_mode == 0
+            ? 0.2 * std::sqrt(big)
+            : std::sqrt(std::fmax(1.0, static_cast<double>(b.A) / static_cast<double>(b.B)));
+    const hipError_t e = launch_muon_apply(ph.plan[j], b.param, O[j], oscale[j], ldo[j], hp->lr,
+                                           hp->weight_decay, static_cast<float>(scale),
+                                           hp->cautious_wd, s);
+    if (e != hipSuccess) return hip_fail(e, "apply launch");
+  }
+  return MA_OK;
+}
+
+// ma_newton_schulz after its argument checks: cast, iterate, write out = NS(in) in fp32.
+ma_status newton_schulz_body(const BucketPlan& p, const float* in, float* out,
+                             const ma_muon_hparams* hp, char* ws, hipStream_t s) {
+  Phase ph;
+  phase_add(ph, p, 0);
+  ma_status st = prep_bucket(p, in, nullptr, hp, ws, s);
+  if (st != MA_OK) return st;
+  const unsigned short* O[kMaxGemmGroups];
+  int64_t ldo[kMaxGemmGroups];
+  const float* oscale[kMaxGemmGroups];
+  st = run_ns(ph, hp, ws, s, O, ldo, oscale);
+  if (st != MA_OK) return st;
+  const hipError_t e = launch_ns_extract(p, out, O[0], oscale[0], ldo[0], s);
+  if (e != hipSuccess) return hip_fail(e, "extract launch");
+  return MA_OK;
+}
+
+// The argument checks of ma_muon_step (everything but the workspace).
+ma_status check_step_args(const ma_muon_bucket* buckets, int32_t n_buckets,
+                          const ma_muon_hparams* hp) {
+  ma_status st = check_hparams(hp);
+  if (st != MA_OK) return st;
+  if (n_buckets < 0) return fail(MA_ERR_INVALID_ARG, "n_buckets %d < 0", n_buckets);
+  if (n_buckets > 0 && !buckets) return fail(MA_ERR_INVALID_ARG, "buckets is NULL");
+  for (int32_t i = 0; i < n_buckets; ++i) {
+    const ma_muon_bucket& b = buckets[i];
+    st = check_shape(b.K, b.A, b.B);
+    if (st != MA_OK) return fail(st, "bucket %d: %s", i, g_last_error.c_str());
+    if (b.K == 0) continue;
+    if (!b.param || !b.grad || !b.momentum)
+      return fail(MA_ERR_INVALID_ARG, "bucket %d: NULL param, grad or momentum", i);
+    if ((reinterpret_cast<uintptr_t>(b.param) | reinterpret_cast<uintptr_t>(b.grad) |
+         reinterpret_cast<uintptr_t>(b.momentum)) & 3u)
+      return fail(MA_ERR_INVALID_ARG, "bucket %d: pointers must be 4-byte aligned", i);
+    const int64_t bytes = b.K * b.A * b.B * 4;
+    const Range rp = range_of(b.param, bytes), rg = range_of(b.grad, bytes),
+                rm = range_of(b.momentum, bytes);
+    if (overlap(rp, rg) || overlap(rp, rm) || overlap(rg, rm))
+      return fail(MA_ERR_INVALID_ARG, "bucket %d: param, grad and momentum overlap", i);
+    // Across buckets: what one bucket writes (param, momentum) must not overlap
+    // anything another bucket touches; gradients are read only and may alias.
+    for (int32_t j = 0; j < i; ++j) {
+      const ma_muon_bucket& o = buckets[j];
+      if (o.K == 0) continue;
+      const int64_t ob = o.K * o.A * o.B * 4;
+      const Range op = range_of(o.param, ob), og = range_of(o.grad, ob),
+                  om = range_of(o.momentum, ob);
+      if (overlap(rp, op) || overlap(rp, og) || overlap(rp, om) || overlap(rm, op) ||
+          overlap(rm, og) || overlap(rm, om) || overlap(rg, op) || overlap(rg, om))
+        return fail(MA_ERR_INVALID_ARG, "buckets %d and %d overlap", j, i);
+    }
+  }
   return MA_OK;
 }
 
@@ -426,7 +513,184 @@ ma_status adamw_const(const ma_adamw_hparams* hp, AdamWConst* c) {
 // Grid size limit of one launch (blocks), with the room the block-count arithmetic needs.
 constexpr int64_t kMaxGridBlocks = (int64_t(1) << 31) - 4096;
 
+// ---------------------------------------------------------------------------
+// Plan check: replays the launches of a step with a recorder installed and checks, block
+// by block, that every read and write stays inside the buffer it addresses, and that
+// the GEMM blocks of each launch cover every output tile exactly once.
+// ---------------------------------------------------------------------------
+struct Region {
+  uintptr_t lo, hi;
+  std::string name;
+};
+
+class PlanChecker final : public LaunchRecorder {
+ public:
+  std::vector<Region> regions;
+  std::string error;
+  int64_t launches = 0, gemm_blocks = 0, tiles = 0;
+
+  // the buffers of one phase (workspace regions of each bucket, and the caller's tensors)
+  void set_phase(const Phase& ph, uintptr_t ws, size_t ws_bytes, const ma_muon_bucket* buckets,
+                 bool has_momentum) {
+    regions.clear();
+    for (int j = 0; j < ph.n; ++j) {
+      const BucketPlan& p = ph.plan[j];
+      const uintptr_t b = ws + ph.base[j];
+      const size_t xb = static_cast<size_t>(p.K * p.m_pad * p.n_pad) * 2;
+      const size_t rb = static_cast<size_t>(p.K * p.m_pad * p.m_pad) * 2;
+      const std::string t = "bucket " + std::to_string(ph.bucket[j]) + " ";
+      add(b + p.off_x[0], xb, t + "X[0]");
+      add(b + p.off_x[1], xb, t + "X[1]");
+      if (p.keeps_xt) {
+        add(b + p.off_xt[0], xb, t + "XT[0]");
+        add(b + p.off_xt[1], xb, t + "XT[1]");
+      }
+      add(b + p.off_r, rb, t + "R");
+      add(b + p.off_p, rb, t + "P");
+      if (p.gram_space) {
+        add(b + p.off_r2, rb, t + "R2");
+        add(b + p.off_q[0], rb, t + "Q[0]");
+        add(b + p.off_q[1], rb, t + "Q[1]");
+        add(b + p.off_t, rb, t + "T");
+      }
+      add(b + p.off_part, static_cast<size_t>(p.K * p.nblk) * 8, t + "partials");
+      add(b + p.off_inv, static_cast<size_t>(p.K) * 4, t + "inv");
+      add(b + p.off_shift, static_cast<size_t>(p.K) * 4, t + "shift");
+      const ma_muon_bucket& u = buckets[ph.bucket[j]];
+      const size_t eb = static_cast<size_t>(u.K * u.A * u.B) * 4;
+      add(reinterpret_cast<uintptr_t>(u.param), eb, t + "param");
+      add(reinterpret_cast<uintptr_t>(u.grad), eb, t + "grad");
+      if (has_momentum) add(reinterpret_cast<uintptr_t>(u.momentum), eb, t + "momentum");
+      if (ph.base[j] + p.bytes > ws_bytes) fail_("bucket workspace beyond the workspace");
+    }
+    for (size_t i = 0; i < regions.size(); ++i)
+      for (size_t k = i + 1; k < regions.size(); ++k)
+        if (regions[i].lo < regions[k].hi && regions[k].lo < regions[i].hi)
+          fail_("buffers " + regions[i].name + " and " + regions[k].name + " overlap");
+  }
+
+  void gemm(int epi, TileCfg cfg, const GemmTable& t) override {
+    ++launches;
+    const TileShape sh = tile_shape(cfg);
+    const bool bt = epi == kCombine && sh.combine_reads_x;
+    const int grid = t.start[t.ngroups];
+    std::vector<std::vector<int>> seen(t.ngroups);
+    for (int gi = 0; gi < t.ngroups; ++gi) {
+      const GemmArgs& a = t.g[gi];
+      if (a.kdim % sh.bk != 0) return fail_("contraction not a multiple of the stage depth");
+      if (a.tiles_per_batch != (epi == kCombine ? a.tiles_m * a.tiles_n
+                                                : a.tiles_m * (a.tiles_m + 1) / 2))
+        return fail_("tile count does not match the tile grid");
+      if (t.start[gi + 1] - t.start[gi] < a.tiles_per_batch * a.tiles_k || t.start[gi] % 8)
+        return fail_("group block range too small or not on a multiple of 8");
+      seen[gi].assign(static_cast<size_t>(a.tiles_per_batch) * a.tiles_k, 0);
+    }
+    for (int bid = 0; bid < grid && error.empty(); ++bid) {
+      int gi, ti, tj;
+      int64_t batch;
+      if (!gemm_block_tile(t, epi, bid, gi, batch, ti, tj)) continue;
+      ++gemm_blocks;
+      const GemmArgs& a = t.g[gi];
+      if (batch < 0 || batch >= a.tiles_k || ti < 0 || ti >= a.tiles_m || tj < 0 ||
+          tj >= a.tiles_n || (epi != kCombine && tj > ti))
+        return fail_("block " + std::to_string(bid) + " maps outside the tile grid");
+      const int64_t slot = epi == kCombine ? static_cast<int64_t>(ti) * a.tiles_n + tj
+                                           : static_cast<int64_t>(ti) * (ti + 1) / 2 + tj;
+      if (++seen[gi][batch * a.tiles_per_batch + slot] != 1)
+        return fail_("tile computed twice in one launch");
+      const int64_t m0 = static_cast<int64_t>(ti) * sh.bm, n0 = static_cast<int64_t>(tj) * sh.bn;
+      // operand panels
+      win(a.A, batch * a.strideA + m0 * a.lda, (sh.bm - 1) * a.lda + a.kdim, "A operand");
+      if (bt)
+        win(a.B, batch * a.strideB + n0, (a.kdim - 1) * a.ldb + sh.bn, "B operand (X rows)");
+      else
+        win(a.B, batch * a.strideB + n0 * a.ldb, (sh.bn - 1) * a.ldb + a.kdim, "B operand");
+      if (epi == kPoly)
+        win(a.aux, batch * a.strideAux + n0 * a.ldaux + m0, (sh.bn - 1) * a.ldaux + sh.bm,
+            "polynomial's R term");
+      if (a.scale) winb(reinterpret_cast<uintptr_t>(a.scale + batch), 4, "scale");
+      // results: the tile, and its transposed / mirrored copy
+      const bool need_c = epi != kCombine || a.C;
+      const bool need_t = epi == kCombine ? a.C2 != nullptr : ti != tj;
+      if (need_c) win(a.C, batch * a.strideC + m0 * a.ldc + n0, (sh.bm - 1) * a.ldc + sh.bn, "C");
+      if (need_t)
+        win(a.C2, batch * a.strideC2 + n0 * a.ldc2 + m0, (sh.bn - 1) * a.ldc2 + sh.bm, "C2");
+    }
+    if (!error.empty()) return;
+    for (int gi = 0; gi < t.ngroups; ++gi)
+      for (int v : seen[gi])
+        if (v != 1) return fail_("an output tile is not computed");
+    for (int gi = 0; gi < t.ngroups; ++gi) tiles += static_cast<int64_t>(seen[gi].size());
+  }
+
+  void prep(const BucketPlan& p, const float* G, const float* M, const double* partials,
+            const unsigned short* S, const unsigned short* T) override {
+    ++launches;
+    const int64_t Ap = p.transposed ? p.n_pad : p.m_pad, Bp = p.transposed ? p.m_pad : p.n_pad;
+    if (Ap % kCastTile || Bp % kCastTile || (Ap / kCastTile) * (Bp / kCastTile) != p.nblk)
+      return fail_("cast grid does not match the partial sums");
+    winb(reinterpret_cast<uintptr_t>(G), p.K * p.A * p.B * 4, "gradient");
+    if (M) winb(reinterpret_cast<uintptr_t>(M), p.K * p.A * p.B * 4, "momentum");
+    winb(reinterpret_cast<uintptr_t>(partials), p.K * p.nblk * 8, "partials");
+    if (S) win(S, 0, p.K * Ap * Bp, "cast S");
+    if (T) win(T, 0, p.K * Ap * Bp, "cast T");
+  }
+  void norm(const BucketPlan& p, const double* partials, const float* inv,
+            const int* shift) override {
+    ++launches;
+    winb(reinterpret_cast<uintptr_t>(partials), p.K * p.nblk * 8, "partials");
+    winb(reinterpret_cast<uintptr_t>(inv), p.K * 4, "inv");
+    winb(reinterpret_cast<uintptr_t>(shift), p.K * 4, "shift");
+  }
+  void rescale(const BucketPlan& p, const unsigned short* S, const unsigned short* T,
+               const int* shift) override {
+    ++launches;
+    if (S) win(S, 0, p.K * p.m_pad * p.n_pad, "rescaled S");
+    if (T) win(T, 0, p.K * p.m_pad * p.n_pad, "rescaled T");
+    winb(reinterpret_cast<uintptr_t>(shift), p.K * 4, "shift");
+  }
+  void apply(const BucketPlan& p, const float* out, const unsigned short* O, const float* oscale,
+             int64_t ldo) override {
+    ++launches;
+    if (ldo < p.B || (p.A - 1) * ldo + p.B > p.m_pad * p.n_pad)
+      return fail_("orthogonalised matrix rows do not fit its slab");
+    win(O, 0, (p.K - 1) * p.m_pad * p.n_pad + (p.A - 1) * ldo + p.B, "orthogonalised matrix");
+    winb(reinterpret_cast<uintptr_t>(out), p.K * p.A * p.B * 4, "parameter / output");
+    if (oscale) winb(reinterpret_cast<uintptr_t>(oscale), p.K * 4, "oscale");
+  }
+
+ private:
+  void add(uintptr_t lo, size_t bytes, std::string name) {
+    regions.push_back(Region{lo, lo + bytes, std::move(name)});
+  }
+  void fail_(const std::string& what) {
+    if (error.empty()) error = what;
+  }
+  // `count` bf16 elements at element offset `off` from q
+  void win(const unsigned short* q, int64_t off, int64_t count, const char* what) {
+    if (!q) return fail_(std::string(what) + ": null pointer");
+    if (off < 0 || count < 0) return fail_(std::string(what) + ": negative extent");
+    winb(reinterpret_cast<uintptr_t>(q) + static_cast<uintptr_t>(off) * 2,
+         static_cast<int64_t>(count) * 2, what);
+  }
+  void winb(uintptr_t lo, int64_t bytes, const char* what) {
+    if (!error.empty()) return;
+    for (const Region& r : regions)
+      if (lo >= r.lo && lo < r.hi) {
+        if (lo + static_cast<uintptr_t>(bytes) > r.hi)
+          fail_(std::string(what) + " runs past the end of " + r.name);
+        return;
+      }
+    fail_(std::string(what) + " starts outside every buffer");
+  }
+};
+
 }  // namespace
+
+LaunchRecorder*& launch_recorder() {
+  static thread_local LaunchRecorder* r = nullptr;
+  return r;
+}
 
 int forced_tile() {
   static const int t = [] {
@@ -438,8 +702,11 @@ int forced_tile() {
 }
 
 bool wants_gram_space(int32_t ns_mode, int64_t A, int64_t B) {
-  const int64_t m = A < B ? A : B, n = A < B ? B : A;
-  return ns_mode == 1 && n >= 2 * m;
+  // wide buckets (A < B: X is the matrix itself) with n >= 2 m and m <= 1024: where the
+  // route's bf16 error was measured inside the Muon tolerance on Gaussian, low-rank and
+  // row log-normal gradients; tall row-scaled gradients (any m) and low-rank ones with
+  // Gram sides from 1536 left it, so those buckets run the printed iteration
+  return ns_mode == 1 && A < B && B >= 2 * A && A <= kGramSpaceMaxM;
 }
 
 BucketPlan plan_bucket(int64_t K, int64_t A, int64_t B, int tile, bool gram_space) {
@@ -482,8 +749,10 @@ BucketPlan plan_bucket(int64_t K, int64_t A, int64_t B, int tile, bool gram_spac
     off = align256(off + rb);
   }
   p.off_part = off;
-  off = align256(off + static_cast<size_t>(K * p.nblk) * 4);
+  off = align256(off + static_cast<size_t>(K * p.nblk) * 8);
   p.off_inv = off;
+  off = align256(off + static_cast<size_t>(K) * 4);
+  p.off_shift = off;
   off = align256(off + static_cast<size_t>(K) * 4);
   p.bytes = off;
   return p;
@@ -504,6 +773,7 @@ const char* ma_status_string(int status) {
     case MA_ERR_UNSUPPORTED: return "unsupported";
     case MA_ERR_WORKSPACE: return "workspace missing or too small";
     case MA_ERR_HIP: return "HIP error";
+    case MA_ERR_INTERNAL: return "internal check failed";
     default: return "unknown status";
   }
 }
@@ -516,7 +786,7 @@ ma_status ma_muon_route_of(int64_t A, int64_t B, const ma_muon_hparams* hp, ma_m
   if (A < 1 || B < 1) return fail(MA_ERR_INVALID_ARG, "matrix shape %lld x %lld", (long long)A, (long long)B);
   const int steps = hp ? hp->ns_steps : 5;
   if (steps < 0 || steps > MA_MAX_NS_STEPS) return fail(MA_ERR_INVALID_ARG, "ns_steps %d", steps);
-  *out = route_of(plan_bucket(1, A, B), steps);
+  *out = route_of(plan_bucket(1, A, B, 0, wants_gram_space(hp ? hp->ns_mode : 0, A, B)), steps);
   return MA_OK;
 }
 
@@ -557,38 +827,8 @@ ma_status ma_muon_step(const ma_muon_bucket* buckets, int32_t n_buckets,
                        const ma_muon_hparams* hp, void* workspace, size_t workspace_bytes,
                        void* stream, ma_muon_route* route_out) {
   g_last_error.clear();
-  ma_status st = check_hparams(hp);
+  const ma_status st = check_step_args(buckets, n_buckets, hp);
   if (st != MA_OK) return st;
-  if (n_buckets < 0) return fail(MA_ERR_INVALID_ARG, "n_buckets %d < 0", n_buckets);
-  if (n_buckets > 0 && !buckets) return fail(MA_ERR_INVALID_ARG, "buckets is NULL");
-  for (int32_t i = 0; i < n_buckets; ++i) {
-    const ma_muon_bucket& b = buckets[i];
-    st = check_shape(b.K, b.A, b.B);
-    if (st != MA_OK) return fail(st, "bucket %d: %s", i, g_last_error.c_str());
-    if (b.K == 0) continue;
-    if (!b.param || !b.grad || !b.momentum)
-      return fail(MA_ERR_INVALID_ARG, "bucket %d: NULL param, grad or momentum", i);
-    if ((reinterpret_cast<uintptr_t>(b.param) | reinterpret_cast<uintptr_t>(b.grad) |
-         reinterpret_cast<uintptr_t>(b.momentum)) & 3u)
-      return fail(MA_ERR_INVALID_ARG, "bucket %d: pointers must be 4-byte aligned", i);
-    const int64_t bytes = b.K * b.A * b.B * 4;
-    const Range rp = range_of(b.param, bytes), rg = range_of(b.grad, bytes),
-                rm = range_of(b.momentum, bytes);
-    if (overlap(rp, rg) || overlap(rp, rm) || overlap(rg, rm))
-      return fail(MA_ERR_INVALID_ARG, "bucket %d: param, grad and momentum overlap", i);
-    // Across buckets: what one bucket writes (param, momentum) must not overlap
-    // anything another bucket touches; gradients are read only and may alias.
-    for (int32_t j = 0; j < i; ++j) {
-      const ma_muon_bucket& o = buckets[j];
-      if (o.K == 0) continue;
-      const int64_t ob = o.K * o.A * o.B * 4;
-      const Range op = range_of(o.param, ob), og = range_of(o.grad, ob),
-                  om = range_of(o.momentum, ob);
-      if (overlap(rp, op) || overlap(rp, og) || overlap(rp, om) || overlap(rm, op) ||
-          overlap(rm, og) || overlap(rm, om) || overlap(rg, op) || overlap(rg, om))
-        return fail(MA_ERR_INVALID_ARG, "buckets %d and %d overlap", j, i);
-    }
-  }
   const size_t need = ma_muon_workspace_bytes(buckets, n_buckets, hp);
   if (need > 0) {
     if (!workspace) return fail(MA_ERR_WORKSPACE, "workspace is NULL, %zu bytes needed", need);
@@ -607,30 +847,8 @@ ma_status ma_muon_step(const ma_muon_bucket* buckets, int32_t n_buckets,
   }
   hipStream_t s = static_cast<hipStream_t>(stream);
   char* ws = static_cast<char*>(workspace);
-  return for_each_phase(buckets, n_buckets, hp->ns_mode, [&](const Phase& ph) -> ma_status {
-    for (int j = 0; j < ph.n; ++j) {
-      const ma_muon_bucket& b = buckets[ph.bucket[j]];
-      const ma_status st2 = prep_bucket(ph.plan[j], b.grad, b.momentum, hp, ws + ph.base[j], s);
-      if (st2 != MA_OK) return st2;
-    }
-    const unsigned short* O[kMaxGemmGroups];
-    int64_t ldo[kMaxGemmGroups];
-    const float* oscale[kMaxGemmGroups];
-    const ma_status st2 = run_ns(ph, hp, ws, s, O, ldo, oscale);
-    if (st2 != MA_OK) return st2;
-    for (int j = 0; j < ph.n; ++j) {
-      const ma_muon_bucket& b = buckets[ph.bucket[j]];
-      const double big = static_cast<double>(b.A > b.B ? b.A : b.B);
-      const double scale =
-          hp->scale_mode == 0
-              ? 0.2 * std::sqrt(big)
-              : std::sqrt(std::fmax(1.0, static_cast<double>(b.A) / static_cast<double>(b.B)));
-      const hipError_t e = launch_muon_apply(ph.plan[j], b.param, O[j], oscale[j], ldo[j], hp->lr,
-                                             hp->weight_decay, static_cast<float>(scale),
-                                             hp->cautious_wd, s);
-      if (e != hipSuccess) return hip_fail(e, "apply launch");
-    }
-    return MA_OK;
+  return for_each_phase(buckets, n_buckets, hp->ns_mode, [&](const Phase& ph) {
+    return run_phase(ph, buckets, hp, ws, s);
   });
 }
 
@@ -663,20 +881,8 @@ ma_status ma_newton_schulz(const float* in, float* out, int64_t K, int64_t A, in
     return fail(MA_ERR_WORKSPACE, "workspace must be 256-byte aligned");
   if (workspace_bytes < p.bytes)
     return fail(MA_ERR_WORKSPACE, "workspace has %zu bytes, %zu needed", workspace_bytes, p.bytes);
-  hipStream_t s = static_cast<hipStream_t>(stream);
-  char* ws = static_cast<char*>(workspace);
-  Phase ph;
-  phase_add(ph, p, 0);
-  st = prep_bucket(p, in, nullptr, hp, ws, s);
-  if (st != MA_OK) return st;
-  const unsigned short* O[kMaxGemmGroups];
-  int64_t ldo[kMaxGemmGroups];
-  const float* oscale[kMaxGemmGroups];
-  st = run_ns(ph, hp, ws, s, O, ldo, oscale);
-  if (st != MA_OK) return st;
-  const hipError_t e = launch_ns_extract(p, out, O[0], oscale[0], ldo[0], s);
-  if (e != hipSuccess) return hip_fail(e, "extract launch");
-  return MA_OK;
+  return newton_schulz_body(p, in, out, hp, static_cast<char*>(workspace),
+                            static_cast<hipStream_t>(stream));
 }
 
 ma_status ma_muon_tune(const ma_muon_bucket* buckets, int32_t n_buckets,
@@ -786,6 +992,133 @@ ma_status ma_muon_tune(const ma_muon_bucket* buckets, int32_t n_buckets,
 void ma_muon_tune_reset(void) {
   std::lock_guard<std::mutex> lock(g_tune_mu);
   g_tune.clear();
+}
+
+ma_status ma_muon_check_plan(const ma_muon_bucket* buckets, int32_t n_buckets,
+                             const ma_muon_hparams* hp, int32_t what, ma_plan_report* out) {
+  g_last_error.clear();
+  if (what != 0 && what != 1) return fail(MA_ERR_INVALID_ARG, "what %d is not 0 or 1", what);
+  if (n_buckets < 0) return fail(MA_ERR_INVALID_ARG, "n_buckets %d < 0", n_buckets);
+  if (n_buckets > 0 && !buckets) return fail(MA_ERR_INVALID_ARG, "buckets is NULL");
+  if (what == 1 && n_buckets < 1) return fail(MA_ERR_INVALID_ARG, "no bucket to orthogonalise");
+  // synthetic, disjoint, 256-byte aligned tensors and workspace (never dereferenced)
+  std::vector<ma_muon_bucket> bk(static_cast<size_t>(n_buckets));
+  uintptr_t addr = uintptr_t(1) << 44;
+  auto take = [&](int64_t bytes) {
+    const uintptr_t a = addr;
+    addr += (static_cast<uintptr_t>(bytes) + 511) & ~static_cast<uintptr_t>(255);
+    return a;
+  };
+  for (int32_t i = 0; i < n_buckets; ++i) {
+    bk[i] = ma_muon_bucket{buckets[i].K, buckets[i].A, buckets[i].B, nullptr, nullptr, nullptr};
+    const ma_status st = check_shape(bk[i].K, bk[i].A, bk[i].B);
+    if (st != MA_OK) return fail(st, "bucket %d: %s", i, g_last_error.c_str());
+    if (bk[i].K == 0) continue;
+    const int64_t bytes = bk[i].K * bk[i].A * bk[i].B * 4;
+    bk[i].param = reinterpret_cast<float*>(take(bytes));
+    bk[i].grad = reinterpret_cast<const float*>(take(bytes));
+    bk[i].momentum = reinterpret_cast<float*>(take(bytes));
+  }
+  ma_status st = what == 0 ? check_step_args(bk.data(), n_buckets, hp) : check_hparams(hp);
+  if (st != MA_OK) return st;
+  PlanChecker chk;
+  struct Install {
+    explicit Install(LaunchRecorder* r) { launch_recorder() = r; }
+    ~Install() { launch_recorder() = nullptr; }
+  } install(&chk);
+  const uintptr_t ws = take(0);
+  if (what == 0) {
+    const size_t need = ma_muon_workspace_bytes(bk.data(), n_buckets, hp);
+    st = for_each_phase(bk.data(), n_buckets, hp->ns_mode, [&](const Phase& ph) -> ma_status {
+      chk.set_phase(ph, ws, need, bk.data(), true);
+      if (chk.error.empty()) {
+        const ma_status s2 = run_phase(ph, bk.data(), hp, reinterpret_cast<char*>(ws), nullptr);
+        if (s2 != MA_OK) return s2;
+      }
+      return chk.error.empty() ? MA_OK : MA_ERR_INTERNAL;
+    });
+  } else if (bk[0].K > 0) {
+    const ma_muon_bucket& b = bk[0];
+    const BucketPlan p = plan_bucket(b.K, b.A, b.B, 0, wants_gram_space(hp->ns_mode, b.A, b.B));
+    Phase ph;
+    phase_add(ph, p, 0);
+    chk.set_phase(ph, ws, p.bytes, bk.data(), false);
+    if (chk.error.empty()) {
+      // in = the gradient, out = the parameter tensor
+      st = newton_schulz_body(p, b.grad, b.param, hp, reinterpret_cast<char*>(ws), nullptr);
+      if (st != MA_OK) return st;
+    }
+    if (!chk.error.empty()) st = MA_ERR_INTERNAL;
+  }
+  if (st == MA_ERR_INTERNAL || !chk.error.empty())
+    return fail(MA_ERR_INTERNAL, "plan check: %s", chk.error.c_str());
+  if (st != MA_OK) return st;
+  if (out) *out = ma_plan_report{chk.launches, chk.gemm_blocks, chk.tiles};
+  return MA_OK;
+}
+
+ma_status ma_muon_ns_time(const ma_muon_bucket* buckets, int32_t n_buckets,
+                          const ma_muon_hparams* hp, void* workspace, size_t workspace_bytes,
+                          void* stream, int32_t reps, float* phase_ms) {
+  g_last_error.clear();
+  ma_status st = check_hparams(hp);
+  if (st != MA_OK) return st;
+  if (n_buckets < 0) return fail(MA_ERR_INVALID_ARG, "n_buckets %d < 0", n_buckets);
+  if (n_buckets > 0 && !buckets) return fail(MA_ERR_INVALID_ARG, "buckets is NULL");
+  if (reps < 1 || reps > 1000) return fail(MA_ERR_INVALID_ARG, "reps %d outside [1, 1000]", reps);
+  if (!phase_ms) return fail(MA_ERR_INVALID_ARG, "phase_ms is NULL");
+  for (int32_t i = 0; i < n_buckets; ++i) {
+    st = check_shape(buckets[i].K, buckets[i].A, buckets[i].B);
+    if (st != MA_OK) return fail(st, "bucket %d: %s", i, g_last_error.c_str());
+    if (buckets[i].K > 0 && (!buckets[i].grad || (reinterpret_cast<uintptr_t>(buckets[i].grad) & 3u)))
+      return fail(MA_ERR_INVALID_ARG, "bucket %d: gradient NULL or not 4-byte aligned", i);
+  }
+  const size_t need = ma_muon_workspace_bytes(buckets, n_buckets, hp);
+  if (need > 0) {
+    if (!workspace) return fail(MA_ERR_WORKSPACE, "workspace is NULL, %zu bytes needed", need);
+    if (reinterpret_cast<uintptr_t>(workspace) & 255u)
+      return fail(MA_ERR_WORKSPACE, "workspace must be 256-byte aligned");
+    if (workspace_bytes < need)
+      return fail(MA_ERR_WORKSPACE, "workspace has %zu bytes, %zu needed", workspace_bytes, need);
+  }
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  char* ws = static_cast<char*>(workspace);
+  hipEvent_t e0 = nullptr, e1 = nullptr;
+  hipError_t he = hipEventCreate(&e0);
+  if (he == hipSuccess) he = hipEventCreate(&e1);
+  if (he != hipSuccess) {
+    if (e0) (void)hipEventDestroy(e0);
+    return hip_fail(he, "event create");
+  }
+  int phase = 0;
+  st = for_each_phase(buckets, n_buckets, hp->ns_mode, [&](const Phase& ph) -> ma_status {
+    double total = 0.0;
+    for (int r = 0; r < reps; ++r) {
+      for (int j = 0; j < ph.n; ++j) {
+        const ma_status s2 = prep_bucket(ph.plan[j], buckets[ph.bucket[j]].grad, nullptr, hp,
+                                         ws + ph.base[j], s);
+        if (s2 != MA_OK) return s2;
+      }
+      const unsigned short* O[kMaxGemmGroups];
+      int64_t ldo[kMaxGemmGroups];
+      const float* oscale[kMaxGemmGroups];
+      hipError_t e = hipEventRecord(e0, s);
+      if (e != hipSuccess) return hip_fail(e, "event record");
+      const ma_status s2 = run_ns(ph, hp, ws, s, O, ldo, oscale);
+      if (s2 != MA_OK) return s2;
+      e = hipEventRecord(e1, s);
+      if (e == hipSuccess) e = hipEventSynchronize(e1);
+      float ms = 0.0f;
+      if (e == hipSuccess) e = hipEventElapsedTime(&ms, e0, e1);
+      if (e != hipSuccess) return hip_fail(e, "timing");
+      total += ms;
+    }
+    phase_ms[phase++] = static_cast<float>(total / reps);
+    return MA_OK;
+  });
+  (void)hipEventDestroy(e0);
+  (void)hipEventDestroy(e1);
+  return st;
 }
 
 ma_status ma_adamw_step(float* param, const float* grad, float* exp_avg, float* exp_avg_sq,

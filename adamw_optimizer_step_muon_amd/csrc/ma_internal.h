@@ -37,8 +37,9 @@ struct BucketPlan {
   int tile;  // square GEMM tile (128 or 256); m and n are padded to it
   int64_t m, n, m_pad, n_pad;
   int64_t nblk;  // momentum/cast tiles per matrix (one partial sum of U^2 each)
-  // byte offsets inside the workspace
-  size_t off_x[2], off_r, off_p, off_part, off_inv, bytes;
+  // byte offsets inside the workspace: X ping-pong, R, P, per-tile fp64 sums of U^2,
+  // per-matrix 1 / (||U|| + eps) (fp32) and power-of-two shift of X (int32)
+  size_t off_x[2], off_r, off_p, off_part, off_inv, off_shift, bytes;
   // buckets with 256-tiles and a Gram side above 2048 also keep X^T (n_pad x m_pad),
   // which their combine reads
   bool keeps_xt;
@@ -52,8 +53,9 @@ struct BucketPlan {
 // Plan of one bucket on the given GEMM tile (128 or 256), or on pick_tile's choice
 // (tile 0); MA_NS_TILE, when set to 128 or 256, overrides either.
 BucketPlan plan_bucket(int64_t K, int64_t A, int64_t B, int tile = 0, bool gram_space = false);
-// Whether a bucket runs the Gram-space iteration under ns_mode: 1 asks for it where the
-// long side is at least twice the Gram side.
+// Whether a bucket runs the Gram-space iteration under ns_mode: 1 asks for it on wide
+// buckets (A < B) with B >= 2 A and A <= kGramSpaceMaxM.
+constexpr int64_t kGramSpaceMaxM = 1024;
 bool wants_gram_space(int32_t ns_mode, int64_t A, int64_t B);
 // Whether GEMM launches holding `tri` lower-triangle and `comb` combine tiles of
 // 256 x 256 fill the chip well enough for 256-tiles.
@@ -80,11 +82,16 @@ struct NsCoeffs {
 // orientation copy S (Ap x Bp) and/or the transposed copy T (Bp x Ap) (either may be
 // null), zero in the padding; per-tile sums of U^2.
 hipError_t launch_muon_prep(const BucketPlan& p, const float* G, float* M, float mu,
-                            int nesterov, float* partials, unsigned short* S,
+                            int nesterov, double* partials, unsigned short* S,
                             unsigned short* T, hipStream_t s);
-// inv[k] = 1 / (sqrt(sum of partials of matrix k) + eps)
-hipError_t launch_norm_finalize(const BucketPlan& p, const float* partials, float eps,
-                                float* inv, hipStream_t s);
+// inv[k] = 1 / (sqrt(sum of partials of matrix k) + eps), shift[k] = 0; for a norm
+// outside [2^-32, 2^32], shift[k] = -e and inv[k] = 2^e / (norm + eps) (e its exponent)
+hipError_t launch_norm_finalize(const BucketPlan& p, const double* partials, float eps,
+                                float* inv, int* shift, hipStream_t s);
+// S and T (m_pad x n_pad bf16 per matrix, either may be null) *= 2^shift[k] where
+// shift[k] != 0, so that inv[k] * X is still X0 = U / (||U|| + eps)
+hipError_t launch_rescale(const BucketPlan& p, unsigned short* S, unsigned short* T,
+                          const int* shift, hipStream_t s);
 // Newton-Schulz products over a group of up to kMaxGemmGroups buckets with the same
 // tile, one launch per product for the whole group.
 constexpr int kMaxGemmGroups = 4;
@@ -98,6 +105,142 @@ struct NsGroup {
   unsigned short* R;    // m_pad x m_pad
   unsigned short* P;
 };
+// One Newton-Schulz GEMM launch: its arguments are read by the kernel in place from the
+// kernel-argument segment (see ns_gemm.hip), so the table must fit there.
+enum Epi { kGram = 0, kPoly = 1, kCombine = 2 };
+
+struct GemmArgs {
+  const unsigned short* A;
+  const unsigned short* B;
+  int64_t lda, ldb, strideA, strideB;
+  int kdim;
+  unsigned short* C;    // row-major target
+  unsigned short* C2;   // transposed target (combine) or mirror target (gram/poly); the
+                        // combine may leave either C or C2 null
+  int64_t ldc, ldc2, strideC, strideC2;
+  const unsigned short* aux;  // poly: R, source of the b R term (read transposed)
+  int64_t ldaux, strideAux;
+  float alpha, beta, diag;  // poly: P = alpha R + beta R R^T + diag I
+  const float* scale;   // per-matrix factor or null: gram R *= scale^2, combine X' *= scale
+  int tiles_m, tiles_n; // tile grid (triangular for gram/poly)
+  int tiles_per_batch;
+  int tiles_k;          // matrices in the group (host side: block count = tiles_k x tiles_per_batch)
+  int band;             // tile rows per L2 band (tile order; 0: plain row-major triangle)
+  int xcd_remap;        // 1: renumber blocks XCD by XCD
+  int spread;           // 1: spread the next stage's DMAs over the first half-stage
+  int symmetrize;       // gram with A != B: copy each diagonal tile's lower triangle up
+};
+
+// Up to kMaxGroups buckets (same tile shape) share one launch: block b belongs to the
+// group g with start[g] <= b' < start[g+1], b' the XCD-remapped block id.
+struct GemmTable {
+  GemmArgs g[kMaxGemmGroups];
+  int start[kMaxGemmGroups + 1];
+  int ngroups;
+};
+static_assert(sizeof(GemmTable) <= 2048, "GemmTable is passed whole as the kernel argument");
+static_assert(offsetof(GemmTable, g) == 0, "the kernel reads the table at the segment start");
+
+// Block id -> logical id so that each XCD's blocks (bid % 8) are a contiguous run.
+__host__ __device__ __forceinline__ int xcd_linear(int bid, int nblocks) {
+  constexpr int kXcd = 8;
+  const int q = nblocks / kXcd, r = nblocks % kXcd;
+  const int xcd = bid % kXcd, local = bid / kXcd;
+  return xcd < r ? xcd * (q + 1) + local : r * (q + 1) + (xcd - r) * q + local;
+}
+
+// The output tile block `bid` of a launch computes: its group gi, matrix `batch`, tile row
+// ti and tile column tj; false for a padding block (which exits at once).  Groups start
+// on multiples of 8 blocks, so a group's blocks keep the round-robin XCD pattern; inside
+// a group the blocks are renumbered so each XCD owns a contiguous run of tiles, in bands
+// of `band` row panels (the combine: column by column inside a band; the symmetric
+// products: the lower triangle band by band).  Used by the kernel and by the host-side
+// plan check, which enumerates every block of every launch.
+__host__ __device__ __forceinline__ bool gemm_block_tile(const GemmTable& t, int epi, int bid,
+                                                         int& gi, int64_t& batch, int& ti,
+                                                         int& tj) {
+  gi = 0;
+#pragma unroll
+  for (int i = 1; i < kMaxGemmGroups; ++i)
+    if (i < t.ngroups && bid >= t.start[i]) gi = i;
+  const GemmArgs& args = t.g[gi];
+  const int g0 = t.start[gi];
+  const int gcount = args.tiles_per_batch * args.tiles_k;
+  const int raw = bid - g0;
+  const int lid = args.xcd_remap ? xcd_linear(raw, (gcount + 7) & ~7) : raw;
+  if (lid >= gcount) return false;
+  batch = lid / args.tiles_per_batch;
+  const int tile = lid - static_cast<int>(batch) * args.tiles_per_batch;
+  if (epi == kCombine) {
+    // bands of `band` row panels; inside a band, column-major over tiles
+    const int G = args.band;
+    const int per_band = G * args.tiles_n;
+    const int b = tile / per_band;
+    const int first = b * G;
+    const int rows = (args.tiles_m - first) < G ? (args.tiles_m - first) : G;
+    const int in = tile - b * per_band;
+    ti = first + in % rows;
+    tj = in / rows;
+  } else if (args.band > 0) {
+    // lower triangle in bands of G tile rows [r0, r1); inside a band, column by column
+    // (the r0 full-height columns, then the band's own triangle), so the blocks that
+    // run together share G row panels and a few column panels
+    const int G = args.band, T = args.tiles_m;
+    int r0 = 0, u = tile;
+    for (;;) {
+      const int r1 = (r0 + G) < T ? (r0 + G) : T, h = r1 - r0;
+      const int cnt = r0 * h + h * (h + 1) / 2;
+      if (u < cnt) {
+        if (u < r0 * h) {
+          tj = u / h;
+          ti = r0 + (u - tj * h);
+        } else {
+          int v = u - r0 * h, c = 0;
+          while (v >= h - c) { v -= h - c; ++c; }
+          tj = r0 + c;
+          ti = tj + v;
+        }
+        break;
+      }
+      u -= cnt;
+      r0 = r1;
+    }
+  } else {
+    // lower-triangle enumeration: tile = ti (ti + 1) / 2 + tj, tj <= ti
+    ti = static_cast<int>((__builtin_sqrtf(8.0f * tile + 1.0f) - 1.0f) * 0.5f);
+    while ((ti + 1) * (ti + 2) / 2 <= tile) ++ti;
+    while (ti * (ti + 1) / 2 > tile) --ti;
+    tj = tile - ti * (ti + 1) / 2;
+  }
+  return true;
+}
+
+// Compiled GEMM configurations: 128 x 128 tiles; 256 x 256 reading X^T in the combine;
+// 256 x 256 whose combine reads X (transposing LDS loads); 192 x 256 combine tiles.
+enum TileCfg { kTileSmall = 0, kTileBig = 1, kTileBigX = 2, kTileMidX = 3 };
+struct TileShape {
+  int bm, bn, bk;
+  bool combine_reads_x;  // the combine's B operand is X (k rows), not X^T
+};
+TileShape tile_shape(TileCfg cfg);
+
+// Dry run: while a recorder is installed on the calling thread, every launcher hands its
+// launch to the recorder and returns hipSuccess without touching the GPU (the host-side
+// plan check replays a step this way).
+struct LaunchRecorder {
+  virtual ~LaunchRecorder() = default;
+  virtual void gemm(int epi, TileCfg cfg, const GemmTable& t) = 0;
+  virtual void prep(const BucketPlan& p, const float* G, const float* M, const double* partials,
+                    const unsigned short* S, const unsigned short* T) = 0;
+  virtual void norm(const BucketPlan& p, const double* partials, const float* inv,
+                    const int* shift) = 0;
+  virtual void rescale(const BucketPlan& p, const unsigned short* S, const unsigned short* T,
+                       const int* shift) = 0;
+  virtual void apply(const BucketPlan& p, const float* out, const unsigned short* O,
+                     const float* oscale, int64_t ldo) = 0;
+};
+LaunchRecorder*& launch_recorder();
+
 // GEMM tiles: `tile` (and `tile_choice`) 0 takes the default for the phase; 128 or 256
 // picks that tile (256 only on a 256-padded phase; the combine of a phase that keeps
 // X^T always runs its own 256-tile configuration), and the combine also takes 192

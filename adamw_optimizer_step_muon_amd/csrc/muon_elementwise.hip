@@ -9,24 +9,26 @@
 //              scalar per matrix, applied by the first Newton-Schulz products
 //              (R = inv^2 U U^T, X1 = inv (a U + P U)), which is X0 = inv U up to the
 //              order of rounding, and saves a second pass over G and M.
-//   finalize:  inv = 1 / (||U||_F + eps), one value per matrix, fixed summation order
+//   finalize:  inv = 1 / (||U||_F + eps), one value per matrix, fixed summation order;
+//              the tile sums are float64, so ||U|| is exact to rounding for any finite
+//              fp32 U.  A matrix whose norm lies outside [2^-32, 2^32] has its bf16 copy
+//              multiplied by 2^-e (e = the exponent of its norm: exact, a power of two)
+//              and inv by 2^e, so the first Gram product accumulates values of order one
+//              in fp32 (unscaled, its sums would overflow above ~1e19 or lose their
+//              small terms below ~1e-19); inside the range nothing is rescaled.
 //   apply:     P <- P - lr wd [mask] P - lr s O   ("dtensor-muon", "Features": the
 //              cautious mask keeps the decay only where update and weight share a sign)
 //
 // Reductions are deterministic: every partial sum has a fixed owner and a fixed
 // order, so a matrix's result does not depend on which bucket it is in.
+#include <algorithm>
+
 #include "ma_internal.h"
 
 namespace ma {
 namespace {
 
 constexpr int kThreads = 256;
-
-__device__ __forceinline__ float wave_sum(float x) {
-#pragma unroll
-  for (int off = 32; off > 0; off >>= 1) x += __shfl_xor(x, off, 64);
-  return x;
-}
 
 __device__ __forceinline__ double wave_sum_d(double x) {
 #pragma unroll
@@ -46,10 +48,10 @@ template <bool kVec, bool kHasM>
 __global__ __launch_bounds__(kThreads) void muon_prep_kernel(
     const float* __restrict__ G, float* __restrict__ M, float mu, int nesterov, int64_t A,
     int64_t B, int64_t Ap, int64_t Bp, unsigned short* __restrict__ S,
-    unsigned short* __restrict__ T, float* __restrict__ partials) {
+    unsigned short* __restrict__ T, double* __restrict__ partials) {
   constexpr int kT = kCastTile;
   __shared__ unsigned short tile[kT][kT + 4];
-  __shared__ float red[kThreads / 64];
+  __shared__ double red[kThreads / 64];
   const int64_t k = blockIdx.z;
   const int64_t a0 = static_cast<int64_t>(blockIdx.y) * kT;
   const int64_t b0 = static_cast<int64_t>(blockIdx.x) * kT;
@@ -58,7 +60,7 @@ __global__ __launch_bounds__(kThreads) void muon_prep_kernel(
   unsigned short* s = S ? S + k * Ap * Bp : nullptr;
   unsigned short* t = T ? T + k * Ap * Bp : nullptr;
   const int c4 = (threadIdx.x & 15) * 4;
-  float ss = 0.0f;
+  double ss = 0.0;
 #pragma unroll
   for (int r = 0; r < 4; ++r) {
     const int row = (threadIdx.x >> 4) + 16 * r;
@@ -97,7 +99,8 @@ __global__ __launch_bounds__(kThreads) void muon_prep_kernel(
         }
       }
     }
-    ss += u[0] * u[0] + u[1] * u[1] + u[2] * u[2] + u[3] * u[3];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) ss = __builtin_fma(static_cast<double>(u[e]), static_cast<double>(u[e]), ss);
     unsigned short h[4];
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
@@ -109,11 +112,11 @@ __global__ __launch_bounds__(kThreads) void muon_prep_kernel(
     packed[1] = static_cast<unsigned>(h[2]) | (static_cast<unsigned>(h[3]) << 16);
     if (s) *reinterpret_cast<u32x2*>(s + a * Bp + b) = packed;
   }
-  ss = wave_sum(ss);
+  ss = wave_sum_d(ss);
   if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = ss;
   __syncthreads();
   if (threadIdx.x == 0) {
-    float tot = 0.0f;
+    double tot = 0.0;
 #pragma unroll
     for (int w = 0; w < kThreads / 64; ++w) tot += red[w];
     partials[k * gridDim.x * gridDim.y + blockIdx.y * gridDim.x + blockIdx.x] = tot;
@@ -131,9 +134,12 @@ __global__ __launch_bounds__(kThreads) void muon_prep_kernel(
   }
 }
 
-// grid (K); inv[k] = 1 / (sqrt(sum of matrix k's partials) + eps)
+// grid (K); inv[k] = 1 / (sqrt(sum of matrix k's partials) + eps) and shift[k] = 0, or,
+// for a finite nonzero norm outside [2^-32, 2^32] with exponent e (norm = f 2^e,
+// 1 <= f < 2), inv[k] = 2^e / (norm + eps) and shift[k] = -e
 __global__ __launch_bounds__(kThreads) void norm_finalize_kernel(
-    const float* __restrict__ partials, int64_t nblk, float eps, float* __restrict__ inv) {
+    const double* __restrict__ partials, int64_t nblk, float eps, float* __restrict__ inv,
+    int* __restrict__ shift) {
   const int64_t k = blockIdx.x;
   double acc = 0.0;
   for (int64_t i = threadIdx.x; i < nblk; i += kThreads) acc += partials[k * nblk + i];
@@ -145,7 +151,44 @@ __global__ __launch_bounds__(kThreads) void norm_finalize_kernel(
     double t = 0.0;
 #pragma unroll
     for (int w = 0; w < kThreads / 64; ++w) t += red[w];
-    inv[k] = static_cast<float>(1.0 / (__builtin_sqrt(t) + static_cast<double>(eps)));
+    const double norm = __builtin_sqrt(t);
+    double iv = 1.0 / (norm + static_cast<double>(eps));
+    int sh = 0;
+    if ((norm > 0.0 && norm < 0x1p-32) || (norm > 0x1p32 && norm <= 1.7976931348623157e308)) {
+      // exponent of a normal double (every nonzero norm of fp32 values is one)
+      const int e = static_cast<int>((__builtin_bit_cast(unsigned long long, norm) >> 52) & 0x7ff) - 1023;
+      iv = __builtin_ldexp(iv, e);
+      sh = -e;
+    }
+    inv[k] = static_cast<float>(iv);
+    shift[k] = sh;
+  }
+}
+
+// grid (nb, K): the `per` bf16 values of matrix k in X and in Y (either may be null) are
+// multiplied by 2^shift[k] where shift[k] != 0 (exact, up to values that leave the
+// normal range); per % 8 == 0
+__global__ __launch_bounds__(kThreads) void rescale_kernel(unsigned short* __restrict__ X,
+                                                           unsigned short* __restrict__ Y,
+                                                           int64_t per, const int* __restrict__ shift) {
+  const int64_t k = blockIdx.y;
+  const int sh = shift[k];
+  if (sh == 0) return;
+  for (int b = 0; b < 2; ++b) {
+    unsigned short* base = b == 0 ? X : Y;
+    if (!base) continue;
+    u32x4* q = reinterpret_cast<u32x4*>(base + k * per);
+    for (int64_t i = static_cast<int64_t>(blockIdx.x) * kThreads + threadIdx.x; i < per / 8;
+         i += static_cast<int64_t>(gridDim.x) * kThreads) {
+      u32x4 v = q[i];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const unsigned lo = f2bf(__builtin_ldexpf(bf2f(static_cast<unsigned short>(v[e] & 0xffffu)), sh));
+        const unsigned hi = f2bf(__builtin_ldexpf(bf2f(static_cast<unsigned short>(v[e] >> 16)), sh));
+        v[e] = lo | (hi << 16);
+      }
+      q[i] = v;
+    }
   }
 }
 
@@ -201,8 +244,12 @@ bool aligned16(const void* q) { return (reinterpret_cast<uintptr_t>(q) & 15u) ==
 }  // namespace
 
 hipError_t launch_muon_prep(const BucketPlan& p, const float* G, float* M, float mu,
-                            int nesterov, float* partials, unsigned short* S,
+                            int nesterov, double* partials, unsigned short* S,
                             unsigned short* T, hipStream_t s) {
+  if (LaunchRecorder* r = launch_recorder()) {
+    r->prep(p, G, M, partials, S, T);
+    return hipSuccess;
+  }
   const int64_t Ap = p.transposed ? p.n_pad : p.m_pad;
   const int64_t Bp = p.transposed ? p.m_pad : p.n_pad;
   const bool vec = (p.B % 4 == 0) && aligned16(G) && (!M || aligned16(M));
@@ -226,10 +273,28 @@ hipError_t launch_muon_prep(const BucketPlan& p, const float* G, float* M, float
   return hipGetLastError();
 }
 
-hipError_t launch_norm_finalize(const BucketPlan& p, const float* partials, float eps,
-                                float* inv, hipStream_t s) {
+hipError_t launch_norm_finalize(const BucketPlan& p, const double* partials, float eps,
+                                float* inv, int* shift, hipStream_t s) {
+  if (LaunchRecorder* r = launch_recorder()) {
+    r->norm(p, partials, inv, shift);
+    return hipSuccess;
+  }
   hipLaunchKernelGGL(norm_finalize_kernel, dim3(static_cast<unsigned>(p.K)), dim3(kThreads), 0,
-                     s, partials, p.nblk, eps, inv);
+                     s, partials, p.nblk, eps, inv, shift);
+  return hipGetLastError();
+}
+
+hipError_t launch_rescale(const BucketPlan& p, unsigned short* S, unsigned short* T,
+                          const int* shift, hipStream_t s) {
+  if (LaunchRecorder* r = launch_recorder()) {
+    r->rescale(p, S, T, shift);
+    return hipSuccess;
+  }
+  // a few blocks per matrix: in-range matrices (the usual case) return at once
+  const int64_t per = p.m_pad * p.n_pad;
+  const int64_t nb = std::min<int64_t>(64, (per / 8 + kThreads - 1) / kThreads);
+  hipLaunchKernelGGL(rescale_kernel, dim3(static_cast<unsigned>(nb), static_cast<unsigned>(p.K)),
+                     dim3(kThreads), 0, s, S, T, per, shift);
   return hipGetLastError();
 }
 
@@ -239,6 +304,10 @@ hipError_t launch_apply_impl(const BucketPlan& p, float* param, const unsigned s
                              int cautious, bool extract, hipStream_t s) {
   const int64_t total = p.K * p.A * p.B;
   if (total == 0) return hipSuccess;
+  if (LaunchRecorder* r = launch_recorder()) {
+    r->apply(p, param, O, oscale, ldo);
+    return hipSuccess;
+  }
   const int64_t slab = p.m_pad * p.n_pad;
   const bool vec = (p.B % 4 == 0) && aligned16(param) && (ldo % 4 == 0);
   const int64_t per_thread = vec ? 4 : 1;

@@ -59,38 +59,6 @@ __device__ void raw_buffer_load_lds(i32x4 rsrc, __attribute__((address_space(3))
 namespace ma {
 namespace {
 
-enum Epi { kGram = 0, kPoly = 1, kCombine = 2 };
-
-struct GemmArgs {
-  const unsigned short* A;
-  const unsigned short* B;
-  int64_t lda, ldb, strideA, strideB;
-  int kdim;
-  unsigned short* C;    // row-major target
-  unsigned short* C2;   // transposed target (combine) or mirror target (gram/poly); the
-                        // combine may leave either C or C2 null
-  int64_t ldc, ldc2, strideC, strideC2;
-  const unsigned short* aux;  // poly: R, source of the b R term (read transposed)
-  int64_t ldaux, strideAux;
-  float alpha, beta, diag;  // poly: P = alpha R + beta R R^T + diag I
-  const float* scale;   // per-matrix factor or null: gram R *= scale^2, combine X' *= scale
-  int tiles_m, tiles_n; // tile grid (triangular for gram/poly)
-  int tiles_per_batch;
-  int tiles_k;          // matrices in the group (host side: block count = tiles_k x tiles_per_batch)
-  int band;             // tile rows per L2 band (tile order; 0: plain row-major triangle)
-  int xcd_remap;        // 1: renumber blocks XCD by XCD
-  int spread;           // 1: spread the next stage's DMAs over the first half-stage
-  int symmetrize;       // gram with A != B: copy each diagonal tile's lower triangle up
-};
-
-// Up to kMaxGroups buckets (same tile shape) share one launch: block b belongs to the
-// group g with start[g] <= b' < start[g+1], b' the XCD-remapped block id.
-struct GemmTable {
-  GemmArgs g[kMaxGemmGroups];
-  int start[kMaxGemmGroups + 1];
-  int ngroups;
-};
-
 template <int BM_, int BN_, int BK_, int WM_, int WN_, int STAGES_, bool READS_X_,
           int BSTAGES_ = STAGES_>
 struct Cfg {
@@ -218,14 +186,6 @@ __device__ __forceinline__ void dma16(const unsigned short* base, int voff, unsi
   }
 }
 
-// Block id -> logical id so that each XCD's blocks (bid % 8) are a contiguous run.
-__device__ __forceinline__ int xcd_linear(int bid, int nblocks) {
-  constexpr int kXcd = 8;
-  const int q = nblocks / kXcd, r = nblocks % kXcd;
-  const int xcd = bid % kXcd, local = bid / kXcd;
-  return xcd < r ? xcd * (q + 1) + local : r * (q + 1) + (xcd - r) * q + local;
-}
-
 template <class C, int kEpi>
 __global__ __launch_bounds__(C::kThreads) void ns_gemm_kernel(GemmTable table) {
   __shared__ __attribute__((aligned(16))) unsigned short smem[C::kLdsElems];
@@ -240,63 +200,12 @@ __global__ __launch_bounds__(C::kThreads) void ns_gemm_kernel(GemmTable table) {
   const int wm = wave / C::WN;
   const int wn = wave % C::WN;
 
-  // Group by raw block id (group starts are multiples of 8, so a group's blocks keep
-  // the round-robin XCD pattern), then renumber inside the group so each XCD owns a
-  // contiguous run of that group's tiles; padding blocks exit at once.
-  int gi = 0;
-#pragma unroll
-  for (int i = 1; i < kMaxGemmGroups; ++i)
-    if (i < kt->ngroups && static_cast<int>(blockIdx.x) >= kt->start[i]) gi = i;
+  // block -> (group, matrix, tile row, tile column): the same function the host-side
+  // plan check enumerates; padding blocks exit at once
+  int gi, ti, tj;
+  int64_t batch;
+  if (!gemm_block_tile(*kt, kEpi, static_cast<int>(blockIdx.x), gi, batch, ti, tj)) return;
   const GemmArgs args = kt->g[gi];
-  const int g0 = kt->start[gi];
-  const int gcount = args.tiles_per_batch * args.tiles_k;
-  const int raw = static_cast<int>(blockIdx.x) - g0;
-  const int lid = args.xcd_remap ? xcd_linear(raw, (gcount + 7) & ~7) : raw;
-  if (lid >= gcount) return;
-  const int64_t batch = lid / args.tiles_per_batch;
-  const int tile = lid - static_cast<int>(batch) * args.tiles_per_batch;
-  int ti, tj;
-  if (kEpi == kCombine) {
-    // bands of `band` row panels; inside a band, column-major over tiles
-    const int G = args.band;
-    const int per_band = G * args.tiles_n;
-    const int b = tile / per_band;
-    const int first = b * G;
-    const int rows = min(args.tiles_m - first, G);
-    const int in = tile - b * per_band;
-    ti = first + in % rows;
-    tj = in / rows;
-  } else if (args.band > 0) {
-    // lower triangle in bands of G tile rows [r0, r1); inside a band, column by column
-    // (the r0 full-height columns, then the band's own triangle), so the blocks that
-    // run together share G row panels and a few column panels
-    const int G = args.band, T = args.tiles_m;
-    int r0 = 0, u = tile;
-    for (;;) {
-      const int r1 = min(r0 + G, T), h = r1 - r0;
-      const int cnt = r0 * h + h * (h + 1) / 2;
-      if (u < cnt) {
-        if (u < r0 * h) {
-          tj = u / h;
-          ti = r0 + (u - tj * h);
-        } else {
-          int v = u - r0 * h, c = 0;
-          while (v >= h - c) { v -= h - c; ++c; }
-          tj = r0 + c;
-          ti = tj + v;
-        }
-        break;
-      }
-      u -= cnt;
-      r0 = r1;
-    }
-  } else {
-    // lower-triangle enumeration: tile = ti (ti + 1) / 2 + tj, tj <= ti
-    ti = static_cast<int>((__builtin_sqrtf(8.0f * tile + 1.0f) - 1.0f) * 0.5f);
-    while ((ti + 1) * (ti + 2) / 2 <= tile) ++ti;
-    while (ti * (ti + 1) / 2 > tile) --ti;
-    tj = tile - ti * (ti + 1) / 2;
-  }
   const int64_t m0 = static_cast<int64_t>(ti) * C::BM;
   const int64_t n0 = static_cast<int64_t>(tj) * C::BN;
 
@@ -712,7 +621,6 @@ using SmallCfg = Cfg<128, 128, 64, 4, 2, 2, true>;
 // of 768, where three-quarter tiles split the work into rounds of the chip with less
 // left over (the 12-layer GPT: 1296 256-tiles are 5.06 rounds, 1728 192-row tiles 6.75).
 using Mid8X = Cfg<192, 256, 64, 2, 4, 3, true, 2>;
-enum TileCfg { kTileSmall = 0, kTileBig = 1, kTileBigX = 2, kTileMidX = 3 };
 
 template <class C>
 hipError_t launch_cfg(int epi, const GemmTable& t, hipStream_t s) {
@@ -773,6 +681,10 @@ hipError_t launch_table(int epi, GemmTable& t, TileCfg cfg, hipStream_t s) {
   for (int i = 0; i < t.ngroups; ++i)
     t.start[i + 1] = t.start[i] + ((t.g[i].tiles_per_batch * t.g[i].tiles_k + 7) & ~7);
   for (int i = t.ngroups + 1; i <= kMaxGemmGroups; ++i) t.start[i] = t.start[t.ngroups];
+  if (LaunchRecorder* r = launch_recorder()) {
+    r->gemm(epi, cfg, t);
+    return hipSuccess;
+  }
   if (cfg == kTileBig)
     return big_variant() == 1 ? launch_cfg<Big8>(epi, t, s) : launch_cfg<Big8K64>(epi, t, s);
   if (cfg == kTileBigX) return launch_cfg<Big8K64X>(epi, t, s);
@@ -795,6 +707,18 @@ int chosen_tile(const BucketPlan& p, int choice) {
 }
 
 }  // namespace
+
+TileShape tile_shape(TileCfg cfg) {
+  switch (cfg) {
+    case kTileBig:
+      return big_variant() == 1 ? TileShape{Big8::BM, Big8::BN, Big8::BK, Big8::kCombineReadsX}
+                                : TileShape{Big8K64::BM, Big8K64::BN, Big8K64::BK,
+                                            Big8K64::kCombineReadsX};
+    case kTileBigX: return TileShape{Big8K64X::BM, Big8K64X::BN, Big8K64X::BK, Big8K64X::kCombineReadsX};
+    case kTileMidX: return TileShape{Mid8X::BM, Mid8X::BN, Mid8X::BK, Mid8X::kCombineReadsX};
+    default: return TileShape{SmallCfg::BM, SmallCfg::BN, SmallCfg::BK, SmallCfg::kCombineReadsX};
+  }
+}
 
 bool combine_192_ok(const BucketPlan& p) {
   return p.tile == 256 && !p.keeps_xt && p.m_pad % Mid8X::BM == 0;

@@ -48,14 +48,15 @@
 extern "C" {
 #endif
 
-#define MA_ABI_VERSION 2
+#define MA_ABI_VERSION 3
 
 typedef enum {
   MA_OK = 0,
   MA_ERR_INVALID_ARG = -1, /* null pointer, bad size, bad hyperparameter, overlap */
   MA_ERR_UNSUPPORTED = -2, /* valid request outside what this build handles */
   MA_ERR_WORKSPACE = -3,   /* workspace missing, misaligned or too small */
-  MA_ERR_HIP = -4          /* a HIP runtime call or launch failed */
+  MA_ERR_HIP = -4,         /* a HIP runtime call or launch failed */
+  MA_ERR_INTERNAL = -5     /* ma_muon_check_plan found a launch that breaks its plan */
 } ma_status;
 
 /* One shape bucket of Muon matrices [NC]: K matrices of A x B, stacked (K, A, B).
@@ -80,18 +81,21 @@ typedef struct {
   const float* ns_coeffs; /* host, ns_steps x 3 (a, b, c) per iteration; NULL selects
                              the quintic (3.4445, -4.7750, 2.0315) for every iteration */
   int32_t ns_mode;        /* 0: the iteration as printed [HB] (default).
-                             1: Gram-space iteration ([DMuon] section 2.2) for buckets
-                             with n >= 2 m (others as 0): R0 = X0 X0^T once, then per step
-                             P = a I + b R + c R^2, Q <- P Q, R <- P R P on m x m matrices,
+                             1: Gram-space iteration ([DMuon] section 2.2) for wide buckets
+                             (A < B) with B >= 2 A and A <= 1024 (others as 0, reported in
+                             ma_muon_route.ns_mode_run): R0 = X0 X0^T once, then per step
+                             P = a I + b R + c R^2, Q <- P Q, R <- P R P on A x A matrices,
                              and X = Q X0 at the end: 3 m^2 n + ~4 N m^3 instead of
                              N (3 m^2 n + m^3) FLOP for N steps (symmetric counts).  Exact
-                             in real arithmetic; in bf16 its error depends on the input
-                             (R holds squared singular values and the recurrence amplifies
-                             rounding): within 2e-2 of the printed iteration on Gaussian
-                             gradients, on low-rank ones up to Gram sides near 1024 and on
-                             row-scaled gradients of wide matrices; 2e-2 to 5e-2 on
-                             row-scaled tall matrices, low-rank ones with Gram sides of
-                             2560 and condition numbers near 1e4.  Opt-in. */
+                             in real arithmetic; in bf16 its error depends on the input:
+                             R holds squared singular values, whose small end bf16 loses,
+                             and the recurrence carries that loss on.  Inside the domain
+                             it was measured within 2e-2 of the printed iteration on
+                             Gaussian, low-rank and row-scaled gradients, but NOT on
+                             gradients with condition numbers near 1e4 (6e-2 to 1.5e-1 at
+                             every Gram side); tall row-scaled gradients and low-rank ones
+                             with Gram sides from 1536 (2e-2 to 5e-2) are why the domain
+                             stops where it does.  Opt-in, for well-conditioned inputs. */
 } ma_muon_hparams;
 
 #define MA_MAX_NS_STEPS 64
@@ -125,8 +129,9 @@ const char* ma_status_string(int status);
 /* Detail of the last failure on the calling thread ("" if none). */
 const char* ma_last_error(void);
 
-/* Host only: the route one A x B matrix takes (see ma_muon_route).  hp may be NULL
- * (ns_steps 5).  Returns MA_ERR_INVALID_ARG for A < 1, B < 1 or a NULL out. */
+/* Host only: the route one A x B matrix takes (see ma_muon_route) under hp->ns_steps and
+ * hp->ns_mode.  hp may be NULL (ns_steps 5, ns_mode 0).  Returns MA_ERR_INVALID_ARG for
+ * A < 1, B < 1 or a NULL out. */
 ma_status ma_muon_route_of(int64_t A, int64_t B, const ma_muon_hparams* hp, ma_muon_route* out);
 
 /* Host only: workspace bytes ma_muon_step needs for these buckets.  Buckets run in
@@ -238,6 +243,40 @@ ma_status ma_muon_tune(const ma_muon_bucket* buckets, int32_t n_buckets,
 
 /* Host only: forget every tuned or pinned tile (back to the default rules). */
 void ma_muon_tune_reset(void);
+
+/* What ma_muon_check_plan replayed. */
+typedef struct {
+  int64_t launches;     /* kernel launches of the step (or of the orthogonalisation) */
+  int64_t gemm_blocks;  /* Newton-Schulz GEMM blocks enumerated (padding blocks excluded) */
+  int64_t gemm_tiles;   /* output tiles those blocks cover */
+} ma_plan_report;
+
+/* Host only: a dry run of every launch ma_muon_step (what = 0) or ma_newton_schulz
+ * (what = 1, bucket 0 alone) would enqueue for buckets of these shapes under hp and the
+ * tiles this process has tuned or pinned.  The pointers in `buckets` are ignored: the
+ * run uses synthetic addresses and touches no GPU.  Every block of every Newton-Schulz
+ * GEMM launch is mapped to its output tile by the kernel's own block-to-tile function;
+ * its operand reads and result writes must lie inside the workspace buffer (or caller
+ * tensor) its argument addresses, and each output tile of a launch must be computed
+ * exactly once.  The elementwise launches (cast, norm, rescale, update) are checked the
+ * same way.  out (host, may be NULL) receives counts of what was checked.
+ * Errors: MA_ERR_INVALID_ARG (what ma_muon_step would reject), MA_ERR_INTERNAL (a launch
+ * that breaks the plan; ma_last_error() names it). */
+ma_status ma_muon_check_plan(const ma_muon_bucket* buckets, int32_t n_buckets,
+                             const ma_muon_hparams* hp, int32_t what, ma_plan_report* out);
+
+/* A benchmark aid: the time of the Newton-Schulz GEMM launches of ma_muon_step, measured
+ * on the device.  For each phase (ma_muon_phases) and each of `reps` repetitions, the
+ * phase's buckets are cast from their gradients into the workspace as ma_muon_step
+ * would (U = G: gradients are read only; parameters and momenta are not touched and may
+ * be NULL), then the phase's Newton-Schulz launches run between two HIP events on
+ * `stream`.  phase_ms (host, one entry per phase) receives the mean milliseconds per
+ * repetition.  This call SYNCHRONISES with `stream` and creates two HIP events.
+ * Errors: MA_ERR_INVALID_ARG (shapes, hp, NULL gradients, reps outside [1, 1000], NULL
+ * phase_ms), MA_ERR_WORKSPACE, MA_ERR_HIP. */
+ma_status ma_muon_ns_time(const ma_muon_bucket* buckets, int32_t n_buckets,
+                          const ma_muon_hparams* hp, void* workspace, size_t workspace_bytes,
+                          void* stream, int32_t reps, float* phase_ms);
 
 #ifdef __cplusplus
 }

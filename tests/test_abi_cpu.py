@@ -310,11 +310,18 @@ def test_tune_rejects_bad_arguments_before_launch(lib):
 
 
 def test_gram_space_routing_and_workspace(lib):
-    """ns_mode 1 routes buckets whose long side is at least twice the Gram side through
-    the Gram-space iteration, in phases of their own, with four more m x m buffers."""
+    """ns_mode 1 routes wide buckets (A < B) with B >= 2 A and A <= 1024 through the
+    Gram-space iteration, in phases of their own, with four more m x m buffers; tall
+    buckets and wider Gram sides keep the printed iteration."""
     mlp, sq = (12, 768, 3072), (48, 768, 768)
     assert ma.muon_phases([sq, mlp, (12, 3072, 768)]) == (1, [0, 0, 0])
-    assert ma.muon_phases([sq, mlp, (12, 3072, 768)], ns_mode=1) == (2, [0, 1, 1])
+    assert ma.muon_phases([sq, mlp, (12, 3072, 768)], ns_mode=1) == (3, [0, 1, 2])
+    for (A, B), gs in [((768, 3072), 1), ((3072, 768), 0), ((1024, 2048), 1), ((1024, 2047), 0),
+                       ((1025, 4096), 0), ((2048, 4096), 0), ((2560, 5120), 0), ((64, 128), 1),
+                       ((1, 7), 1), ((512, 2048), 1), ((2048, 512), 0), ((768, 768), 0)]:
+        assert ma.muon_route_of(A, B, 5, ns_mode=1).ns_mode_run == gs, (A, B)
+        assert ma.muon_route_of(A, B, 5, ns_mode=0).ns_mode_run == 0
+        assert ma.muon_route_of(A, B, 0, ns_mode=1).ns_mode_run == 0
     m_pad = 768 if not os.environ.get("MA_NS_TILE") else None
     extra = ma.muon_workspace_bytes([mlp], ns_mode=1) - ma.muon_workspace_bytes([mlp])
     if m_pad:

@@ -92,6 +92,53 @@ def test_newton_schulz_printed_spectrum(golden):
     assert abs(frac - float(g["steps5_in_band_pct"][0]) / 100) < 0.05
 
 
+@pytest.mark.parametrize("scale", [1e-30, 1e-20, 1e-12, 1e12, 1e18, 1e30])
+@pytest.mark.parametrize("shape", [(96, 200), (300, 130)])
+def test_newton_schulz_input_range(scale, shape):
+    """Gradients far from unit scale: the Frobenius norm is summed in float64 and a matrix
+    whose norm lies outside [2^-32, 2^32] is rescaled by a power of two before its first
+    product, so the fp32 Gram accumulation neither overflows (entries above ~1e17 would
+    overflow an fp32 tile sum of squares, ~1e19 the Gram itself) nor drops its small
+    terms (below ~1e-19 the squares leave fp32's normal range).  ns_eps = 0, so the
+    normalisation is exactly U / ||U|| at every scale, as in the oracle."""
+    G = (_grad(shape, 31).astype(np.float64) * scale).astype(np.float32)[None]
+    assert np.all(np.isfinite(G))
+    gi = torch.from_numpy(G).to(DEV)
+    go = torch.empty_like(gi)
+    ma.newton_schulz(gi, go, ns_steps=5, ns_eps=0.0)
+    torch.cuda.synchronize()
+    ref = oracle.newton_schulz(G[0], 5, eps=0.0)
+    err = rel_fro(go.cpu().numpy()[0], ref)
+    assert err <= MUON_RTOL, (scale, shape, err)
+
+
+@pytest.mark.parametrize("scale,eps", [(1e18, 1e-7), (1e30, 1e-7), (1e-20, 0.0), (1e-30, 0.0)])
+def test_muon_step_input_range(scale, eps):
+    """The whole Muon step (momentum, norm, Newton-Schulz, update) on gradients 1e-30 to
+    1e30: each step's update against the oracle over two steps (tiny gradients with
+    ns_eps = 0: with 1e-7 the eps would dominate the norm and the update would vanish
+    below fp32's resolution of the parameters, in the oracle as here)."""
+    shapes = [(2, 96, 200), (2, 300, 130)]
+    rng = np.random.default_rng(77)
+    P0 = [rng.standard_normal(s).astype(np.float32) for s in shapes]
+    grads = [[np.stack([(gen.np_grad(77, t, 10 * i + k, s[1:], "rowlognormal", gen.MUON_SIGMA)
+                         .astype(np.float64) * scale).astype(np.float32) for k in range(s[0])])
+              for i, s in enumerate(shapes)] for t in (1, 2)]
+    hist, routes = _muon_run(P0, grads, lr=LR, momentum=MU, weight_decay=WD, ns_eps=eps)
+    ohp = dict(lr=f32(LR), mu=f32(MU), weight_decay=f32(WD), ns_eps=eps)
+    for bi, p0 in enumerate(P0):
+        for k in range(p0.shape[0]):
+            prev, mom = p0[k].astype(np.float64), np.zeros(p0.shape[1:])
+            for t in range(2):
+                gp, gm = hist[t][bi][0][k], hist[t][bi][1][k]
+                ref = oracle.muon_step(prev, grads[t][bi][k], mom, **ohp)
+                assert rel_err_floor(gm, ref.momentum) <= MOMENTUM_RTOL, (scale, bi, k, t)
+                keep = 1.0 - ohp["lr"] * ohp["weight_decay"]
+                err = rel_fro(prev * keep - gp, prev * keep - ref.param)
+                assert err <= MUON_RTOL, (scale, bi, k, t, err)
+                prev, mom = gp.astype(np.float64), ref.momentum
+
+
 # --------------------------------------------------------------------------
 # Muon step
 # --------------------------------------------------------------------------
@@ -293,51 +340,80 @@ def test_optimizer_wrapper_matches_direct_calls():
     assert sd["param_groups"][0]["step"] == 2
 
 
+def _oracle_check_step(prev, g, mom, got_p, got_m, A, B, hp, tol=MUON_RTOL):
+    """One step of one matrix against the oracle stepped from the GPU's previous
+    parameters and the oracle's own momentum; returns the oracle's new momentum."""
+    ref = oracle.muon_step(prev, g, mom, lr=f32(hp.lr), mu=f32(hp.momentum),
+                           weight_decay=f32(hp.weight_decay), cautious_wd=hp.cautious_wd)
+    assert rel_err_floor(got_m, ref.momentum) <= MOMENTUM_RTOL
+    got = got_p.astype(np.float64)
+    if hp.cautious_wd:
+        err, flips = cautious_check(prev, got, ref.ortho, f32(hp.lr), f32(hp.weight_decay),
+                                    oracle.update_scale(A, B), tol)
+        assert flips == 0.0, flips
+    else:
+        keep = 1.0 - f32(hp.lr) * f32(hp.weight_decay)
+        err = rel_fro(prev * keep - got, prev * keep - ref.param)
+    assert err <= tol, err
+    return ref.momentum, err
+
+
 @pytest.mark.parametrize("index", [1, 2, 3])
-def test_muon_full_size_sampled(index):
+def test_muon_full_size_all_steps(index):
     """Every bucket of the workload at full size, in the launch configuration the
-    benchmark times (one ma_muon_step over all buckets); the first and last matrix
-    of each bucket re-computed by the oracle."""
+    benchmark times (one ma_muon_step over all buckets), for the workload's whole step
+    count (10, 10 and 5 steps): the first and last matrix of each bucket (the last only
+    on the 24-layer workload) against the oracle at every step, stepped from the GPU's
+    previous parameters and the oracle's own momentum."""
     wl = workloads.workload(index)
     hp = wl.muon_hp
     ps, gs, ms = [], [], []
     for bi, b in enumerate(wl.muon):
         p = torch.empty((b.K, b.A, b.B), dtype=torch.float32, device=DEV)
         gen.torch_muon_bucket(torch, wl, bi, 0, p)
-        g = torch.empty_like(p)
-        gen.torch_muon_bucket(torch, wl, bi, 1, g)
         ps.append(p)
-        gs.append(g)
+        gs.append(torch.empty_like(p))
         ms.append(torch.zeros_like(p))
     picks = [(bi, k) for bi, b in enumerate(wl.muon) for k in sorted({0, b.K - 1})]
     if index == 3:
         picks = [(bi, b.K - 1) for bi, b in enumerate(wl.muon)]
-    saved = {(bi, k): (ps[bi][k].cpu().numpy().copy(), gs[bi][k].cpu().numpy().copy())
-             for bi, k in picks}
-    routes = ma.muon_step(list(zip(ps, gs, ms)), lr=hp.lr, momentum=hp.momentum,
-                          weight_decay=hp.weight_decay, cautious_wd=hp.cautious_wd)
-    torch.cuda.synchronize()
-    for bi, b in enumerate(wl.muon):
-        o = oracle.route(b.A, b.B)
-        r = routes[bi]
-        assert (r.transposed, r.m, r.n, r.ns_steps_run) == (o.transposed, o.m, o.n, o.ns_steps)
-    for bi, k in picks:
-        b = wl.muon[bi]
-        p0, g1 = saved[(bi, k)]
-        ref = oracle.muon_step(p0, g1, np.zeros_like(p0, dtype=np.float64), lr=f32(hp.lr),
-                               mu=f32(hp.momentum), weight_decay=f32(hp.weight_decay),
-                               cautious_wd=hp.cautious_wd)
-        got = ps[bi][k].cpu().numpy().astype(np.float64)
-        prev = p0.astype(np.float64)
-        if hp.cautious_wd:
-            err, flips = cautious_check(prev, got, ref.ortho, f32(hp.lr), f32(hp.weight_decay),
-                                        oracle.update_scale(b.A, b.B), MUON_RTOL)
-            assert flips == 0.0, (bi, k, flips)
-        else:
-            keep = 1.0 - f32(hp.lr) * f32(hp.weight_decay)
-            err = rel_fro(prev * keep - got, prev * keep - ref.param)
-        assert err <= MUON_RTOL, (bi, k, err)
-        assert rel_err_floor(ms[bi][k].cpu().numpy(), ref.momentum) <= MOMENTUM_RTOL
+    prev = {pk: ps[pk[0]][pk[1]].cpu().numpy().astype(np.float64) for pk in picks}
+    mom = {pk: np.zeros((wl.muon[pk[0]].A, wl.muon[pk[0]].B)) for pk in picks}
+    worst = 0.0
+    for t in range(1, wl.steps + 1):
+        for bi in range(len(wl.muon)):
+            gen.torch_muon_bucket(torch, wl, bi, t, gs[bi])
+        grads = {pk: gs[pk[0]][pk[1]].cpu().numpy() for pk in picks}
+        routes = ma.muon_step(list(zip(ps, gs, ms)), lr=hp.lr, momentum=hp.momentum,
+                              weight_decay=hp.weight_decay, cautious_wd=hp.cautious_wd)
+        torch.cuda.synchronize()
+        for bi, b in enumerate(wl.muon):
+            o = oracle.route(b.A, b.B)
+            r = routes[bi]
+            assert (r.transposed, r.m, r.n, r.ns_steps_run) == (o.transposed, o.m, o.n, o.ns_steps)
+        for bi, k in picks:
+            b = wl.muon[bi]
+            got_p = ps[bi][k].cpu().numpy()
+            mom[(bi, k)], err = _oracle_check_step(prev[(bi, k)], grads[(bi, k)], mom[(bi, k)],
+                                                   got_p, ms[bi][k].cpu().numpy(), b.A, b.B, hp)
+            prev[(bi, k)] = got_p.astype(np.float64)
+            worst = max(worst, err)
+        print(f"workload {index} step {t}: worst update error {worst:.3e}", flush=True)
+
+
+@pytest.mark.parametrize("shapes", [[(6, 4096, 2304), (6, 2304, 4096)], [(6, 4096, 2304)]])
+def test_muon_buckets_that_keep_xt(shapes):
+    """Gram sides above 2048 on 256-tiles keep X^T: the combine reads the stored X^T and
+    the last combine of a transposed bucket writes only X'^T, which the update reads.
+    A transposed 4096 x 2304 bucket (alone, and in one phase with its wide twin) over two
+    steps, first and last matrix of each against the oracle."""
+    for A, B in [(4096, 2304), (2304, 4096)]:
+        assert ma.muon_route_of(A, B).m_pad == 2304
+    assert ma.muon_phases(shapes)[0] == 1
+    P0, grads = _buckets(shapes, 61, 2)
+    hist, routes = _muon_run(P0, grads, lr=LR, momentum=MU, weight_decay=WD)
+    assert [r.m_pad for r in routes] == [2304] * len(shapes)
+    _check_muon(P0, grads, hist, routes, only=[[0, 5]] * len(shapes))
 
 
 @pytest.mark.parametrize("bad", [float("nan"), float("inf")])
@@ -364,3 +440,14 @@ def test_muon_non_finite_gradient_propagates_to_its_matrix_only(bad):
     assert bad_m.sum() == 1 and bad_m[5, 7]
     for k in (0, 2):
         assert np.array_equal(p[k], pc[k]) and np.array_equal(m[k], mc[k])
+
+
+def test_ns_time_reads_gradients_only():
+    """ma_muon_ns_time (the benchmark's Newton-Schulz timer): one positive time per phase,
+    gradients unchanged, and no parameter or momentum touched (none is passed)."""
+    shapes = [(4, 256, 512), (2, 600, 200), (3, 768, 768)]
+    gs = [torch.randn(s, device=DEV) * 0.02 for s in shapes]
+    before = [g.clone() for g in gs]
+    ms = ma.muon_ns_time(gs, reps=2)
+    assert len(ms) == ma.muon_phases(shapes)[0] and all(t > 0 for t in ms)
+    assert all(torch.equal(a, b) for a, b in zip(gs, before))
