@@ -10,7 +10,9 @@ throughput against the bf16 MFMA peak and the AdamW bandwidth against HBM peak, 
 measured with HIP events on the launch stream, plus the fp64 CPU oracle timed on a
 bounded sample of the same workload.
 
-Default workload: index 1, the 12-layer GPT with hidden 768.
+Default workload: index 4, one GPU's owned subset at large shape (8 x 8192x28672,
+8 x 28672x8192 and 16 x 8192x8192 Muon matrices, a 128256x8192 AdamW embedding), the
+largest configuration that fits one GPU; --workload 0-3 select the smaller ones.
 """
 from __future__ import annotations
 
@@ -30,8 +32,13 @@ ADAMW_BYTES_PER_ELEM = 28        # read p, g, m, v; write p, m, v (fp32)
 
 
 def gram_space(b, ns_mode):
-    m, n = min(b.A, b.B), max(b.A, b.B)
-    return ns_mode == 1 and n >= 2 * m
+    """Whether the library runs this bucket's Newton-Schulz in Gram space (its own
+    routing report: wide buckets with n >= 2 m and m <= 2048 under ns_mode 1)."""
+    if ns_mode != 1:
+        return False
+    import adamw_optimizer_step_muon_amd as ma
+
+    return bool(ma.muon_route_of(b.A, b.B, 5, ns_mode=1).ns_mode_run)
 
 
 def ns_flops(wl, steps=None, symmetric=True, ns_mode=0):
@@ -79,7 +86,7 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=2)
-    ap.add_argument("--workload", type=int, default=1)
+    ap.add_argument("--workload", type=int, default=4)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--ns-mode", type=int, default=0, choices=(0, 1),
                     help="1: Gram-space Newton-Schulz for buckets with n >= 2 m (opt-in; its "
@@ -123,14 +130,23 @@ def counted_traffic(summary, source, key="traffic_bytes_per_launch"):
         return None
 
 
+def oracle_cost(b):
+    """Relative cost of the oracle on one A x B matrix: two m^2 n products (the Gram
+    matrix and the final product) and the symmetric eigendecomposition of the m x m
+    Gram matrix, which on the host costs about as much as 10 m^3 of matrix products
+    (measured: 8192 x 8192 and 8192 x 28672 in 46 and 78 s on 8 cores)."""
+    m, n = min(b.A, b.B), max(b.A, b.B)
+    return 4 * m * m * n + 10 * m ** 3
+
+
 def cpu_baseline(wl, budget_s):
     """The fp64 oracle as it stands on the host cores, timed on a bounded sample of one
     step and scaled to the whole step.  About budget_s seconds of oracle work: half on
-    Muon matrices taken round-robin over the buckets (matrix k of every bucket before
-    matrix k + 1 of any), half on AdamW slices of 4M elements.  Each bucket's time is
-    its mean per sampled matrix x K; a bucket the budget never reached is extrapolated
-    from the sampled ones by its dense Newton-Schulz FLOP count, and the sample text
-    says so.  Input generation is not timed."""
+    Muon matrices, taken round-robin over the buckets from the cheapest bucket up
+    (matrix k of every bucket before matrix k + 1 of any), half on AdamW slices of 4M
+    elements.  Each bucket's time is its mean per sampled matrix x K; a bucket the
+    budget never reached is extrapolated from the sampled ones by the oracle's cost
+    model (oracle_cost), and the sample text says so.  Input generation is not timed."""
     import numpy as np
 
     import oracle
@@ -145,8 +161,9 @@ def cpu_baseline(wl, budget_s):
     hp = wl.muon_hp
     nb = len(wl.muon)
     per_t, per_n = [0.0] * nb, [0] * nb
-    order = [(bi, k) for k in range(max(b.K for b in wl.muon)) for bi, b in enumerate(wl.muon)
-             if k < b.K]
+    by_cost = sorted(range(nb), key=lambda bi: oracle_cost(wl.muon[bi]))
+    order = [(bi, k) for k in range(max(b.K for b in wl.muon)) for bi in by_cost
+             if k < wl.muon[bi].K]
     t_muon = 0.0
     for bi, k in order:
         if per_n != [0] * nb and t_muon >= budget_s / 2:
@@ -154,7 +171,7 @@ def cpu_baseline(wl, budget_s):
         b = wl.muon[bi]
         p0 = gen.np_param(wl.seed, gen.muon_index(wl, bi, k), (b.A, b.B))
         g1 = gen.np_grad(wl.seed, 1, gen.muon_index(wl, bi, k), (b.A, b.B), wl.muon_grad,
-                         gen.MUON_SIGMA)
+                         wl.muon_sigma)
         t0 = time.perf_counter()
         oracle.muon_step(p0, g1, np.zeros((b.A, b.B)), lr=hp.lr, mu=hp.momentum,
                          weight_decay=hp.weight_decay, cautious_wd=hp.cautious_wd)
@@ -163,11 +180,7 @@ def cpu_baseline(wl, budget_s):
         per_n[bi] += 1
         t_muon += dt
 
-    def dense(b):
-        m, n = min(b.A, b.B), max(b.A, b.B)
-        return hp.ns_steps * (4 * m * m * n + 2 * m ** 3)
-
-    s_per_flop = sum(per_t) / sum(dense(b) * per_n[i] for i, b in enumerate(wl.muon))
+    s_per_unit = sum(per_t) / sum(oracle_cost(b) * per_n[i] for i, b in enumerate(wl.muon))
     muon_s = 0.0
     parts = []
     for bi, b in enumerate(wl.muon):
@@ -175,8 +188,9 @@ def cpu_baseline(wl, budget_s):
             muon_s += per_t[bi] / per_n[bi] * b.K
             parts.append(f"{per_n[bi]} of {b.K} {b.A}x{b.B}")
         else:
-            muon_s += s_per_flop * dense(b) * b.K
-            parts.append(f"0 of {b.K} {b.A}x{b.B} (extrapolated by FLOP count)")
+            muon_s += s_per_unit * oracle_cost(b) * b.K
+            parts.append(f"0 of {b.K} {b.A}x{b.B} (extrapolated by the oracle's cost model "
+                         "4 m^2 n + 10 m^3)")
     n = wl.adamw_numel
     ah = wl.adamw_hp
     chunk = min(n, 4_000_000)
@@ -271,15 +285,31 @@ def main():
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
+    # the timed region: K steps between two synchronisations, one HIP event between
+    # consecutive steps for the per-step median and minimum
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
+    torch.cuda.synchronize()
     wall0 = time.perf_counter()
-    step_ms = timed(step, args.steps)
+    evs[0].record(stream)
+    for i in range(args.steps):
+        step()
+        evs[i + 1].record(stream)
+    torch.cuda.synchronize()
     wall_s = time.perf_counter() - wall0
+    per_step = sorted(evs[i].elapsed_time(evs[i + 1]) for i in range(args.steps))
+    step_ms = evs[0].elapsed_time(evs[-1]) / args.steps
+    median_ms = per_step[len(per_step) // 2] if len(per_step) % 2 else \
+        0.5 * (per_step[len(per_step) // 2 - 1] + per_step[len(per_step) // 2])
 
     # ---- per-kernel figures, live, same stream ----
-    reps = max(3, args.steps)
+    reps = max(3, min(args.steps, 10))
+    # the Newton-Schulz GEMM launches alone, per phase, between HIP events on the launch
+    # stream (ma_muon_ns_time: each repetition casts the gradients first, untimed)
+    phase_ms = ma.muon_ns_time([b[1] for b in buckets], reps=reps, ns_steps=mh.ns_steps,
+                               ns_eps=mh.ns_eps, ns_mode=args.ns_mode, workspace=ws,
+                               stream=stream)
+    ns_ms = sum(phase_ms)
     muon_ms = timed(lambda: muon(mh.ns_steps), reps)
-    muon0_ms = timed(lambda: muon(0), reps)
-    ns_ms = max(muon_ms - muon0_ms, 1e-9)          # exactly the Newton-Schulz GEMM launches
     # same-tile buckets share launches: 3 x ns_steps per phase of the printed iteration,
     # 4 ns_steps - 1 per Gram-space phase (Gram, polynomials, products, final product)
     phases, phase_of = ma.muon_phases(shapes, args.ns_mode)
@@ -296,6 +326,8 @@ def main():
     state["t"] = 1
     adamw_ms = timed(adamw, reps)
     adamw_gbs = ADAMW_BYTES_PER_ELEM * n / (adamw_ms * 1e-3) / 1e9
+    clock = counted_traffic(f"ns_gemm_mfma_workload{args.workload}.txt", "ns_gemm.hip",
+                            key="clock_ghz")
 
     out = {
         "metric": "optimizer-step ms + NS TFLOP/s (%MFMA peak) + AdamW GB/s (%HBM)",
@@ -315,13 +347,17 @@ def main():
                    "adamw_elements": n, "ns_steps": mh.ns_steps, "ns_mode": args.ns_mode,
                    "cautious_wd": mh.cautious_wd},
         "ns_tiles": ns_tiles,
+        "step_ms_median": round(median_ms, 4),
+        "step_ms_min": round(per_step[0], 4),
         "ns_tflops": round(ns_tflops, 2),
         "ns_mfma_frac": round(ns_tflops / MFMA_BF16_PEAK_TFLOPS, 4),
         "ns_ms": round(ns_ms, 4),
+        "ns_phase_ms": [round(x, 4) for x in phase_ms],
+        "muon_step_ms": round(muon_ms, 4),
         "adamw_ms": round(adamw_ms, 4),
         "adamw_gbs": round(adamw_gbs, 1),
         "adamw_hbm_frac": round(adamw_gbs / HBM_PEAK_GBS, 4),
-        "muon_elementwise_ms": round(muon0_ms, 4),
+        "muon_elementwise_ms": round(max(muon_ms - ns_ms, 0.0), 4),
         "roofline": {
             "kernel": "ns_gemm_kernel (gram, poly, combine launches of Newton-Schulz)",
             "bound": "mfma",
@@ -334,6 +370,12 @@ def main():
             # SQ_VALU_MFMA_BUSY_CYCLES / GRBM_GUI_ACTIVE, at the clock the part ran)
             "mfma_busy_counter": counted_traffic(f"ns_gemm_mfma_workload{args.workload}.txt",
                                                  "ns_gemm.hip", key="mfma_busy"),
+            # the shader clock the GEMM kernels ran at (rocprofv3 GRBM_GUI_ACTIVE per XCD
+            # over the kernel's duration), and the bf16 peak at that clock
+            "clock_ghz_counter": clock,
+            "peak_at_clock": round(MFMA_BF16_PEAK_TFLOPS * clock / 2.4, 1) if clock else None,
+            "frac_at_clock": round(ns_tflops / (MFMA_BF16_PEAK_TFLOPS * clock / 2.4), 4)
+            if clock else None,
             "flops_per_launch": flops / launches,
             "avg_launch_ms": ns_ms / launches,
             # the same launches against both ceilings: algorithmic FLOP per algorithmic HBM

@@ -12,8 +12,16 @@ def test_cpu_baseline_samples_every_bucket_within_budget():
 
 
 def test_cpu_baseline_extrapolates_unsampled_buckets():
-    # a zero budget still times one matrix; the other bucket is scaled by FLOP count
+    # a zero budget still times one matrix (the cheapest bucket first); the other bucket
+    # is scaled by the oracle's cost model
     out = bench.cpu_baseline(workloads.workload(0), budget_s=0.0)
     assert out["value"] > 0
     assert "1 of 1 64x128" in out["sample"]
-    assert "0 of 1 128x64 (extrapolated by FLOP count)" in out["sample"]
+    assert "0 of 1 128x64 (extrapolated by the oracle's cost model" in out["sample"]
+
+
+def test_oracle_cost_orders_the_owner_subset_buckets():
+    """The square 8192 x 8192 bucket is the cheapest to sample; the two rectangular
+    buckets (one the other's transpose) cost the same."""
+    b = workloads.workload(4).muon
+    assert bench.oracle_cost(b[2]) < bench.oracle_cost(b[0]) == bench.oracle_cost(b[1])

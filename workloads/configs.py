@@ -84,6 +84,10 @@ class Workload:
     adamw_grad: str
     muon_hp: MuonHP = field(default_factory=MuonHP)
     adamw_hp: AdamWHP = field(default_factory=AdamWHP)
+    # sigma0 of the gradient recipes: 0.02 for Muon matrices and 1e-3 for AdamW tensors
+    # (the tiny workload's statement), 1e-3 for both where a workload states it
+    muon_sigma: float = 0.02
+    adamw_sigma: float = 1e-3
 
     @property
     def muon_numel(self) -> int:
@@ -99,7 +103,7 @@ class Workload:
 
 
 def _gpt(index, name, layers, hidden, mlp, vocab, steps, seed, muon_grad, adamw_grad,
-         kv=None, cautious=False):
+         kv=None, cautious=False, muon_sigma=0.02):
     """Buckets for a GPT-style stack: attention Q,K,V,O and an up/down MLP."""
     kv = hidden if kv is None else kv
     buckets: List[MuonBucket] = []
@@ -114,7 +118,7 @@ def _gpt(index, name, layers, hidden, mlp, vocab, steps, seed, muon_grad, adamw_
     # two normalisation gains per block plus the final one
     adamw += [AdamWTensor(f"norm{i}", (hidden,)) for i in range(2 * layers + 1)]
     return Workload(index, name, buckets, adamw, steps, seed, muon_grad, adamw_grad,
-                    muon_hp=MuonHP(cautious_wd=cautious))
+                    muon_hp=MuonHP(cautious_wd=cautious), muon_sigma=muon_sigma)
 
 
 WORKLOADS: List[Workload] = [
@@ -124,8 +128,10 @@ WORKLOADS: List[Workload] = [
         [AdamWTensor("vec", (4096,)), AdamWTensor("embedding", (512, 64))],
         steps=3, seed=0, muon_grad="rowlognormal", adamw_grad="gauss",
     ),
+    # gradients N(0, 1e-3^2) plus a rank-8 component with 30 % of the energy, for every
+    # tensor (Muon matrices included)
     _gpt(1, "12-layer GPT, hidden 768, MLP 3072, vocab 65536", 12, 768, 3072, 65536,
-         steps=10, seed=1, muon_grad="lowrank", adamw_grad="lowrank"),
+         steps=10, seed=1, muon_grad="lowrank", adamw_grad="lowrank", muon_sigma=1e-3),
     _gpt(2, "20-layer GPT, hidden 1280, MLP 5120, vocab 65536", 20, 1280, 5120, 65536,
          steps=10, seed=2, muon_grad="rowlognormal", adamw_grad="gauss"),
     _gpt(3, "24-layer GQA model, hidden 2048, KV 512, MLP 8192, vocab 128000", 24, 2048, 8192,

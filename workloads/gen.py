@@ -18,7 +18,8 @@ Two backends draw from the same recipes:
   values; used where only timing matters or where the oracle reads back the
   generated inputs (large workloads).
 
-Gradient recipes (sigma0 = 0.02 for Muon matrices, 1e-3 for AdamW tensors):
+Gradient recipes (sigma0: the workload's muon_sigma for Muon matrices, 0.02 unless the
+workload states otherwise, and adamw_sigma, 1e-3, for AdamW tensors):
 
 * ``gauss``:        sigma0 * z
 * ``rowlognormal``: sigma0 * z * exp(xi_row), xi ~ N(0, 1) per row (1-D: gauss)
@@ -124,7 +125,7 @@ def np_muon_bucket_grads(wl: Workload, bucket: int, step: int) -> np.ndarray:
     out = np.empty((b.K, b.A, b.B), dtype=np.float32)
     for k in range(b.K):
         out[k] = np_grad(wl.seed, step, muon_index(wl, bucket, k), (b.A, b.B),
-                         wl.muon_grad, MUON_SIGMA)
+                         wl.muon_grad, wl.muon_sigma)
     return out
 
 
@@ -139,7 +140,7 @@ def np_adamw_flat_grads(wl: Workload, step: int) -> np.ndarray:
     out = np.empty(wl.adamw_numel, dtype=np.float32)
     for j, lo, hi in adamw_offsets(wl):
         out[lo:hi] = np_grad(wl.seed, step, adamw_index(wl, j), wl.adamw[j].shape,
-                             wl.adamw_grad, ADAMW_SIGMA).reshape(-1)
+                             wl.adamw_grad, wl.adamw_sigma).reshape(-1)
     return out
 
 
@@ -202,7 +203,7 @@ def torch_muon_bucket(torch, wl: Workload, bucket: int, step: int, out):
         if step == 0:
             torch_fill_param(torch, out[k], wl.seed, idx)
         else:
-            torch_fill_grad(torch, out[k], wl.seed, step, idx, wl.muon_grad, MUON_SIGMA)
+            torch_fill_grad(torch, out[k], wl.seed, step, idx, wl.muon_grad, wl.muon_sigma)
     return out
 
 
@@ -214,5 +215,5 @@ def torch_adamw_flat(torch, wl: Workload, step: int, out):
         if step == 0:
             torch_fill_param(torch, view, wl.seed, idx)
         else:
-            torch_fill_grad(torch, view, wl.seed, step, idx, wl.adamw_grad, ADAMW_SIGMA)
+            torch_fill_grad(torch, view, wl.seed, step, idx, wl.adamw_grad, wl.adamw_sigma)
     return out
