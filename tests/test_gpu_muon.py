@@ -359,7 +359,7 @@ def _oracle_check_step(prev, g, mom, got_p, got_m, A, B, hp, tol=MUON_RTOL):
 
 
 @pytest.mark.parametrize("index", [1, 2, 3])
-def test_muon_full_size_all_steps(index):
+def test_muon_full_size_all_steps(index, capsys):
     """Every bucket of the workload at full size, in the launch configuration the
     benchmark times (one ma_muon_step over all buckets), for the workload's whole step
     count (10, 10 and 5 steps): the first and last matrix of each bucket (the last only
@@ -398,7 +398,8 @@ def test_muon_full_size_all_steps(index):
                                                    got_p, ms[bi][k].cpu().numpy(), b.A, b.B, hp)
             prev[(bi, k)] = got_p.astype(np.float64)
             worst = max(worst, err)
-        print(f"workload {index} step {t}: worst update error {worst:.3e}", flush=True)
+        with capsys.disabled():  # progress on the terminal even under capture
+            print(f"workload {index} step {t}: worst update error {worst:.3e}", flush=True)
 
 
 @pytest.mark.parametrize("shapes", [[(6, 4096, 2304), (6, 2304, 4096)], [(6, 4096, 2304)]])

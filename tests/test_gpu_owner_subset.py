@@ -27,8 +27,15 @@ pytestmark = pytest.mark.gpu
 DEV = "cuda:0"
 
 
-def test_owner_subset_full_size_three_steps():
+def test_owner_subset_full_size_three_steps(capsys):
     wl = workloads.workload(4)
+
+    def progress(msg):
+        # straight to the terminal even when pytest captures output: the oracle calls
+        # take tens of seconds each, and a silent run looks hung
+        with capsys.disabled():
+            print(msg, flush=True)
+
     hp = wl.muon_hp
     ps, gs, ms = [], [], []
     for bi, b in enumerate(wl.muon):
@@ -58,10 +65,10 @@ def test_owner_subset_full_size_three_steps():
             got_p = ps[pk[0]][pk[1]].cpu().numpy()
             got_m = ms[pk[0]][pk[1]].cpu().numpy()
             if pk == down or t == wl.steps:
+                progress(f"step {t} bucket {pk[0]} matrix {pk[1]}: oracle running")
                 mom[pk], err = _oracle_check_step(prev[pk], grads[pk], mom[pk], got_p, got_m,
                                                   b.A, b.B, hp)
-                print(f"step {t} bucket {pk[0]} matrix {pk[1]}: update error {err:.3e}",
-                      flush=True)
+                progress(f"step {t} bucket {pk[0]} matrix {pk[1]}: update error {err:.3e}")
             else:
                 # momentum only (sum form, exact closed form per step)
                 mom[pk] = mu * mom[pk] + grads[pk].astype(np.float64)
