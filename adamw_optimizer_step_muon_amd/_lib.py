@@ -27,8 +27,10 @@ EXPORTED = (
     "ma_abi_version", "ma_status_string", "ma_last_error", "ma_muon_route_of",
     "ma_muon_workspace_bytes", "ma_muon_phases", "ma_muon_step", "ma_adamw_step",
     "ma_newton_schulz_workspace_bytes", "ma_newton_schulz", "ma_muon_tune", "ma_muon_tune_reset",
-    "ma_adamw_step_multi", "ma_muon_check_plan", "ma_muon_ns_time",
+    "ma_adamw_step_multi", "ma_muon_check_plan", "ma_muon_ns_time", "ma_muon_static_init",
+    "ma_muon_step_static",
 )
+MA_STATIC_WORKSPACE_BYTES = 512 << 20
 
 
 class MuonAdamWError(RuntimeError):
@@ -141,6 +143,12 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.ma_muon_check_plan.argtypes = [ctypes.POINTER(_MuonBucket), ctypes.c_int32,
                                        ctypes.POINTER(_MuonHParams), ctypes.c_int32,
                                        ctypes.POINTER(_PlanReport)]
+    lib.ma_muon_static_init.restype = ctypes.c_int
+    lib.ma_muon_static_init.argtypes = []
+    lib.ma_muon_step_static.restype = ctypes.c_int
+    lib.ma_muon_step_static.argtypes = [ctypes.POINTER(_MuonBucket), ctypes.c_int32,
+                                        ctypes.POINTER(_MuonHParams), ctypes.c_void_p,
+                                        ctypes.POINTER(_MuonRoute)]
     lib.ma_muon_ns_time.restype = ctypes.c_int
     lib.ma_muon_ns_time.argtypes = [ctypes.POINTER(_MuonBucket), ctypes.c_int32,
                                     ctypes.POINTER(_MuonHParams), ctypes.c_void_p,
@@ -347,6 +355,33 @@ def muon_step(buckets, *, lr: float, momentum: float = 0.95, weight_decay: float
     ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
     _check(lib.ma_muon_step(arr, len(stacks), ctypes.byref(hp), _ptr(workspace), ws_bytes,
                             _stream_handle(stream, device) if device is not None else 0, routes))
+    return [Route(bool(r.transposed), r.m, r.n, r.ns_steps_run, r.m_pad, r.n_pad, r.ns_mode_run)
+            for r in routes[:len(stacks)]]
+
+
+def muon_step_static(buckets, *, lr: float, momentum: float = 0.95, weight_decay: float = 0.0,
+                     nesterov: bool = True, ns_steps: int = 5, ns_coeffs=None,
+                     ns_eps: float = 1e-7, cautious_wd: bool = False, scale_mode: int = 0,
+                     ns_mode: int = 0, stream=None):
+    """ma_muon_step on the library's static workspace (ma_muon_step_static): no device
+    memory is allocated, by the library or here.  Calls on one GPU share that workspace
+    and must not overlap.  Returns the routing report of each bucket."""
+    stacks = []
+    for i, (p, g, m) in enumerate(buckets):
+        for name, t in (("param", p), ("grad", g), ("momentum", m)):
+            _require_f32_cuda(f"bucket {i} {name}", t)
+        p3, g3, m3 = _as_stack(p), _as_stack(g), _as_stack(m)
+        if not (p3.shape == g3.shape == m3.shape):
+            raise ValueError(f"bucket {i}: param, grad and momentum shapes differ")
+        stacks.append((p3, g3, m3))
+    arr = _bucket_array(stacks)
+    hp, _keep = _muon_hparams(lr, momentum, weight_decay, nesterov, ns_steps, ns_coeffs, ns_eps,
+                              cautious_wd, scale_mode, ns_mode)
+    routes = (_MuonRoute * max(len(stacks), 1))()
+    device = stacks[0][0].device if stacks else None
+    _check(load().ma_muon_step_static(arr, len(stacks), ctypes.byref(hp),
+                                      _stream_handle(stream, device) if device is not None else 0,
+                                      routes))
     return [Route(bool(r.transposed), r.m, r.n, r.ns_steps_run, r.m_pad, r.n_pad, r.ns_mode_run)
             for r in routes[:len(stacks)]]
 

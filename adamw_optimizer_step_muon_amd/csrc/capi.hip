@@ -18,6 +18,11 @@
 namespace ma {
 namespace {
 
+// Workspace of ma_muon_step_static: a file-scope device array, one copy per GPU, kept
+// until the process ends.  Host code never uses this name as an address (on the host it
+// is only a handle); it resolves each device's copy with hipGetSymbolAddress.
+static __device__ __align__(256) unsigned char scratch[MA_STATIC_WORKSPACE_BYTES];
+
 thread_local std::string g_last_error;
 
 ma_status fail(ma_status st, const char* fmt, ...) {
@@ -510,6 +515,11 @@ ma_status adamw_const(const ma_adamw_hparams* hp, AdamWConst* c) {
   return MA_OK;
 }
 
+// Each device's copy of the static workspace (resolved once per device).
+constexpr int kMaxDevices = 64;
+std::mutex g_static_mu;
+void* g_static_ws[kMaxDevices] = {};
+
 // Grid size limit of one launch (blocks), with the room the block-count arithmetic needs.
 constexpr int64_t kMaxGridBlocks = (int64_t(1) << 31) - 4096;
 
@@ -992,6 +1002,48 @@ ma_status ma_muon_tune(const ma_muon_bucket* buckets, int32_t n_buckets,
 void ma_muon_tune_reset(void) {
   std::lock_guard<std::mutex> lock(g_tune_mu);
   g_tune.clear();
+}
+
+ma_status ma_muon_static_init(void) {
+  g_last_error.clear();
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+  if (dev < 0 || dev >= kMaxDevices) return fail(MA_ERR_UNSUPPORTED, "device %d", dev);
+  std::lock_guard<std::mutex> lock(g_static_mu);
+  if (g_static_ws[dev]) return MA_OK;
+  void* ptr = nullptr;
+  e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+  if (e != hipSuccess) return hip_fail(e, "hipGetSymbolAddress(scratch)");
+  if (!ptr || (reinterpret_cast<uintptr_t>(ptr) & 255u))
+    return fail(MA_ERR_HIP, "static workspace address %p is null or not 256-byte aligned", ptr);
+  g_static_ws[dev] = ptr;
+  return MA_OK;
+}
+
+ma_status ma_muon_step_static(const ma_muon_bucket* buckets, int32_t n_buckets,
+                              const ma_muon_hparams* hp, void* stream,
+                              ma_muon_route* route_out) {
+  g_last_error.clear();
+  ma_status st = check_step_args(buckets, n_buckets, hp);
+  if (st != MA_OK) return st;
+  const size_t need = ma_muon_workspace_bytes(buckets, n_buckets, hp);
+  if (need > MA_STATIC_WORKSPACE_BYTES)
+    return fail(MA_ERR_WORKSPACE,
+                "these buckets need %zu bytes of workspace, above the static workspace's %zu "
+                "(use ma_muon_step with a caller workspace)",
+                need, static_cast<size_t>(MA_STATIC_WORKSPACE_BYTES));
+  st = ma_muon_static_init();
+  if (st != MA_OK) return st;
+  int dev = 0;
+  const hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+  void* ws = nullptr;
+  {
+    std::lock_guard<std::mutex> lock(g_static_mu);
+    ws = g_static_ws[dev];
+  }
+  return ma_muon_step(buckets, n_buckets, hp, ws, MA_STATIC_WORKSPACE_BYTES, stream, route_out);
 }
 
 ma_status ma_muon_check_plan(const ma_muon_bucket* buckets, int32_t n_buckets,

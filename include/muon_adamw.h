@@ -244,6 +244,30 @@ ma_status ma_muon_tune(const ma_muon_bucket* buckets, int32_t n_buckets,
 /* Host only: forget every tuned or pinned tile (back to the default rules). */
 void ma_muon_tune_reset(void);
 
+/* For callers that cannot allocate device memory (code under HIP graph capture, tight
+ * serving loops, harnesses that forbid hipMalloc): ma_muon_step with the library's own
+ * static workspace of MA_STATIC_WORKSPACE_BYTES instead of a caller workspace.  The
+ * workspace is a file-scope device array; each GPU holds its own copy from the first
+ * use on that device until the process ends.  Nothing is allocated or freed by these
+ * calls; parameters, gradients and momenta are still the caller's.
+ *
+ * ma_muon_static_init: resolves the current device's copy (hipGetSymbolAddress); called
+ * by ma_muon_step_static on its first use on a device.  Call it once per device before
+ * capturing a graph that contains ma_muon_step_static.
+ * ma_muon_step_static: exactly ma_muon_step (same kernels, same results bit for bit) on
+ * the current device's static workspace.  Buckets needing more than
+ * MA_STATIC_WORKSPACE_BYTES (ma_muon_workspace_bytes) are rejected with
+ * MA_ERR_WORKSPACE before anything is launched.  Every call on one GPU shares that GPU's
+ * workspace: calls that overlap on one GPU (other streams, other threads) RACE and must
+ * be serialised by the caller; each step rewrites every workspace byte it reads, so
+ * nothing needs clearing between calls.
+ * Errors: as ma_muon_step, MA_ERR_UNSUPPORTED (device index above 63), MA_ERR_HIP. */
+#define MA_STATIC_WORKSPACE_BYTES ((size_t)512 << 20)
+ma_status ma_muon_static_init(void);
+ma_status ma_muon_step_static(const ma_muon_bucket* buckets, int32_t n_buckets,
+                              const ma_muon_hparams* hp, void* stream,
+                              ma_muon_route* route_out);
+
 /* What ma_muon_check_plan replayed. */
 typedef struct {
   int64_t launches;     /* kernel launches of the step (or of the orthogonalisation) */
