@@ -28,7 +28,7 @@ EXPORTED = (
     "ma_muon_workspace_bytes", "ma_muon_phases", "ma_muon_step", "ma_adamw_step",
     "ma_newton_schulz_workspace_bytes", "ma_newton_schulz", "ma_muon_tune", "ma_muon_tune_reset",
     "ma_adamw_step_multi", "ma_muon_check_plan", "ma_muon_ns_time", "ma_muon_static_init",
-    "ma_muon_step_static",
+    "ma_muon_step_static", "ma_muon_tune_configs",
 )
 MA_STATIC_WORKSPACE_BYTES = 512 << 20
 
@@ -57,6 +57,11 @@ class _MuonRoute(ctypes.Structure):
     _fields_ = [("transposed", ctypes.c_int32), ("m", ctypes.c_int32), ("n", ctypes.c_int32),
                 ("ns_steps_run", ctypes.c_int32), ("m_pad", ctypes.c_int32),
                 ("n_pad", ctypes.c_int32), ("ns_mode_run", ctypes.c_int32)]
+
+
+class _GemmConfig(ctypes.Structure):
+    _fields_ = [("tile", ctypes.c_int32), ("band", ctypes.c_int32), ("spread", ctypes.c_int32),
+                ("pipeline", ctypes.c_int32)]
 
 
 class _PlanReport(ctypes.Structure):
@@ -137,6 +142,11 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.ma_adamw_step_multi.restype = ctypes.c_int
     lib.ma_adamw_step_multi.argtypes = [ctypes.POINTER(_AdamWSegment), ctypes.c_int32,
                                         ctypes.POINTER(_AdamWHParams), ctypes.c_void_p]
+    lib.ma_muon_tune_configs.restype = ctypes.c_int
+    lib.ma_muon_tune_configs.argtypes = [ctypes.POINTER(_MuonBucket), ctypes.c_int32,
+                                         ctypes.POINTER(_MuonHParams), ctypes.c_void_p,
+                                         ctypes.c_size_t, ctypes.c_void_p, ctypes.c_int32,
+                                         ctypes.POINTER(_GemmConfig)]
     lib.ma_muon_tune_reset.restype = None
     lib.ma_muon_tune_reset.argtypes = []
     lib.ma_muon_check_plan.restype = ctypes.c_int
@@ -319,6 +329,55 @@ def muon_tune(shapes: Sequence[Sequence[int]], *, reps: int = 3, tiles=None, wor
         _check(lib.ma_muon_tune(arr, n, ctypes.byref(hp), _ptr(workspace), ws_bytes,
                                 _stream_handle(stream, device), int(reps), out))
     return [[int(out[3 * i + q]) for q in range(3)] for i in range(nph)]
+
+
+CONFIG_KEYS = ("tile", "band", "spread", "pipeline")
+DEFAULT_CONFIG = {"tile": 0, "band": 0, "spread": -1, "pipeline": 0}
+
+
+def muon_tune_configs(shapes: Sequence[Sequence[int]], *, reps: int = 3, configs=None,
+                      workspace=None, stream=None, device=None, ns_mode: int = 0, grads=None):
+    """Per-shape Newton-Schulz GEMM configurations (ma_muon_tune_configs) for buckets of
+    these (K, A, B) shapes.  reps > 0: search tile, pipeline, band width and spreading on
+    the workspace (scratch; allocated for the call when None) and keep the fastest;
+    reps == 0: pin `configs` (per phase, three dicts with keys tile, band, spread,
+    pipeline; missing keys take their defaults).  grads: the buckets' (K, A, B) gradients,
+    cast into the workspace before the timing so the candidates run on real operands.
+    Returns the configurations in force."""
+    import torch
+
+    n = len(shapes)
+    arr = (_MuonBucket * max(n, 1))()
+    for i, (K, A, B) in enumerate(shapes):
+        g = 0
+        if grads is not None:
+            _require_f32_cuda(f"gradient {i}", grads[i])
+            if tuple(_as_stack(grads[i]).shape) != (int(K), int(A), int(B)):
+                raise ValueError(f"gradient {i} does not have shape {(K, A, B)}")
+            g = _ptr(grads[i])
+        arr[i] = _MuonBucket(int(K), int(A), int(B), 0, g, 0)
+    hp = _mode_hparams(ns_mode)
+    lib = load()
+    nph, _ = muon_phases(shapes, ns_mode)
+    out = (_GemmConfig * max(3 * nph, 1))()
+    if int(reps) == 0:
+        flat = [c for ph in (configs or []) for c in ph]
+        if len(flat) != 3 * nph:
+            raise ValueError(f"configs needs {nph} phases of 3 entries")
+        for i, c in enumerate(flat):
+            full = {**DEFAULT_CONFIG, **c}
+            out[i] = _GemmConfig(*(int(full[k]) for k in CONFIG_KEYS))
+        _check(lib.ma_muon_tune_configs(arr, n, ctypes.byref(hp), None, 0, None, 0, out))
+    else:
+        device = torch.device("cuda", torch.cuda.current_device()) if device is None else device
+        need = int(lib.ma_muon_workspace_bytes(arr, n, ctypes.byref(hp)))
+        if workspace is None and need > 0:
+            workspace = _scratch(need, device, stream)
+        ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+        _check(lib.ma_muon_tune_configs(arr, n, ctypes.byref(hp), _ptr(workspace), ws_bytes,
+                                        _stream_handle(stream, device), int(reps), out))
+    return [[{k: int(getattr(out[3 * i + q], k)) for k in CONFIG_KEYS} for q in range(3)]
+            for i in range(nph)]
 
 
 def muon_tune_reset() -> None:

@@ -197,15 +197,16 @@ ma_status for_each_phase(const ma_muon_bucket* buckets, int32_t n_buckets, int32
   return MA_OK;
 }
 
-// Tuned GEMM tiles ("DMuon: Efficient Distributed Muon Training with Near-Adam
+// Tuned GEMM configurations ("DMuon: Efficient Distributed Muon Training with Near-Adam
 // Overhead", section 2.4, autotuning per shape): one entry per phase shape (its buckets'
-// K, padded sides, orientation and X^T choice), the tile of the Gram, polynomial and
-// combine launches (0: the default rule).  Filled by ma_muon_tune, read by every
-// Newton-Schulz run; process-wide, guarded by a mutex.
+// K, padded sides, orientation and X^T choice), the configuration of the Gram,
+// polynomial and combine launches (defaults: the library's rules).  Filled by
+// ma_muon_tune / ma_muon_tune_configs, read by every Newton-Schulz run; process-wide,
+// guarded by a mutex.
 enum Product { kProdGram = 0, kProdPoly = 1, kProdCombine = 2 };
-using Tiles = std::array<int, 3>;
+using Choices = std::array<GemmChoice, 3>;
 std::mutex g_tune_mu;
-std::map<std::vector<int64_t>, Tiles> g_tune;
+std::map<std::vector<int64_t>, Choices> g_tune;
 
 std::vector<int64_t> phase_key(const Phase& ph) {
   std::vector<int64_t> k{ph.n};
@@ -217,10 +218,10 @@ std::vector<int64_t> phase_key(const Phase& ph) {
   return k;
 }
 
-Tiles tuned_tiles(const Phase& ph) {
+Choices tuned_choices(const Phase& ph) {
   std::lock_guard<std::mutex> lock(g_tune_mu);
   const auto it = g_tune.find(phase_key(ph));
-  return it == g_tune.end() ? Tiles{0, 0, 0} : it->second;
+  return it == g_tune.end() ? Choices{} : it->second;
 }
 
 // Tiles a product of this phase can run: 256 and 128 on a 256-padded phase (the
@@ -247,6 +248,23 @@ bool tile_available(const Phase& ph, int prod, int tile) {
   for (int i = 0; i < nc; ++i)
     if (c[i] == tile) return true;
   return false;
+}
+
+// Whether a product with this tile runs the 256-tile kernel whose pipeline can be chosen
+// (the Gram-side products, and the combine of a phase that keeps X^T).
+bool has_pipeline_choice(const Phase& ph, int prod, int tile) {
+  if (forced_tile() ? forced_tile() != 256 : (tile ? tile : ph.tile) != 256 || ph.tile != 256)
+    return false;
+  return prod != kProdCombine || ph.plan[0].keeps_xt;
+}
+
+// A pinned configuration the phase can run: tile available (or 0), pipeline 0..2 (1, 2
+// only where has_pipeline_choice), band 0..64, spread -1..1.
+bool choice_valid(const Phase& ph, int prod, const GemmChoice& c) {
+  if (c.tile != 0 && !tile_available(ph, prod, c.tile)) return false;
+  if (c.pipeline < 0 || c.pipeline > 2) return false;
+  if (c.pipeline != 0 && !has_pipeline_choice(ph, prod, c.tile)) return false;
+  return c.band >= 0 && c.band <= 64 && c.spread >= -1 && c.spread <= 1;
 }
 
 template <class T>
@@ -291,7 +309,7 @@ ma_status run_ns_gram_space(const Phase& ph, const ma_muon_hparams* hp, char* ws
   SymProd sp[kMaxGemmGroups];
   const float* inv[kMaxGemmGroups];
   for (int j = 0; j < ph.n; ++j) inv[j] = at<const float>(ws, ph.base[j] + ph.plan[j].off_inv);
-  const Tiles tiles = tuned_tiles(ph);
+  const Choices tiles = tuned_choices(ph);
   phase_groups(ph, ws, 0, g);  // X = X_0 (bf16 U), Xn = the output, R = R_0
   auto buf = [&](int j, size_t off) { return at<unsigned short>(ws + ph.base[j], off); };
   hipError_t e = launch_gram(g, ph.n, inv, tiles[kProdGram], s);
@@ -349,7 +367,7 @@ ma_status run_ns(const Phase& ph, const ma_muon_hparams* hp, char* ws, hipStream
   NsGroup g[kMaxGemmGroups];
   const float* inv[kMaxGemmGroups];
   for (int j = 0; j < ph.n; ++j) inv[j] = at<const float>(ws, ph.base[j] + ph.plan[j].off_inv);
-  const Tiles tiles = tuned_tiles(ph);
+  const Choices tiles = tuned_choices(ph);
   int cur = 0;
   for (int it = 0; it < hp->ns_steps; ++it) {
     phase_groups(ph, ws, cur, g);
@@ -579,9 +597,8 @@ class PlanChecker final : public LaunchRecorder {
           fail_("buffers " + regions[i].name + " and " + regions[k].name + " overlap");
   }
 
-  void gemm(int epi, TileCfg cfg, const GemmTable& t) override {
+  void gemm(int epi, const TileShape& sh, const GemmTable& t) override {
     ++launches;
-    const TileShape sh = tile_shape(cfg);
     const bool bt = epi == kCombine && sh.combine_reads_x;
     const int grid = t.start[t.ngroups];
     std::vector<std::vector<int>> seen(t.ngroups);
@@ -694,6 +711,197 @@ class PlanChecker final : public LaunchRecorder {
     fail_(std::string(what) + " starts outside every buffer");
   }
 };
+
+GemmChoice to_choice(const ma_gemm_config& c) {
+  GemmChoice g;
+  g.tile = c.tile;
+  g.band = c.band;
+  g.spread = c.spread;
+  g.pipeline = c.pipeline;
+  return g;
+}
+
+ma_gemm_config to_config(const GemmChoice& g) {
+  return ma_gemm_config{g.tile, g.band, g.spread, g.pipeline};
+}
+
+// ma_muon_tune and ma_muon_tune_configs.  cfg: 3 entries per phase, input when reps = 0
+// (pin), output when reps > 0 (search).  The search, per product of each phase, times
+// candidates one dimension at a time from the defaults: the tile, then (for the 256-tile
+// kernels with a choice) the pipeline, then the L2 band width (2, 4, 8 row panels), then
+// (256- and 192-tiles) the DMA spreading; each candidate runs once to warm up and `reps`
+// times between two HIP events on the phase's workspace operands (the buckets'
+// gradients cast there first when every bucket of the phase gives one), and replaces the
+// kept one only when at least 3 % faster.  tiles_only: the tile alone.
+ma_status tune_impl(const ma_muon_bucket* buckets, int32_t n_buckets, const ma_muon_hparams* hp,
+                    void* workspace, size_t workspace_bytes, void* stream, int32_t reps,
+                    ma_gemm_config* cfg, bool tiles_only) {
+  if (hp) {
+    const ma_status st = check_hparams(hp);
+    if (st != MA_OK) return st;
+  }
+  if (n_buckets < 0) return fail(MA_ERR_INVALID_ARG, "n_buckets %d < 0", n_buckets);
+  if (n_buckets > 0 && !buckets) return fail(MA_ERR_INVALID_ARG, "buckets is NULL");
+  if (reps < 0 || reps > 1000) return fail(MA_ERR_INVALID_ARG, "reps %d outside [0, 1000]", reps);
+  for (int32_t i = 0; i < n_buckets; ++i) {
+    const ma_status st = check_shape(buckets[i].K, buckets[i].A, buckets[i].B);
+    if (st != MA_OK) return fail(st, "bucket %d: %s", i, g_last_error.c_str());
+  }
+  const int32_t mode = hp ? hp->ns_mode : 0;
+  if (reps == 0) {
+    // pin: check every requested configuration first, then store (all default: forget)
+    int phase = 0;
+    ma_status st = for_each_phase(buckets, n_buckets, mode, [&](const Phase& ph) -> ma_status {
+      for (int q = 0; q < 3; ++q)
+        if (!choice_valid(ph, q, to_choice(cfg[3 * phase + q])))
+          return fail(MA_ERR_INVALID_ARG,
+                      "phase %d, product %d: configuration (tile %d, band %d, spread %d, "
+                      "pipeline %d) is not available", phase, q, cfg[3 * phase + q].tile,
+                      cfg[3 * phase + q].band, cfg[3 * phase + q].spread,
+                      cfg[3 * phase + q].pipeline);
+      ++phase;
+      return MA_OK;
+    });
+    if (st != MA_OK) return st;
+    phase = 0;
+    std::lock_guard<std::mutex> lock(g_tune_mu);
+    return for_each_phase(buckets, n_buckets, mode, [&](const Phase& ph) -> ma_status {
+      const Choices c{to_choice(cfg[3 * phase]), to_choice(cfg[3 * phase + 1]),
+                      to_choice(cfg[3 * phase + 2])};
+      if (c[0].is_default() && c[1].is_default() && c[2].is_default())
+        g_tune.erase(phase_key(ph));
+      else
+        g_tune[phase_key(ph)] = c;
+      ++phase;
+      return MA_OK;
+    });
+  }
+  const size_t need = ma_muon_workspace_bytes(buckets, n_buckets, hp);
+  if (need > 0) {
+    if (!workspace) return fail(MA_ERR_WORKSPACE, "workspace is NULL, %zu bytes needed", need);
+    if (reinterpret_cast<uintptr_t>(workspace) & 255u)
+      return fail(MA_ERR_WORKSPACE, "workspace must be 256-byte aligned");
+    if (workspace_bytes < need)
+      return fail(MA_ERR_WORKSPACE, "workspace has %zu bytes, %zu needed", workspace_bytes, need);
+  }
+  int phases = 0;
+  for_each_phase(buckets, n_buckets, mode, [&](const Phase&) { ++phases; return MA_OK; });
+  if (phases == 0) return MA_OK;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  char* ws = static_cast<char*>(workspace);
+  const NsCoeffs c = hp ? coeff_at(hp, 0) : kQuintic;
+  hipEvent_t e0 = nullptr, e1 = nullptr;
+  hipError_t he = hipEventCreate(&e0);
+  if (he == hipSuccess) he = hipEventCreate(&e1);
+  if (he != hipSuccess) {
+    if (e0) (void)hipEventDestroy(e0);
+    return hip_fail(he, "event create");
+  }
+  int phase = 0;
+  const ma_status st = for_each_phase(buckets, n_buckets, mode, [&](const Phase& ph) -> ma_status {
+    // the phase's operands: its gradients cast as ma_muon_step casts them, when given
+    // (the matrix cores' power, and so the clock and the timing, depends on the data)
+    bool have_grads = true;
+    for (int j = 0; j < ph.n; ++j) have_grads = have_grads && buckets[ph.bucket[j]].grad;
+    if (have_grads) {
+      ma_muon_hparams cast_hp{};
+      cast_hp.ns_eps = hp ? hp->ns_eps : 1e-7f;
+      for (int j = 0; j < ph.n; ++j) {
+        const ma_status s2 = prep_bucket(ph.plan[j], buckets[ph.bucket[j]].grad, nullptr,
+                                         &cast_hp, ws + ph.base[j], s);
+        if (s2 != MA_OK) return s2;
+      }
+    }
+    NsGroup g[kMaxGemmGroups];
+    phase_groups(ph, ws, 0, g);
+    auto launch = [&](int q, const GemmChoice& ch) {
+      switch (q) {
+        case kProdGram: return launch_gram(g, ph.n, nullptr, ch, s);
+        case kProdPoly: return launch_poly(g, ph.n, c.a, c.b, c.c, ch, s);
+        default: return launch_combine(g, ph.n, nullptr, false, ch, s);
+      }
+    };
+    // milliseconds of `reps` launches of one candidate (after one warm-up launch)
+    auto time_of = [&](int q, const GemmChoice& ch, float* ms) -> hipError_t {
+      hipError_t e = launch(q, ch);
+      if (e == hipSuccess) e = hipEventRecord(e0, s);
+      for (int r = 0; r < reps && e == hipSuccess; ++r) e = launch(q, ch);
+      if (e == hipSuccess) e = hipEventRecord(e1, s);
+      if (e == hipSuccess) e = hipEventSynchronize(e1);
+      if (e == hipSuccess) e = hipEventElapsedTime(ms, e0, e1);
+      return e;
+    };
+    Choices best{};
+    for (int q = 0; q < 3; ++q) {
+      GemmChoice cur{};
+      float cur_ms = 0.0f;
+      bool first = true;
+      // a candidate replaces the one kept only when it is clearly faster: differences
+      // of a few percent between launches of one configuration are noise
+      constexpr float kMargin = 0.97f;
+      auto consider = [&](const GemmChoice& cand) -> hipError_t {
+        float ms = 0.0f;
+        const hipError_t e = time_of(q, cand, &ms);
+        if (e != hipSuccess) return e;
+        if (first || ms < kMargin * cur_ms) {
+          cur = cand;
+          cur_ms = ms;
+          first = false;
+        }
+        return hipSuccess;
+      };
+      // 1. tile
+      int cand[3];
+      const int nc = tile_candidates(ph, q, cand);
+      for (int i = 0; i < nc; ++i) {
+        GemmChoice t{};
+        t.tile = cand[i];
+        const hipError_t e = consider(t);
+        if (e != hipSuccess) return hip_fail(e, "tuning launch");
+      }
+      if (!tiles_only) {
+        // 2. pipeline of the 256-tile kernels
+        const GemmChoice base = cur;
+        if (has_pipeline_choice(ph, q, base.tile))
+          for (int pl : {1, 2}) {
+            GemmChoice t = base;
+            t.pipeline = pl;
+            const hipError_t e = consider(t);
+            if (e != hipSuccess) return hip_fail(e, "tuning launch");
+          }
+        // 3. L2 band width of the tile order
+        const GemmChoice base2 = cur;
+        for (int band : {2, 4, 8}) {
+          GemmChoice t = base2;
+          t.band = band;
+          const hipError_t e = consider(t);
+          if (e != hipSuccess) return hip_fail(e, "tuning launch");
+        }
+        // 4. DMA spreading (256- and 192-tiles)
+        const GemmChoice base3 = cur;
+        const int tl = base3.tile ? base3.tile : ph.tile;
+        if (tl >= 192 && !forced_tile())
+          for (int sp : {0, 1}) {
+            GemmChoice t = base3;
+            t.spread = sp;
+            const hipError_t e = consider(t);
+            if (e != hipSuccess) return hip_fail(e, "tuning launch");
+          }
+      }
+      best[q] = cur;
+      cfg[3 * phase + q] = to_config(cur);
+    }
+    {
+      std::lock_guard<std::mutex> lock(g_tune_mu);
+      g_tune[phase_key(ph)] = best;
+    }
+    ++phase;
+    return MA_OK;
+  });
+  (void)hipEventDestroy(e0);
+  (void)hipEventDestroy(e1);
+  return st;
+}
 
 }  // namespace
 
@@ -898,104 +1106,38 @@ ma_status ma_newton_schulz(const float* in, float* out, int64_t K, int64_t A, in
 ma_status ma_muon_tune(const ma_muon_bucket* buckets, int32_t n_buckets,
                        const ma_muon_hparams* hp, void* workspace, size_t workspace_bytes,
                        void* stream, int32_t reps, int32_t* tiles) {
+  // the tile-only form of ma_muon_tune_configs
   g_last_error.clear();
-  if (hp) {
-    const ma_status st = check_hparams(hp);
-    if (st != MA_OK) return st;
-  }
-  if (n_buckets < 0) return fail(MA_ERR_INVALID_ARG, "n_buckets %d < 0", n_buckets);
-  if (n_buckets > 0 && !buckets) return fail(MA_ERR_INVALID_ARG, "buckets is NULL");
-  if (reps < 0 || reps > 1000) return fail(MA_ERR_INVALID_ARG, "reps %d outside [0, 1000]", reps);
   if (reps == 0 && !tiles) return fail(MA_ERR_INVALID_ARG, "tiles is NULL with reps 0");
-  for (int32_t i = 0; i < n_buckets; ++i) {
-    const ma_status st = check_shape(buckets[i].K, buckets[i].A, buckets[i].B);
-    if (st != MA_OK) return fail(st, "bucket %d: %s", i, g_last_error.c_str());
-  }
-  if (reps == 0) {
-    // pin: check every requested tile first, then store (all zero: back to the rule)
-    int phase = 0;
-    ma_status st = for_each_phase(buckets, n_buckets, hp ? hp->ns_mode : 0, [&](const Phase& ph) -> ma_status {
-      for (int q = 0; q < 3; ++q) {
-        const int t = tiles[3 * phase + q];
-        if (t != 0 && !tile_available(ph, q, t))
-          return fail(MA_ERR_INVALID_ARG, "phase %d, product %d: tile %d is not available", phase,
-                      q, t);
-      }
-      ++phase;
-      return MA_OK;
-    });
-    if (st != MA_OK) return st;
-    phase = 0;
-    std::lock_guard<std::mutex> lock(g_tune_mu);
-    return for_each_phase(buckets, n_buckets, hp ? hp->ns_mode : 0, [&](const Phase& ph) -> ma_status {
-      const Tiles t{tiles[3 * phase], tiles[3 * phase + 1], tiles[3 * phase + 2]};
-      if (t == Tiles{0, 0, 0}) g_tune.erase(phase_key(ph)); else g_tune[phase_key(ph)] = t;
-      ++phase;
-      return MA_OK;
-    });
-  }
-  const size_t need = ma_muon_workspace_bytes(buckets, n_buckets, hp);
-  if (need > 0) {
-    if (!workspace) return fail(MA_ERR_WORKSPACE, "workspace is NULL, %zu bytes needed", need);
-    if (reinterpret_cast<uintptr_t>(workspace) & 255u)
-      return fail(MA_ERR_WORKSPACE, "workspace must be 256-byte aligned");
-    if (workspace_bytes < need)
-      return fail(MA_ERR_WORKSPACE, "workspace has %zu bytes, %zu needed", workspace_bytes, need);
-  }
-  int phases = 0;
-  for_each_phase(buckets, n_buckets, hp ? hp->ns_mode : 0, [&](const Phase&) { ++phases; return MA_OK; });
-  if (phases == 0) return MA_OK;
-  hipStream_t s = static_cast<hipStream_t>(stream);
-  char* ws = static_cast<char*>(workspace);
-  const NsCoeffs c = hp ? coeff_at(hp, 0) : kQuintic;
-  hipEvent_t e0 = nullptr, e1 = nullptr;
-  hipError_t he = hipEventCreate(&e0);
-  if (he == hipSuccess) he = hipEventCreate(&e1);
-  if (he != hipSuccess) {
-    if (e0) (void)hipEventDestroy(e0);
-    return hip_fail(he, "event create");
-  }
-  int phase = 0;
-  const ma_status st = for_each_phase(buckets, n_buckets, hp ? hp->ns_mode : 0, [&](const Phase& ph) -> ma_status {
-    NsGroup g[kMaxGemmGroups];
-    phase_groups(ph, ws, 0, g);
-    auto launch = [&](int q, int tile) {
-      switch (q) {
-        case kProdGram: return launch_gram(g, ph.n, nullptr, tile, s);
-        case kProdPoly: return launch_poly(g, ph.n, c.a, c.b, c.c, tile, s);
-        default: return launch_combine(g, ph.n, nullptr, false, tile, s);
-      }
-    };
-    Tiles best{0, 0, 0};
-    for (int q = 0; q < 3; ++q) {
-      int cand[3];
-      const int nc = tile_candidates(ph, q, cand);
-      float best_ms = 0.0f;
-      for (int i = 0; i < nc; ++i) {
-        hipError_t e = launch(q, cand[i]);  // warm-up
-        if (e == hipSuccess) e = hipEventRecord(e0, s);
-        for (int r = 0; r < reps && e == hipSuccess; ++r) e = launch(q, cand[i]);
-        if (e == hipSuccess) e = hipEventRecord(e1, s);
-        if (e == hipSuccess) e = hipEventSynchronize(e1);
-        float ms = 0.0f;
-        if (e == hipSuccess) e = hipEventElapsedTime(&ms, e0, e1);
-        if (e != hipSuccess) return hip_fail(e, "tuning launch");
-        if (i == 0 || ms < best_ms) {
-          best_ms = ms;
-          best[q] = cand[i];
-        }
-      }
-      if (tiles) tiles[3 * phase + q] = best[q];
-    }
-    {
-      std::lock_guard<std::mutex> lock(g_tune_mu);
-      g_tune[phase_key(ph)] = best;
-    }
-    ++phase;
-    return MA_OK;
-  });
-  (void)hipEventDestroy(e0);
-  (void)hipEventDestroy(e1);
+  const int32_t nph = ma_muon_phases(buckets, n_buckets, hp, nullptr);
+  if (nph < 0) return static_cast<ma_status>(nph);
+  std::vector<ma_gemm_config> cfg(static_cast<size_t>(3 * std::max(nph, 1)),
+                                  ma_gemm_config{0, 0, -1, 0});
+  if (reps == 0)
+    for (int i = 0; i < 3 * nph; ++i) cfg[i].tile = tiles[i];
+  const ma_status st = tune_impl(buckets, n_buckets, hp, workspace, workspace_bytes, stream, reps,
+                                 cfg.data(), /*tiles_only=*/true);
+  if (st == MA_OK && reps > 0 && tiles)
+    for (int i = 0; i < 3 * nph; ++i) tiles[i] = cfg[i].tile;
+  return st;
+}
+
+ma_status ma_muon_tune_configs(const ma_muon_bucket* buckets, int32_t n_buckets,
+                               const ma_muon_hparams* hp, void* workspace,
+                               size_t workspace_bytes, void* stream, int32_t reps,
+                               ma_gemm_config* configs) {
+  g_last_error.clear();
+  if (reps == 0 && !configs) return fail(MA_ERR_INVALID_ARG, "configs is NULL with reps 0");
+  const int32_t nph = ma_muon_phases(buckets, n_buckets, hp, nullptr);
+  if (nph < 0) return static_cast<ma_status>(nph);
+  std::vector<ma_gemm_config> cfg(static_cast<size_t>(3 * std::max(nph, 1)),
+                                  ma_gemm_config{0, 0, -1, 0});
+  if (reps == 0)
+    for (int i = 0; i < 3 * nph; ++i) cfg[i] = configs[i];
+  const ma_status st = tune_impl(buckets, n_buckets, hp, workspace, workspace_bytes, stream, reps,
+                                 cfg.data(), /*tiles_only=*/false);
+  if (st == MA_OK && reps > 0 && configs)
+    for (int i = 0; i < 3 * nph; ++i) configs[i] = cfg[i];
   return st;
 }
 

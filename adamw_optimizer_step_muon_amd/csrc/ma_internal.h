@@ -222,14 +222,30 @@ struct TileShape {
   int bm, bn, bk;
   bool combine_reads_x;  // the combine's B operand is X (k rows), not X^T
 };
-TileShape tile_shape(TileCfg cfg);
+
+// The GEMM configuration of one Newton-Schulz product of a phase.  A field at its
+// default (0, or -1 for spread) takes the library's rule for it.  Every configuration
+// accumulates each output over the same k order, so results do not depend on it.
+struct GemmChoice {
+  int tile = 0;      // 128 or 256 (on a 256-padded phase), 192 (combine only)
+  int band = 0;      // row panels per L2 band in the tile order (default 4)
+  int spread = -1;   // 256-tiles: 1 spreads the next stage's DMAs over half a stage, 0
+                     // issues them in one burst (default 1; 128-tiles always 0)
+  int pipeline = 0;  // 256-tiles of the Gram, polynomial and X^T-reading combine:
+                     // 1 = stages of k = 64 in a 3 + 2 ring, 2 = 4 stages of k = 32
+                     // (default 1)
+  bool operator==(const GemmChoice& o) const {
+    return tile == o.tile && band == o.band && spread == o.spread && pipeline == o.pipeline;
+  }
+  bool is_default() const { return *this == GemmChoice{}; }
+};
 
 // Dry run: while a recorder is installed on the calling thread, every launcher hands its
 // launch to the recorder and returns hipSuccess without touching the GPU (the host-side
 // plan check replays a step this way).
 struct LaunchRecorder {
   virtual ~LaunchRecorder() = default;
-  virtual void gemm(int epi, TileCfg cfg, const GemmTable& t) = 0;
+  virtual void gemm(int epi, const TileShape& shape, const GemmTable& t) = 0;
   virtual void prep(const BucketPlan& p, const float* G, const float* M, const double* partials,
                     const unsigned short* S, const unsigned short* T) = 0;
   virtual void norm(const BucketPlan& p, const double* partials, const float* inv,
@@ -241,23 +257,22 @@ struct LaunchRecorder {
 };
 LaunchRecorder*& launch_recorder();
 
-// GEMM tiles: `tile` (and `tile_choice`) 0 takes the default for the phase; 128 or 256
+// GEMM configurations (GemmChoice): tile 0 takes the default for the phase; 128 or 256
 // picks that tile (256 only on a 256-padded phase; the combine of a phase that keeps
 // X^T always runs its own 256-tile configuration), and the combine also takes 192
-// (192 x 256 tiles) where combine_192_ok holds for every bucket.  Every choice
-// accumulates each output over the same k order, so results do not depend on it.
+// (192 x 256 tiles) where combine_192_ok holds for every bucket.
 bool combine_192_ok(const BucketPlan& p);
 // R = X X^T (lower-triangle tiles, mirrored); R *= scale[i][k]^2 where scale[i] is given
-hipError_t launch_gram(const NsGroup* g, int n, const float* const* scale, int tile,
-                       hipStream_t s);
+hipError_t launch_gram(const NsGroup* g, int n, const float* const* scale,
+                       const GemmChoice& ch, hipStream_t s);
 // P = a I + b R + c R R^T (lower-triangle tiles, mirrored)
-hipError_t launch_poly(const NsGroup* g, int n, float a, float b, float c, int tile_choice,
-                       hipStream_t s);
+hipError_t launch_poly(const NsGroup* g, int n, float a, float b, float c,
+                       const GemmChoice& ch, hipStream_t s);
 // Xn = P X (times scale[i][k] where given), written row-major (and as X^T into
 // XTn for keeps_xt buckets); with `last`, only in the orientation of the parameter
 // (X^T when A > B: n_pad x m_pad, into XTn, or into Xn for one-orientation buckets)
 hipError_t launch_combine(const NsGroup* g, int n, const float* const* scale, bool last,
-                          int tile, hipStream_t s);
+                          const GemmChoice& ch, hipStream_t s);
 // One symmetric product per bucket: C = A B^T (= A B for symmetric B) on lower-triangle
 // tiles, mirrored, all m_pad x m_pad; exact only when A B is symmetric (A and B
 // polynomials in one matrix, as in the Gram-space iteration).  Tile as launch_poly's.
@@ -267,7 +282,7 @@ struct SymProd {
   const unsigned short* B;
   unsigned short* C;
 };
-hipError_t launch_sym(const SymProd* p, int n, int tile_choice, hipStream_t s);
+hipError_t launch_sym(const SymProd* p, int n, const GemmChoice& ch, hipStream_t s);
 // param <- param - lr*wd*mask*param - lr*scale*O with O = oscale[k] * (bf16 O) (oscale
 // may be null: 1), row stride ldo
 hipError_t launch_muon_apply(const BucketPlan& p, float* param, const unsigned short* O,

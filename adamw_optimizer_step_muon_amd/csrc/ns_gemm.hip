@@ -649,16 +649,20 @@ int env_int(const char* name, int dflt) {
 }
 
 // Fill the tile-grid and tile-order fields of one group's arguments (bm x bn tiles).
-void set_tiles(int epi, GemmArgs& a, const BucketPlan& p, int bm, int bn) {
-  // Defaults measured on the MI355X (env knobs for tuning): bands of 4 row panels for
-  // both tile orders, XCD renumbering on, spread DMA issue for 256-tiles only.
+void set_tiles(int epi, GemmArgs& a, const BucketPlan& p, int bm, int bn, const GemmChoice& ch) {
+  // Defaults measured on the MI355X (env knobs for tuning, a tuned choice above both):
+  // bands of 4 row panels for both tile orders, XCD renumbering on, spread DMA issue
+  // for 256-tiles only.
   static const int band_combine = env_int("MA_NS_BAND_COMBINE", 4);
   static const int band_tri = env_int("MA_NS_BAND_TRI", 4);
   static const int xcd = env_int("MA_NS_XCD", 1);
   static const int spread = env_int("MA_NS_SPREAD", -1);
-  a.band = epi == kCombine ? (band_combine > 0 ? band_combine : 1) : band_tri;
+  if (ch.band > 0) a.band = ch.band;
+  else a.band = epi == kCombine ? (band_combine > 0 ? band_combine : 1) : band_tri;
   a.xcd_remap = xcd;
-  a.spread = spread >= 0 ? spread : (bm >= 192 ? 1 : 0);
+  if (bm < 192) a.spread = 0;  // measured slower on 128-tiles
+  else if (ch.spread >= 0) a.spread = ch.spread ? 1 : 0;
+  else a.spread = spread >= 0 ? spread : 1;
   if (epi == kCombine) {
     a.tiles_m = static_cast<int>(p.m_pad / bm);
     a.tiles_n = static_cast<int>(p.n_pad / bn);
@@ -669,7 +673,23 @@ void set_tiles(int epi, GemmArgs& a, const BucketPlan& p, int bm, int bn) {
   }
 }
 
-hipError_t launch_table(int epi, GemmTable& t, TileCfg cfg, hipStream_t s) {
+// 256-tile kernel of the Gram-side products and of the X^T-reading combine: the 4-stage
+// k = 32 pipeline when chosen (or forced by MA_NS_BIG=1), else the 3 + 2 ring of k = 64
+bool use_big8(int pipeline) { return pipeline == 2 || (pipeline == 0 && big_variant() == 1); }
+
+TileShape shape_of(TileCfg cfg, int pipeline) {
+  switch (cfg) {
+    case kTileBig:
+      return use_big8(pipeline) ? TileShape{Big8::BM, Big8::BN, Big8::BK, Big8::kCombineReadsX}
+                                : TileShape{Big8K64::BM, Big8K64::BN, Big8K64::BK,
+                                            Big8K64::kCombineReadsX};
+    case kTileBigX: return TileShape{Big8K64X::BM, Big8K64X::BN, Big8K64X::BK, Big8K64X::kCombineReadsX};
+    case kTileMidX: return TileShape{Mid8X::BM, Mid8X::BN, Mid8X::BK, Mid8X::kCombineReadsX};
+    default: return TileShape{SmallCfg::BM, SmallCfg::BN, SmallCfg::BK, SmallCfg::kCombineReadsX};
+  }
+}
+
+hipError_t launch_table(int epi, GemmTable& t, TileCfg cfg, int pipeline, hipStream_t s) {
   // longest contraction first, so the blocks with the most work are dispatched first
   for (int i = 1; i < t.ngroups; ++i)
     for (int j = i; j > 0 && t.g[j].kdim > t.g[j - 1].kdim; --j) {
@@ -682,11 +702,11 @@ hipError_t launch_table(int epi, GemmTable& t, TileCfg cfg, hipStream_t s) {
     t.start[i + 1] = t.start[i] + ((t.g[i].tiles_per_batch * t.g[i].tiles_k + 7) & ~7);
   for (int i = t.ngroups + 1; i <= kMaxGemmGroups; ++i) t.start[i] = t.start[t.ngroups];
   if (LaunchRecorder* r = launch_recorder()) {
-    r->gemm(epi, cfg, t);
+    r->gemm(epi, shape_of(cfg, pipeline), t);
     return hipSuccess;
   }
   if (cfg == kTileBig)
-    return big_variant() == 1 ? launch_cfg<Big8>(epi, t, s) : launch_cfg<Big8K64>(epi, t, s);
+    return use_big8(pipeline) ? launch_cfg<Big8>(epi, t, s) : launch_cfg<Big8K64>(epi, t, s);
   if (cfg == kTileBigX) return launch_cfg<Big8K64X>(epi, t, s);
   if (cfg == kTileMidX) {
     if (epi != kCombine) return hipErrorInvalidValue;  // not a symmetric tile
@@ -707,18 +727,6 @@ int chosen_tile(const BucketPlan& p, int choice) {
 }
 
 }  // namespace
-
-TileShape tile_shape(TileCfg cfg) {
-  switch (cfg) {
-    case kTileBig:
-      return big_variant() == 1 ? TileShape{Big8::BM, Big8::BN, Big8::BK, Big8::kCombineReadsX}
-                                : TileShape{Big8K64::BM, Big8K64::BN, Big8K64::BK,
-                                            Big8K64::kCombineReadsX};
-    case kTileBigX: return TileShape{Big8K64X::BM, Big8K64X::BN, Big8K64X::BK, Big8K64X::kCombineReadsX};
-    case kTileMidX: return TileShape{Mid8X::BM, Mid8X::BN, Mid8X::BK, Mid8X::kCombineReadsX};
-    default: return TileShape{SmallCfg::BM, SmallCfg::BN, SmallCfg::BK, SmallCfg::kCombineReadsX};
-  }
-}
 
 bool combine_192_ok(const BucketPlan& p) {
   return p.tile == 256 && !p.keeps_xt && p.m_pad % Mid8X::BM == 0;
@@ -747,9 +755,9 @@ int pick_tile(int64_t K, int64_t m, int64_t n) {
              ? 256 : SmallCfg::BM;
 }
 
-hipError_t launch_gram(const NsGroup* g, int n, const float* const* scale, int tile,
-                       hipStream_t s) {
-  tile = chosen_tile(*g[0].plan, tile);
+hipError_t launch_gram(const NsGroup* g, int n, const float* const* scale,
+                       const GemmChoice& ch, hipStream_t s) {
+  const int tile = chosen_tile(*g[0].plan, ch.tile);
   GemmTable t{};
   t.ngroups = n;
   for (int i = 0; i < n; ++i) {
@@ -764,13 +772,14 @@ hipError_t launch_gram(const NsGroup* g, int n, const float* const* scale, int t
     a.strideC = a.strideC2 = p.m_pad * p.m_pad;
     a.scale = scale ? scale[i] : nullptr;
     a.tiles_k = static_cast<int>(p.K);
-    set_tiles(kGram, a, p, tile, tile);
+    set_tiles(kGram, a, p, tile, tile, ch);
   }
-  return launch_table(kGram, t, tile == 256 ? kTileBig : kTileSmall, s);
+  return launch_table(kGram, t, tile == 256 ? kTileBig : kTileSmall, ch.pipeline, s);
 }
 
-hipError_t launch_poly(const NsGroup* g, int n, float a_coef, float b, float c, int tile_choice,
-                       hipStream_t s) {
+hipError_t launch_poly(const NsGroup* g, int n, float a_coef, float b, float c,
+                       const GemmChoice& ch, hipStream_t s) {
+  const int tile_choice = ch.tile;
   // The polynomial contracts over the Gram side alone.  Where a 256-tile phase's
   // triangles fill less than two rounds of the chip, it runs on 128-tiles (two blocks
   // per CU, four times the blocks) over the same 256-padded layout: measured 17 %
@@ -798,12 +807,13 @@ hipError_t launch_poly(const NsGroup* g, int n, float a_coef, float b, float c, 
     a.strideAux = p.m_pad * p.m_pad;
     a.alpha = b; a.beta = c; a.diag = a_coef;
     a.tiles_k = static_cast<int>(p.K);
-    set_tiles(kPoly, a, p, tile, tile);
+    set_tiles(kPoly, a, p, tile, tile, ch);
   }
-  return launch_table(kPoly, t, tile == 256 ? kTileBig : kTileSmall, s);
+  return launch_table(kPoly, t, tile == 256 ? kTileBig : kTileSmall, ch.pipeline, s);
 }
 
-hipError_t launch_sym(const SymProd* pr, int n, int tile_choice, hipStream_t s) {
+hipError_t launch_sym(const SymProd* pr, int n, const GemmChoice& ch, hipStream_t s) {
+  const int tile_choice = ch.tile;
   // contracts over the Gram side like the polynomial: same tile rule
   int tile = chosen_tile(*pr[0].plan, tile_choice);
   if (tile_choice == 0 && tile == 256 && !forced_tile()) {
@@ -825,18 +835,18 @@ hipError_t launch_sym(const SymProd* pr, int n, int tile_choice, hipStream_t s) 
     a.strideC = a.strideC2 = p.m_pad * p.m_pad;
     a.symmetrize = 1;
     a.tiles_k = static_cast<int>(p.K);
-    set_tiles(kGram, a, p, tile, tile);
+    set_tiles(kGram, a, p, tile, tile, ch);
   }
-  return launch_table(kGram, t, tile == 256 ? kTileBig : kTileSmall, s);
+  return launch_table(kGram, t, tile == 256 ? kTileBig : kTileSmall, ch.pipeline, s);
 }
 
 hipError_t launch_combine(const NsGroup* g, int n, const float* const* scale, bool last,
-                          int tile, hipStream_t s) {
+                          const GemmChoice& ch, hipStream_t s) {
   // a phase's buckets agree on the tile and on keeping X^T; a 256-tile phase that reads
   // X (no X^T) may also run its combine on 128-tiles
-  bool mid = tile == 192 && !forced_tile();
+  bool mid = ch.tile == 192 && !forced_tile();
   for (int i = 0; i < n && mid; ++i) mid = combine_192_ok(*g[i].plan);
-  tile = g[0].plan->keeps_xt ? g[0].plan->tile : chosen_tile(*g[0].plan, tile);
+  const int tile = g[0].plan->keeps_xt ? g[0].plan->tile : chosen_tile(*g[0].plan, ch.tile);
   const TileCfg cfg = g[0].plan->keeps_xt ? kTileBig
                       : mid                ? kTileMidX
                       : tile == 256        ? kTileBigX
@@ -871,9 +881,9 @@ hipError_t launch_combine(const NsGroup* g, int n, const float* const* scale, bo
     }
     a.scale = scale ? scale[i] : nullptr;
     a.tiles_k = static_cast<int>(p.K);
-    set_tiles(kCombine, a, p, mid ? Mid8X::BM : tile, mid ? Mid8X::BN : tile);
+    set_tiles(kCombine, a, p, mid ? Mid8X::BM : tile, mid ? Mid8X::BN : tile, ch);
   }
-  return launch_table(kCombine, t, cfg, s);
+  return launch_table(kCombine, t, cfg, ch.pipeline, s);
 }
 
 }  // namespace ma

@@ -92,8 +92,9 @@ def parse():
                     help="1: Gram-space Newton-Schulz for buckets with n >= 2 m (opt-in; its "
                          "bf16 error is input-dependent)")
     ap.add_argument("--no-tune", action="store_true",
-                    help="keep the default GEMM tile rules instead of timing the tiles of each "
-                         "Newton-Schulz product once before the warm-up (ma_muon_tune)")
+                    help="keep the default GEMM rules instead of searching each Newton-Schulz "
+                         "product's configuration once before the warm-up "
+                         "(ma_muon_tune_configs)")
     ap.add_argument("--cpu-budget-s", type=float, default=20.0)
     ap.add_argument("--calibration-copy-mib", type=int, default=0,
                     help="after timing, copy this many MiB device-to-device once (a plain "
@@ -251,10 +252,11 @@ def main():
     stream = torch.cuda.current_stream(dev)
     state = {"t": 0}
     shapes = [(b.K, b.A, b.B) for b in wl.muon]
-    # per-shape GEMM tiles, timed once on the workspace (untimed set-up, like the warm-up)
-    ns_tiles = (ma.muon_phases(shapes, args.ns_mode)[0] * [[0, 0, 0]] if args.no_tune
-                else ma.muon_tune(shapes, reps=3, workspace=ws, stream=stream,
-                                  ns_mode=args.ns_mode))
+    # per-shape GEMM configurations (tile, pipeline, band width, spreading), searched once
+    # on the workspace (untimed set-up, like the warm-up)
+    ns_configs = (None if args.no_tune
+                  else ma.muon_tune_configs(shapes, reps=3, workspace=ws, stream=stream,
+                                            ns_mode=args.ns_mode, grads=[b[1] for b in buckets]))
 
     def adamw():
         ma.adamw_step(ap_, ag, am, av, step=state["t"], lr=ah.lr, beta1=ah.beta1, beta2=ah.beta2,
@@ -346,7 +348,7 @@ def main():
         "config": {"workload": wl.name, "muon_buckets": [[b.K, b.A, b.B] for b in wl.muon],
                    "adamw_elements": n, "ns_steps": mh.ns_steps, "ns_mode": args.ns_mode,
                    "cautious_wd": mh.cautious_wd},
-        "ns_tiles": ns_tiles,
+        "ns_configs": ns_configs,
         "step_ms_median": round(median_ms, 4),
         "step_ms_min": round(per_step[0], 4),
         "ns_tflops": round(ns_tflops, 2),

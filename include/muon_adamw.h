@@ -241,7 +241,39 @@ ma_status ma_muon_tune(const ma_muon_bucket* buckets, int32_t n_buckets,
                        const ma_muon_hparams* hp, void* workspace, size_t workspace_bytes,
                        void* stream, int32_t reps, int32_t* tiles);
 
-/* Host only: forget every tuned or pinned tile (back to the default rules). */
+/* The GEMM configuration of one Newton-Schulz product of a phase ([DMuon] section 2.4:
+ * tile shape, pipeline configuration, tile order).  A field at its default (0, or -1 for
+ * spread) takes the library's rule for it.  Every configuration accumulates each output
+ * over the same k order, so results are bitwise the same; only the time differs. */
+typedef struct {
+  int32_t tile;      /* 128 or 256 (on a 256-padded phase); 192 (combine, Gram sides padded
+                        to a multiple of 192); 0: the phase's rule */
+  int32_t band;      /* row panels per L2 band of the tile order, 1..64; 0: 4 */
+  int32_t spread;    /* 256- and 192-tiles: 1 spreads the next stage's operand loads over
+                        half a stage, 0 issues them at once; -1: 1 */
+  int32_t pipeline;  /* 256-tiles of the Gram, the polynomial and the combine of a phase
+                        that keeps X^T: 1 = stages of k = 64 in a ring of 3 A and 2 B
+                        stages, 2 = four stages of k = 32; 0: 1 */
+} ma_gemm_config;
+
+/* ma_muon_tune over whole configurations.  reps > 0: for each product of each phase,
+ * search one dimension at a time from the defaults -- tile, then pipeline (where the
+ * tile has a choice), then band width (2, 4, 8), then spreading -- timing each candidate
+ * as ma_muon_tune does; a candidate replaces the kept one only when at least 3 % faster.
+ * The result is reported in configs (host, 3 entries per phase: Gram, polynomial,
+ * combine; may be NULL).  SYNCHRONISES, as ma_muon_tune.  When every bucket of a phase
+ * gives its gradient pointer, the gradients are first cast into the workspace as
+ * ma_muon_step casts them (read only), so the candidates are timed on real operands: the
+ * matrix cores' power draw, and with it the clock, depends on the data.
+ * reps = 0: pin the given configs (all-default entries of a phase: back to the rules).
+ * Errors: as ma_muon_tune (a pinned configuration the phase cannot run:
+ * MA_ERR_INVALID_ARG). */
+ma_status ma_muon_tune_configs(const ma_muon_bucket* buckets, int32_t n_buckets,
+                               const ma_muon_hparams* hp, void* workspace,
+                               size_t workspace_bytes, void* stream, int32_t reps,
+                               ma_gemm_config* configs);
+
+/* Host only: forget every tuned or pinned configuration (back to the default rules). */
 void ma_muon_tune_reset(void);
 
 /* For callers that cannot allocate device memory (code under HIP graph capture, tight

@@ -452,3 +452,45 @@ def test_ns_time_reads_gradients_only():
     ms = ma.muon_ns_time(gs, reps=2)
     assert len(ms) == ma.muon_phases(shapes)[0] and all(t > 0 for t in ms)
     assert all(torch.equal(a, b) for a, b in zip(gs, before))
+
+
+def test_optimizer_buckets_a_models_matrices():
+    """MuonAdamW over the 12-layer GPT's 72 separate hidden matrices (per layer Q, K, V, O
+    768 x 768, MLP 768 x 3072 and 3072 x 768, interleaved as a model lists them): they
+    become three (K, A, B) buckets that run as one phase, the parameters the caller
+    holds see the updates, and two steps are bit for bit the stacked ma_muon_step's.
+    A third step where one matrix has no gradient leaves that matrix alone."""
+    wl = workloads.workload(1)
+    shapes = [(768, 768)] * 4 + [(768, 3072), (3072, 768)]
+    gen_ = torch.Generator(device=DEV).manual_seed(3)
+    params = [torch.nn.Parameter(torch.randn(s, generator=gen_, device=DEV))
+              for _ in range(12) for s in shapes]
+    grads = [[0.02 * torch.randn(p.shape, generator=gen_, device=DEV) for p in params]
+             for _ in range(3)]
+    stacks = [torch.stack([p.detach().clone() for p in params if tuple(p.shape) == s])
+              for s in [(768, 768), (768, 3072), (3072, 768)]]
+    opt = ma.MuonAdamW([{"params": params, "kind": "muon", "lr": LR, "momentum": MU,
+                         "weight_decay": WD}])
+    assert opt.muon_buckets() == [(48, 768, 768), (12, 768, 3072), (12, 3072, 768)]
+    assert ma.muon_phases(opt.muon_buckets()) == (1, [0, 0, 0])
+    moms = [torch.zeros_like(s) for s in stacks]
+    for t in range(2):
+        for p, g in zip(params, grads[t]):
+            p.grad = g.clone()
+        opt.step()
+        gst = [torch.stack([g for p, g in zip(params, grads[t]) if tuple(p.shape) == tuple(s.shape[1:])])
+               for s in stacks]
+        ma.muon_step(list(zip(stacks, gst, moms)), lr=LR, momentum=MU, weight_decay=WD)
+        torch.cuda.synchronize()
+        for s, st in zip([(768, 768), (768, 3072), (3072, 768)], stacks):
+            mine = [p.detach() for p in params if tuple(p.shape) == s]
+            assert all(torch.equal(a, b) for a, b in zip(mine, st)), (t, s)
+        opt.zero_grad()
+    keep = params[5].detach().clone()
+    for k, (p, g) in enumerate(zip(params, grads[2])):
+        p.grad = None if k == 5 else g.clone()
+    opt.step()
+    torch.cuda.synchronize()
+    assert torch.equal(params[5].detach(), keep)
+    assert not torch.equal(params[4].detach(), stacks[1][0])
+    del wl

@@ -105,3 +105,41 @@ def test_tuned_tiles_keep_results(case):
         assert _same(_step(state, ws), ref)
     finally:
         ma.muon_tune_reset()
+
+
+@pytest.mark.parametrize("case", ["gpt12", "keeps_xt"])
+def test_searched_configurations_keep_results(case):
+    """The full search (tile, pipeline, band width, spreading): the configuration it keeps
+    gives the default's result bit for bit, and so meets the oracle."""
+    shapes = CASES[case]
+    state = _state(shapes, 9)
+    ws = torch.empty(ma.muon_workspace_bytes(shapes), dtype=torch.uint8, device="cuda")
+    ma.muon_tune_reset()
+    try:
+        ref = _step(state, ws)
+        cfg = ma.muon_tune_configs(shapes, reps=2, workspace=ws)
+        print(f"{case}: searched {cfg}", flush=True)
+        assert len(cfg) == 1 and all(c["tile"] in (128, 192, 256) for c in cfg[0])
+        got = _step(state, ws)
+        assert _same(got, ref)
+        assert max(_oracle_errors(state, got)) <= MUON_RTOL
+    finally:
+        ma.muon_tune_reset()
+
+
+@pytest.mark.parametrize("config", [{"tile": 256, "pipeline": 2}, {"band": 2}, {"band": 8},
+                                    {"spread": 0}])
+def test_pinned_configurations_are_bitwise_identical(config):
+    """Each dimension pinned on its own for every product that accepts it (the 4096-wide
+    phase keeps X^T, so its combine has a pipeline choice too)."""
+    shapes = CASES["keeps_xt"]
+    state = _state(shapes, 10)
+    ws = torch.empty(ma.muon_workspace_bytes(shapes), dtype=torch.uint8, device="cuda")
+    ma.muon_tune_reset()
+    try:
+        ref = _step(state, ws)
+        ma.muon_tune_configs(shapes, reps=0, configs=[[config, config, config]])
+        got = _step(state, ws)
+        assert _same(got, ref), config
+    finally:
+        ma.muon_tune_reset()

@@ -125,3 +125,50 @@ def test_environment_tile_overrides(env):
     r = subprocess.run([sys.executable, "-c", _ENV_SCRIPT], cwd=ROOT, capture_output=True,
                        text=True, env={**os.environ, **env}, timeout=120)
     assert r.returncode == 0 and r.stdout.strip().endswith("ok"), r.stderr[-2000:]
+
+
+CONFIGS = [
+    {"tile": 256, "pipeline": 2}, {"tile": 256, "pipeline": 1, "band": 2},
+    {"tile": 256, "band": 8, "spread": 0}, {"tile": 128, "band": 1}, {"band": 16},
+    {"spread": 1}, {"tile": 192, "band": 3, "spread": 0},
+]
+
+
+@pytest.mark.parametrize("index", range(5))
+def test_workload_plans_under_pinned_configurations(index):
+    """Every configuration dimension the tuner searches (tile, pipeline, band width,
+    spreading), pinned per product wherever the phase accepts it."""
+    shapes = _shapes(index)
+    nph = ma.muon_phases(shapes)[0]
+    tried = 0
+    try:
+        for ph in range(nph):
+            for q in range(3):
+                for c in CONFIGS:
+                    cfg = [[{}, {}, {}] for _ in range(nph)]
+                    cfg[ph][q] = c
+                    try:
+                        ma.muon_tune_configs(shapes, reps=0, configs=cfg)
+                    except _lib.MuonAdamWError as e:
+                        assert e.status == _lib.MA_ERR_INVALID_ARG
+                        continue
+                    ma.muon_check_plan(shapes)
+                    tried += 1
+    finally:
+        ma.muon_tune_reset()
+    assert tried >= 3 * nph
+
+
+def test_configuration_pins_are_validated():
+    shapes = [(48, 768, 768), (12, 768, 3072), (12, 3072, 768)]
+    bad = [{"tile": 128, "pipeline": 2}, {"pipeline": 3}, {"band": 65}, {"spread": 2},
+           {"tile": 512}]
+    for c in bad:
+        with pytest.raises(_lib.MuonAdamWError):
+            ma.muon_tune_configs(shapes, reps=0, configs=[[c, {}, {}]])
+    # the combine of this phase reads X (no X^T): no pipeline choice there
+    with pytest.raises(_lib.MuonAdamWError):
+        ma.muon_tune_configs(shapes, reps=0, configs=[[{}, {}, {"pipeline": 2}]])
+    got = ma.muon_tune_configs(shapes, reps=0, configs=[[{"pipeline": 2}, {}, {"tile": 192}]])
+    assert got[0][0]["pipeline"] == 2 and got[0][2]["tile"] == 192
+    ma.muon_tune_reset()
