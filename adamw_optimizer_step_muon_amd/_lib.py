@@ -28,7 +28,7 @@ EXPORTED = (
     "ma_muon_workspace_bytes", "ma_muon_phases", "ma_muon_step", "ma_adamw_step",
     "ma_newton_schulz_workspace_bytes", "ma_newton_schulz", "ma_muon_tune", "ma_muon_tune_reset",
     "ma_adamw_step_multi", "ma_muon_check_plan", "ma_muon_ns_time", "ma_muon_static_init",
-    "ma_muon_step_static", "ma_muon_tune_configs",
+    "ma_muon_step_static", "ma_muon_tune_configs", "ma_stream_probe",
 )
 MA_STATIC_WORKSPACE_BYTES = 512 << 20
 
@@ -147,6 +147,10 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
                                          ctypes.POINTER(_MuonHParams), ctypes.c_void_p,
                                          ctypes.c_size_t, ctypes.c_void_p, ctypes.c_int32,
                                          ctypes.POINTER(_GemmConfig)]
+    lib.ma_stream_probe.restype = ctypes.c_int
+    lib.ma_stream_probe.argtypes = [ctypes.POINTER(ctypes.c_void_p), ctypes.c_int32,
+                                    ctypes.POINTER(ctypes.c_void_p), ctypes.c_int32,
+                                    ctypes.c_int64, ctypes.c_void_p]
     lib.ma_muon_tune_reset.restype = None
     lib.ma_muon_tune_reset.argtypes = []
     lib.ma_muon_check_plan.restype = ctypes.c_int
@@ -554,3 +558,19 @@ def muon_ns_time(grads, *, reps: int = 3, ns_steps: int = 5, ns_coeffs=None, ns_
                                _stream_handle(stream, device) if device is not None else 0,
                                int(reps), out))
     return [float(out[i]) for i in range(nph)]
+
+
+def stream_probe(inputs, outputs, *, stream=None) -> None:
+    """The reference stream of ma_stream_probe: reads every tensor of `inputs` (1-4) and
+    writes every tensor of `outputs` (0-3), all contiguous fp32 GPU tensors of one size
+    (a multiple of 4), with the AdamW kernel's access pattern and no other arithmetic."""
+    ts = list(inputs) + list(outputs)
+    for i, t in enumerate(ts):
+        _require_f32_cuda(f"array {i}", t)
+    n = ts[0].numel()
+    if any(t.numel() != n for t in ts):
+        raise ValueError("arrays differ in size")
+    ins = (ctypes.c_void_p * 4)(*([_ptr(t) for t in inputs] + [0] * (4 - len(inputs))))
+    outs = (ctypes.c_void_p * 3)(*([_ptr(t) for t in outputs] + [0] * (3 - len(outputs))))
+    _check(load().ma_stream_probe(ins, len(inputs), outs, len(outputs), n,
+                                  _stream_handle(stream, ts[0].device)))

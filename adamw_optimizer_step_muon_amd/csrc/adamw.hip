@@ -242,7 +242,64 @@ __global__ __launch_bounds__(kThreads) void adamw_multi_kernel(AdamWSegTable tab
   }
 }
 
+// Reference stream for the bandwidth ceiling of an access pattern: R fp32 arrays read,
+// W written (out[j] = in[0] + ... + in[R-1] + j), float4 groups with the same
+// non-temporal accesses and the same 4 groups per thread as adamw_vec_kernel, and no
+// other arithmetic.
+struct ProbePtrs {
+  const f32x4* in[4];
+  f32x4* out[3];
+};
+
+template <int R, int W>
+__global__ __launch_bounds__(kThreads) void stream_probe_entry(ProbePtrs p, int64_t n4) {
+  // the pointer table lives in the kernel arguments
+  const f32x4* const* in = p.in;
+  f32x4* const* out = p.out;
+  const int64_t base = static_cast<int64_t>(blockIdx.x) * (kThreads * 4) + threadIdx.x;
+  f32x4 acc[4];
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    const int64_t i = base + static_cast<int64_t>(u) * kThreads;
+    acc[u] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+    if (i < n4) {
+#pragma unroll
+      for (int r = 0; r < R; ++r) acc[u] += __builtin_nontemporal_load(&in[r][i]);
+    }
+  }
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    const int64_t i = base + static_cast<int64_t>(u) * kThreads;
+    if (i < n4) {
+#pragma unroll
+      for (int w = 0; w < W; ++w) __builtin_nontemporal_store(acc[u] + static_cast<float>(w), &out[w][i]);
+    }
+  }
+}
+
 }  // namespace
+
+hipError_t launch_stream_probe(const float* const* in, int reads, float* const* out, int writes,
+                               int64_t n, hipStream_t s) {
+  ProbePtrs p{};
+  for (int r = 0; r < reads; ++r) p.in[r] = reinterpret_cast<const f32x4*>(in[r]);
+  for (int w = 0; w < writes; ++w) p.out[w] = reinterpret_cast<f32x4*>(out[w]);
+  const int64_t n4 = n / 4;
+  const int64_t blocks = (n4 + kThreads * 4 - 1) / (kThreads * 4);
+  if (blocks <= 0) return hipSuccess;
+  const dim3 grid(static_cast<unsigned>(blocks));
+#define MA_PROBE(R, W)                                                                        \
+  if (reads == R && writes == W) {                                                           \
+    hipLaunchKernelGGL((stream_probe_entry<R, W>), grid, dim3(kThreads), 0, s, p, n4);     \
+    return hipGetLastError();                                                                \
+  }
+  MA_PROBE(1, 0) MA_PROBE(2, 0) MA_PROBE(3, 0) MA_PROBE(4, 0)
+  MA_PROBE(1, 1) MA_PROBE(2, 1) MA_PROBE(3, 1) MA_PROBE(4, 1)
+  MA_PROBE(1, 2) MA_PROBE(2, 2) MA_PROBE(3, 2) MA_PROBE(4, 2)
+  MA_PROBE(1, 3) MA_PROBE(2, 3) MA_PROBE(3, 3) MA_PROBE(4, 3)
+#undef MA_PROBE
+  return hipErrorInvalidValue;
+}
 
 int64_t adamw_multi_blocks(int64_t n) { return (n + kMultiChunk - 1) / kMultiChunk; }
 

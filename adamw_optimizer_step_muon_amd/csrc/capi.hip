@@ -1315,6 +1315,33 @@ ma_status ma_muon_ns_time(const ma_muon_bucket* buckets, int32_t n_buckets,
   return st;
 }
 
+ma_status ma_stream_probe(const float* const* in, int32_t reads, float* const* out,
+                          int32_t writes, int64_t n, void* stream) {
+  g_last_error.clear();
+  if (reads < 1 || reads > 4 || writes < 0 || writes > 3)
+    return fail(MA_ERR_INVALID_ARG, "reads %d / writes %d outside 1..4 / 0..3", reads, writes);
+  if (n < 0 || n % 4) return fail(MA_ERR_INVALID_ARG, "n = %lld is not a multiple of 4", (long long)n);
+  if (n == 0) return MA_OK;
+  if (!in || (writes > 0 && !out)) return fail(MA_ERR_INVALID_ARG, "NULL pointer table");
+  // an output may be exactly one of the inputs (streamed in place, as the AdamW step
+  // updates p, m and v); any other overlap is rejected
+  std::vector<Range> rs;
+  for (int i = 0; i < reads + writes; ++i) {
+    const void* q = i < reads ? static_cast<const void*>(in[i]) : static_cast<const void*>(out[i - reads]);
+    if (!q || (reinterpret_cast<uintptr_t>(q) & 15u))
+      return fail(MA_ERR_INVALID_ARG, "array %d NULL or not 16-byte aligned", i);
+    const Range r = range_of(q, n * 4);
+    for (size_t k = 0; k < rs.size(); ++k) {
+      const bool in_place = i >= reads && static_cast<int>(k) < reads && rs[k].lo == r.lo;
+      if (overlap(r, rs[k]) && !in_place) return fail(MA_ERR_INVALID_ARG, "arrays overlap");
+    }
+    rs.push_back(r);
+  }
+  const hipError_t e = launch_stream_probe(in, reads, out, writes, n, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "probe launch");
+  return MA_OK;
+}
+
 ma_status ma_adamw_step(float* param, const float* grad, float* exp_avg, float* exp_avg_sq,
                         int64_t n, const ma_adamw_hparams* hp, void* stream) {
   g_last_error.clear();

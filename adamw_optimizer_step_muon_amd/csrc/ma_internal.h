@@ -314,6 +314,10 @@ struct AdamWSegTable {
   AdamWConst c;
 };
 int64_t adamw_multi_blocks(int64_t n);
+// Reference stream: `reads` (1..4) fp32 arrays in, `writes` (0..3) out, n elements
+// (n % 4 == 0, 16-byte aligned), the AdamW kernel's access pattern without its arithmetic.
+hipError_t launch_stream_probe(const float* const* in, int reads, float* const* out, int writes,
+                               int64_t n, hipStream_t s);
 hipError_t launch_adamw_multi(const AdamWSegTable& t, hipStream_t s);
 
 }  // namespace ma

@@ -330,6 +330,12 @@ def main():
     adamw_gbs = ADAMW_BYTES_PER_ELEM * n / (adamw_ms * 1e-3) / 1e9
     clock = counted_traffic(f"ns_gemm_mfma_workload{args.workload}.txt", "ns_gemm.hip",
                             key="clock_ghz")
+    # the ceiling of AdamW's access pattern on this part: the same 4-read / 3-write stream
+    # in place over the same buffers, with the same accesses and no arithmetic (last:
+    # it overwrites the AdamW state)
+    probe_ms = timed(lambda: ma.stream_probe([ap_, ag, am, av], [ap_, am, av], stream=stream),
+                     reps)
+    probe_gbs = ADAMW_BYTES_PER_ELEM * n / (probe_ms * 1e-3) / 1e9
 
     out = {
         "metric": "optimizer-step ms + NS TFLOP/s (%MFMA peak) + AdamW GB/s (%HBM)",
@@ -396,6 +402,10 @@ def main():
             "frac": round(adamw_gbs / HBM_PEAK_GBS, 4),
             "traffic": counted_traffic(f"adamw_traffic_workload{args.workload}.txt", "adamw.hip"),
             "bytes_per_launch": ADAMW_BYTES_PER_ELEM * n,
+            # a 4-read / 3-write fp32 stream in place with AdamW's accesses and no
+            # arithmetic (ma_stream_probe), timed here: the access pattern's own ceiling
+            "stream_ceiling_gbs": round(probe_gbs, 1),
+            "frac_of_stream_ceiling": round(adamw_gbs / probe_gbs, 4),
         },
         "timed_wall_s": round(wall_s, 3),
     }

@@ -185,6 +185,17 @@ ma_status ma_muon_step(const ma_muon_bucket* buckets, int32_t n_buckets,
 ma_status ma_adamw_step(float* param, const float* grad, float* exp_avg, float* exp_avg_sq,
                         int64_t n, const ma_adamw_hparams* hp, void* stream);
 
+/* A benchmark aid: the bandwidth ceiling of an elementwise access pattern.  Streams
+ * `reads` fp32 arrays in (1..4) and `writes` out (0..3), n elements each (n % 4 == 0,
+ * every array 16-byte aligned; an output may be exactly one of the inputs, streamed in
+ * place, other overlaps are rejected), with the access pattern of the AdamW
+ * kernel (float4 groups, non-temporal loads and stores, four groups per thread) and no
+ * other arithmetic: out[j] = in[0] + ... + in[reads-1] + j.  reads = 4, writes = 3 is
+ * the AdamW step's pattern (28 bytes per element).  in, out: host arrays of device
+ * pointers.  Errors: MA_ERR_INVALID_ARG, MA_ERR_HIP. */
+ma_status ma_stream_probe(const float* const* in, int32_t reads, float* const* out,
+                          int32_t writes, int64_t n, void* stream);
+
 /* One AdamW tensor of ma_adamw_step_multi: n fp32 elements at each pointer (device). */
 typedef struct {
   float* param;

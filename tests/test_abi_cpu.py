@@ -404,3 +404,22 @@ def test_adamw_step_multi_overlap_sweep_matches_brute_force(lib):
         tried += 1
         assert lib.ma_adamw_step_multi(segs, k, ctypes.byref(hp), None) == _lib.MA_ERR_INVALID_ARG
         assert b"overlap" in lib.ma_last_error()
+
+
+def test_stream_probe_rejects_before_launch(lib):
+    P = ctypes.c_void_p
+    base = 1 << 40
+    n = 4096
+    ins = (P * 4)(base, base + 1 * 65536, base + 2 * 65536, base + 3 * 65536)
+    outs = (P * 3)(base + 4 * 65536, base + 5 * 65536, base + 6 * 65536)
+    assert lib.ma_stream_probe(ins, 0, outs, 1, n, None) == _lib.MA_ERR_INVALID_ARG
+    assert lib.ma_stream_probe(ins, 5, outs, 1, n, None) == _lib.MA_ERR_INVALID_ARG
+    assert lib.ma_stream_probe(ins, 2, outs, 4, n, None) == _lib.MA_ERR_INVALID_ARG
+    assert lib.ma_stream_probe(ins, 2, outs, 1, n + 2, None) == _lib.MA_ERR_INVALID_ARG
+    assert lib.ma_stream_probe(ins, 2, outs, 1, 0, None) == _lib.MA_OK
+    bad = (P * 4)(base + 4, base + 65536, 0, 0)   # misaligned
+    assert lib.ma_stream_probe(bad, 2, outs, 1, n, None) == _lib.MA_ERR_INVALID_ARG
+    part = (P * 3)(base + 8192, 0, 0)              # overlaps input 0 without being it
+    assert lib.ma_stream_probe(ins, 2, part, 1, n, None) == _lib.MA_ERR_INVALID_ARG
+    two = (P * 4)(base, base + 8192, 0, 0)         # two overlapping inputs
+    assert lib.ma_stream_probe(two, 2, outs, 1, n, None) == _lib.MA_ERR_INVALID_ARG

@@ -224,3 +224,19 @@ def test_adamw_non_finite_gradient_stays_in_its_element():
     for a, b in zip(got, clean):
         assert np.isnan(a[mask]).all()
         assert np.array_equal(a[~mask], b[~mask])
+
+
+def test_stream_probe_values():
+    """The bandwidth probe computes what it states (so its loads and stores are real):
+    out[j] = in[0] + ... + in[R-1] + j, also streamed in place."""
+    n = 1 << 16
+    gen_ = torch.Generator(device="cuda").manual_seed(4)
+    a, b, c, d = (torch.randn(n, generator=gen_, device="cuda") for _ in range(4))
+    o1, o2 = torch.empty_like(a), torch.empty_like(a)
+    ma.stream_probe([a, b, c], [o1, o2])
+    torch.cuda.synchronize()
+    assert torch.equal(o1, ((a + b) + c)) and torch.equal(o2, ((a + b) + c) + 1.0)
+    ref = ((a + b) + c) + d
+    ma.stream_probe([a, b, c, d], [a, c, d])
+    torch.cuda.synchronize()
+    assert torch.equal(a, ref) and torch.equal(c, ref + 1.0) and torch.equal(d, ref + 2.0)
