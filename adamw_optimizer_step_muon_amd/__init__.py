@@ -6,13 +6,14 @@ parameter-group wrapper.  PyTorch supplies device memory and streams only.
 """
 from ._lib import (LIB_PATH, MuonAdamWError, Route, abi_version, adamw_step, adamw_step_multi, load,
                    muon_check_plan, muon_ns_time, muon_phases, muon_route_of, muon_step,
-                   muon_step_static, muon_tune, muon_tune_configs, muon_tune_reset,
+                   muon_static_init, muon_step_static, muon_tune, muon_tune_configs,
+                   muon_tune_reset,
                    muon_workspace_bytes, newton_schulz, newton_schulz_workspace_bytes,
                    stream_probe)
 from .optim import MuonAdamW
 
 __all__ = ["LIB_PATH", "MuonAdamWError", "Route", "abi_version", "adamw_step", "adamw_step_multi",
            "load", "muon_check_plan", "muon_ns_time", "muon_phases", "muon_route_of",
-           "muon_step", "muon_step_static", "muon_tune", "muon_tune_configs", "muon_tune_reset",
+           "muon_static_init", "muon_step", "muon_step_static", "muon_tune", "muon_tune_configs", "muon_tune_reset",
            "muon_workspace_bytes", "newton_schulz", "newton_schulz_workspace_bytes",
            "stream_probe", "MuonAdamW"]

@@ -61,7 +61,7 @@ class _MuonRoute(ctypes.Structure):
 
 class _GemmConfig(ctypes.Structure):
     _fields_ = [("tile", ctypes.c_int32), ("band", ctypes.c_int32), ("spread", ctypes.c_int32),
-                ("pipeline", ctypes.c_int32)]
+                ("pipeline", ctypes.c_int32), ("xcd", ctypes.c_int32)]
 
 
 class _PlanReport(ctypes.Structure):
@@ -335,17 +335,18 @@ def muon_tune(shapes: Sequence[Sequence[int]], *, reps: int = 3, tiles=None, wor
     return [[int(out[3 * i + q]) for q in range(3)] for i in range(nph)]
 
 
-CONFIG_KEYS = ("tile", "band", "spread", "pipeline")
-DEFAULT_CONFIG = {"tile": 0, "band": 0, "spread": -1, "pipeline": 0}
+CONFIG_KEYS = ("tile", "band", "spread", "pipeline", "xcd")
+DEFAULT_CONFIG = {"tile": 0, "band": 0, "spread": -1, "pipeline": 0, "xcd": 0}
 
 
 def muon_tune_configs(shapes: Sequence[Sequence[int]], *, reps: int = 3, configs=None,
                       workspace=None, stream=None, device=None, ns_mode: int = 0, grads=None):
     """Per-shape Newton-Schulz GEMM configurations (ma_muon_tune_configs) for buckets of
-    these (K, A, B) shapes.  reps > 0: search tile, pipeline, band width and spreading on
+    these (K, A, B) shapes.  reps > 0: search tile, pipeline, band width, spreading and
+    XCD order on
     the workspace (scratch; allocated for the call when None) and keep the fastest;
     reps == 0: pin `configs` (per phase, three dicts with keys tile, band, spread,
-    pipeline; missing keys take their defaults).  grads: the buckets' (K, A, B) gradients,
+    pipeline, xcd; missing keys take their defaults).  grads: the buckets' (K, A, B) gradients,
     cast into the workspace before the timing so the candidates run on real operands.
     Returns the configurations in force."""
     import torch
@@ -382,6 +383,12 @@ def muon_tune_configs(shapes: Sequence[Sequence[int]], *, reps: int = 3, configs
                                         _stream_handle(stream, device), int(reps), out))
     return [[{k: int(getattr(out[3 * i + q], k)) for k in CONFIG_KEYS} for q in range(3)]
             for i in range(nph)]
+
+
+def muon_static_init() -> None:
+    """Resolve the current device's static workspace (ma_muon_static_init); call before
+    capturing muon_step_static in a graph."""
+    _check(load().ma_muon_static_init())
 
 
 def muon_tune_reset() -> None:

@@ -259,12 +259,13 @@ bool has_pipeline_choice(const Phase& ph, int prod, int tile) {
 }
 
 // A pinned configuration the phase can run: tile available (or 0), pipeline 0..2 (1, 2
-// only where has_pipeline_choice), band 0..64, spread -1..1.
+// only where has_pipeline_choice), band 0..64, spread -1..1, xcd 0..2.
 bool choice_valid(const Phase& ph, int prod, const GemmChoice& c) {
   if (c.tile != 0 && !tile_available(ph, prod, c.tile)) return false;
   if (c.pipeline < 0 || c.pipeline > 2) return false;
   if (c.pipeline != 0 && !has_pipeline_choice(ph, prod, c.tile)) return false;
-  return c.band >= 0 && c.band <= 64 && c.spread >= -1 && c.spread <= 1;
+  return c.band >= 0 && c.band <= 64 && c.spread >= -1 && c.spread <= 1 && c.xcd >= 0 &&
+         c.xcd <= 2;
 }
 
 template <class T>
@@ -718,18 +719,20 @@ GemmChoice to_choice(const ma_gemm_config& c) {
   g.band = c.band;
   g.spread = c.spread;
   g.pipeline = c.pipeline;
+  g.xcd = c.xcd;
   return g;
 }
 
 ma_gemm_config to_config(const GemmChoice& g) {
-  return ma_gemm_config{g.tile, g.band, g.spread, g.pipeline};
+  return ma_gemm_config{g.tile, g.band, g.spread, g.pipeline, g.xcd};
 }
 
 // ma_muon_tune and ma_muon_tune_configs.  cfg: 3 entries per phase, input when reps = 0
 // (pin), output when reps > 0 (search).  The search, per product of each phase, times
 // candidates one dimension at a time from the defaults: the tile, then (for the 256-tile
 // kernels with a choice) the pipeline, then the L2 band width (2, 4, 8 row panels), then
-// (256- and 192-tiles) the DMA spreading; each candidate runs once to warm up and `reps`
+// (256- and 192-tiles) the DMA spreading, then the XCD block order; each candidate runs
+// once to warm up and `reps`
 // times between two HIP events on the phase's workspace operands (the buckets'
 // gradients cast there first when every bucket of the phase gives one), and replaces the
 // kept one only when at least 3 % faster.  tiles_only: the tile alone.
@@ -756,9 +759,9 @@ ma_status tune_impl(const ma_muon_bucket* buckets, int32_t n_buckets, const ma_m
         if (!choice_valid(ph, q, to_choice(cfg[3 * phase + q])))
           return fail(MA_ERR_INVALID_ARG,
                       "phase %d, product %d: configuration (tile %d, band %d, spread %d, "
-                      "pipeline %d) is not available", phase, q, cfg[3 * phase + q].tile,
+                      "pipeline %d, xcd %d) is not available", phase, q, cfg[3 * phase + q].tile,
                       cfg[3 * phase + q].band, cfg[3 * phase + q].spread,
-                      cfg[3 * phase + q].pipeline);
+                      cfg[3 * phase + q].pipeline, cfg[3 * phase + q].xcd);
       ++phase;
       return MA_OK;
     });
@@ -887,6 +890,14 @@ ma_status tune_impl(const ma_muon_bucket* buckets, int32_t n_buckets, const ma_m
             const hipError_t e = consider(t);
             if (e != hipSuccess) return hip_fail(e, "tuning launch");
           }
+        // 5. block order across the XCDs
+        const GemmChoice base4 = cur;
+        for (int x : {1, 2}) {
+          GemmChoice t = base4;
+          t.xcd = x;
+          const hipError_t e = consider(t);
+          if (e != hipSuccess) return hip_fail(e, "tuning launch");
+        }
       }
       best[q] = cur;
       cfg[3 * phase + q] = to_config(cur);
@@ -1112,7 +1123,7 @@ ma_status ma_muon_tune(const ma_muon_bucket* buckets, int32_t n_buckets,
   const int32_t nph = ma_muon_phases(buckets, n_buckets, hp, nullptr);
   if (nph < 0) return static_cast<ma_status>(nph);
   std::vector<ma_gemm_config> cfg(static_cast<size_t>(3 * std::max(nph, 1)),
-                                  ma_gemm_config{0, 0, -1, 0});
+                                  ma_gemm_config{0, 0, -1, 0, 0});
   if (reps == 0)
     for (int i = 0; i < 3 * nph; ++i) cfg[i].tile = tiles[i];
   const ma_status st = tune_impl(buckets, n_buckets, hp, workspace, workspace_bytes, stream, reps,
@@ -1131,7 +1142,7 @@ ma_status ma_muon_tune_configs(const ma_muon_bucket* buckets, int32_t n_buckets,
   const int32_t nph = ma_muon_phases(buckets, n_buckets, hp, nullptr);
   if (nph < 0) return static_cast<ma_status>(nph);
   std::vector<ma_gemm_config> cfg(static_cast<size_t>(3 * std::max(nph, 1)),
-                                  ma_gemm_config{0, 0, -1, 0});
+                                  ma_gemm_config{0, 0, -1, 0, 0});
   if (reps == 0)
     for (int i = 0; i < 3 * nph; ++i) cfg[i] = configs[i];
   const ma_status st = tune_impl(buckets, n_buckets, hp, workspace, workspace_bytes, stream, reps,

@@ -234,8 +234,10 @@ struct GemmChoice {
   int pipeline = 0;  // 256-tiles of the Gram, polynomial and X^T-reading combine:
                      // 1 = stages of k = 64 in a 3 + 2 ring, 2 = 4 stages of k = 32
                      // (default 1)
+  int xcd = 0;       // 1 = blocks renumbered XCD by XCD, 2 = round-robin order (default 1)
   bool operator==(const GemmChoice& o) const {
-    return tile == o.tile && band == o.band && spread == o.spread && pipeline == o.pipeline;
+    return tile == o.tile && band == o.band && spread == o.spread && pipeline == o.pipeline &&
+           xcd == o.xcd;
   }
   bool is_default() const { return *this == GemmChoice{}; }
 };

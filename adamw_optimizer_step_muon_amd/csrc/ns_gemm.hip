@@ -659,7 +659,7 @@ void set_tiles(int epi, GemmArgs& a, const BucketPlan& p, int bm, int bn, const 
   static const int spread = env_int("MA_NS_SPREAD", -1);
   if (ch.band > 0) a.band = ch.band;
   else a.band = epi == kCombine ? (band_combine > 0 ? band_combine : 1) : band_tri;
-  a.xcd_remap = xcd;
+  a.xcd_remap = ch.xcd == 1 ? 1 : ch.xcd == 2 ? 0 : xcd;
   if (bm < 192) a.spread = 0;  // measured slower on 128-tiles
   else if (ch.spread >= 0) a.spread = ch.spread ? 1 : 0;
   else a.spread = spread >= 0 ? spread : 1;

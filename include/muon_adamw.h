@@ -265,11 +265,15 @@ typedef struct {
   int32_t pipeline;  /* 256-tiles of the Gram, the polynomial and the combine of a phase
                         that keeps X^T: 1 = stages of k = 64 in a ring of 3 A and 2 B
                         stages, 2 = four stages of k = 32; 0: 1 */
+  int32_t xcd;       /* block order across the 8 XCDs: 1 = each XCD takes a contiguous run
+                        of tiles (so its L2 serves neighbouring tiles), 2 = the hardware's
+                        round-robin order; 0: 1 */
 } ma_gemm_config;
 
 /* ma_muon_tune over whole configurations.  reps > 0: for each product of each phase,
  * search one dimension at a time from the defaults -- tile, then pipeline (where the
- * tile has a choice), then band width (2, 4, 8), then spreading -- timing each candidate
+ * tile has a choice), then band width (2, 4, 8), then spreading, then the XCD order --
+ * timing each candidate
  * as ma_muon_tune does; a candidate replaces the kept one only when at least 3 % faster.
  * The result is reported in configs (host, 3 entries per phase: Gram, polynomial,
  * combine; may be NULL).  SYNCHRONISES, as ma_muon_tune.  When every bucket of a phase

@@ -44,6 +44,29 @@ def test_muon_step_graph_replays_match_eager(ns_mode):
             assert torch.equal(a, b), step
 
 
+def test_static_workspace_step_graph_replays_match_eager():
+    """ma_muon_step_static, the entry point for callers that cannot allocate, captured in
+    a HIP graph (its workspace resolved once before the capture): replays with eager work
+    between them match eager ma_muon_step calls on a caller workspace bit for bit."""
+    ps, gs, ms = _state(8)
+    ps_e, ms_e = [p.clone() for p in ps], [m.clone() for m in ms]
+    ws_e = torch.empty(ma.muon_workspace_bytes(SHAPES), dtype=torch.uint8, device=DEV)
+    hp = dict(lr=0.02, momentum=0.95, weight_decay=0.1)
+    ma.muon_static_init()
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        ma.muon_step_static(list(zip(ps, gs, ms)), **hp)
+    for step in range(3):
+        graph.replay()
+        torch.cuda.synchronize()
+        _ = (torch.ones(1024, device=DEV) * step).sum().item()  # eager work between replays
+        ma.muon_step(list(zip(ps_e, gs, ms_e)), workspace=ws_e, **hp)
+        torch.cuda.synchronize()
+        for a, b in zip(ps + ms, ps_e + ms_e):
+            assert torch.equal(a, b), step
+
+
 def test_adamw_step_graph_replay_matches_eager():
     g = torch.Generator(device=DEV)
     g.manual_seed(6)

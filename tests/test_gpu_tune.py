@@ -128,7 +128,7 @@ def test_searched_configurations_keep_results(case):
 
 
 @pytest.mark.parametrize("config", [{"tile": 256, "pipeline": 2}, {"band": 2}, {"band": 8},
-                                    {"spread": 0}])
+                                    {"spread": 0}, {"xcd": 2}])
 def test_pinned_configurations_are_bitwise_identical(config):
     """Each dimension pinned on its own for every product that accepts it (the 4096-wide
     phase keeps X^T, so its combine has a pipeline choice too)."""

@@ -64,11 +64,11 @@ int main() {
         std::vector<int32_t> tiles(3 * nph, 128);
         ma_muon_tune(l.data(), (int)l.size(), &hp, nullptr, 0, nullptr, 0, tiles.data());
         EXPECT(ma_muon_check_plan(l.data(), (int)l.size(), &hp, 0, &rep) == MA_OK);
-        std::vector<ma_gemm_config> cfg(3 * nph, ma_gemm_config{0, 8, -1, 0});
+        std::vector<ma_gemm_config> cfg(3 * nph, ma_gemm_config{0, 8, -1, 0, 2});
         EXPECT(ma_muon_tune_configs(l.data(), (int)l.size(), &hp, nullptr, 0, nullptr, 0,
                                     cfg.data()) == MA_OK);
         EXPECT(ma_muon_check_plan(l.data(), (int)l.size(), &hp, 0, &rep) == MA_OK);
-        cfg.assign(3 * nph, ma_gemm_config{0, 0, -1, 7});
+        cfg.assign(3 * nph, ma_gemm_config{0, 0, -1, 7, 0});
         EXPECT(ma_muon_tune_configs(l.data(), (int)l.size(), &hp, nullptr, 0, nullptr, 0,
                                     cfg.data()) == MA_ERR_INVALID_ARG);
         ma_muon_tune_reset();
