@@ -163,6 +163,11 @@ int32_t ma_muon_phases(const ma_muon_bucket* buckets, int32_t n_buckets,
  *   O <- X (un-transposed);
  *   s <- scale(A, B);  P <- P - eta lambda [mask] P - eta s O,
  *   mask = (s O * P > 0) when cautious_wd, else 1.
+ * Range: any finite fp32 gradients and momenta whose sum mu M + G stays finite.  ||U||_F
+ * is summed in fp64, and a matrix whose norm lies outside [2^-32, 2^32] has its bf16 copy
+ * multiplied by a power of two before the first product (exact), so the fp32
+ * accumulation of the first Gram product neither overflows nor loses its small terms.
+ * NaN or Inf in a matrix's gradient makes that matrix's update non-finite (no scrubbing).
  * buckets:    host array of n_buckets descriptors (n_buckets >= 0).
  * workspace:  device, 256-byte aligned, at least ma_muon_workspace_bytes(...) bytes;
  *             may be NULL when that is 0.  Its contents are scratch.
