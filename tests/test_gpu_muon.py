@@ -494,3 +494,59 @@ def test_optimizer_buckets_a_models_matrices():
     assert torch.equal(params[5].detach(), keep)
     assert not torch.equal(params[4].detach(), stacks[1][0])
     del wl
+
+
+def test_newton_schulz_maximum_iteration_count():
+    """MA_MAX_NS_STEPS (64) iterations of the cubic (1.5, -0.5, 0), which converges to the
+    polar factor U V^T and is contractive there, so bf16 rounding does not accumulate:
+    against the oracle and against numpy's U V^T."""
+    G = _grad((96, 160), 71)[None]
+    gi = torch.from_numpy(G).to(DEV)
+    go = torch.empty_like(gi)
+    ma.newton_schulz(gi, go, ns_steps=64, ns_coeffs=(1.5, -0.5, 0.0))
+    torch.cuda.synchronize()
+    ref = oracle.newton_schulz(G[0], 64, (1.5, -0.5, 0.0))
+    assert rel_fro(go.cpu().numpy()[0], ref) <= MUON_RTOL
+    U, _, Vt = np.linalg.svd(G[0].astype(np.float64), full_matrices=False)
+    assert rel_fro(go.cpu().numpy()[0], U @ Vt) <= MUON_RTOL
+
+
+def test_muon_largest_bucket_count():
+    """A bucket of K = 65535 matrices (the largest the launch grids take; K = 65536 is
+    rejected before launch): first, middle and last matrix against the oracle."""
+    K, A, B = 65535, 16, 40
+    gen_ = torch.Generator(device=DEV).manual_seed(12)
+    p = torch.randn((K, A, B), generator=gen_, device=DEV)
+    g = 0.02 * torch.randn((K, A, B), generator=gen_, device=DEV)
+    m = torch.zeros_like(p)
+    picks = [0, K // 2, K - 1]
+    saved = {k: (p[k].cpu().numpy().copy(), g[k].cpu().numpy().copy()) for k in picks}
+    ma.muon_step([(p, g, m)], lr=LR, momentum=MU, weight_decay=WD)
+    torch.cuda.synchronize()
+    keep = 1.0 - f32(LR) * f32(WD)
+    for k in picks:
+        p0, g0 = saved[k]
+        ref = oracle.muon_step(p0, g0, np.zeros((A, B)), lr=f32(LR), mu=f32(MU), weight_decay=f32(WD))
+        prev = p0.astype(np.float64)
+        err = rel_fro(prev * keep - p[k].cpu().numpy(), prev * keep - ref.param)
+        assert err <= MUON_RTOL, (k, err)
+    with pytest.raises(ma.MuonAdamWError):
+        big = torch.zeros((65536, 1, 2), device=DEV)
+        ma.muon_step([(big, big.clone(), big.clone())], lr=LR)
+
+
+def test_muon_step_with_empty_buckets():
+    """Empty buckets (K = 0) between real ones are skipped: their route records stay
+    zero and the real buckets match the oracle."""
+    P0, grads = _buckets([(2, 64, 128), (3, 130, 70)], 81, 1)
+    empty = torch.zeros((0, 50, 60), device=DEV)
+    ps = [torch.from_numpy(x).to(DEV) for x in P0]
+    ms = [torch.zeros_like(x) for x in ps]
+    gs = [torch.from_numpy(x).to(DEV) for x in grads[0]]
+    routes = ma.muon_step([(empty, empty.clone(), empty.clone()), (ps[0], gs[0], ms[0]),
+                           (empty, empty.clone(), empty.clone()), (ps[1], gs[1], ms[1])],
+                          lr=LR, momentum=MU, weight_decay=WD)
+    torch.cuda.synchronize()
+    assert routes[0].m == 0 and routes[2].m == 0 and routes[1].m == 64 and routes[3].m == 70
+    hist = [[(ps[i].cpu().numpy(), ms[i].cpu().numpy()) for i in range(2)]]
+    _check_muon(P0, grads, hist, [routes[1], routes[3]])
