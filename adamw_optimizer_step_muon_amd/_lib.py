@@ -28,7 +28,7 @@ EXPORTED = (
     "ma_muon_workspace_bytes", "ma_muon_phases", "ma_muon_step", "ma_adamw_step",
     "ma_newton_schulz_workspace_bytes", "ma_newton_schulz", "ma_muon_tune", "ma_muon_tune_reset",
     "ma_adamw_step_multi", "ma_muon_check_plan", "ma_muon_ns_time", "ma_muon_static_init",
-    "ma_muon_step_static", "ma_muon_tune_configs", "ma_stream_probe",
+    "ma_muon_step_static", "ma_muon_tune_configs", "ma_stream_probe", "ma_mfma_probe",
 )
 MA_STATIC_WORKSPACE_BYTES = 512 << 20
 
@@ -151,6 +151,9 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.ma_stream_probe.argtypes = [ctypes.POINTER(ctypes.c_void_p), ctypes.c_int32,
                                     ctypes.POINTER(ctypes.c_void_p), ctypes.c_int32,
                                     ctypes.c_int64, ctypes.c_void_p]
+    lib.ma_mfma_probe.restype = ctypes.c_int
+    lib.ma_mfma_probe.argtypes = [ctypes.c_void_p, ctypes.c_int32, ctypes.c_int32,
+                                  ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]
     lib.ma_muon_tune_reset.restype = None
     lib.ma_muon_tune_reset.argtypes = []
     lib.ma_muon_check_plan.restype = ctypes.c_int
@@ -565,6 +568,39 @@ def muon_ns_time(grads, *, reps: int = 3, ns_steps: int = 5, ns_coeffs=None, ns_
                                _stream_handle(stream, device) if device is not None else 0,
                                int(reps), out))
     return [float(out[i]) for i in range(nph)]
+
+
+MFMA_PROBE_THREADS = 512
+MFMA_PROBE_OPERAND_VALUES = 16 * 64 * 8
+
+
+def mfma_probe_flops(blocks: int, iters: int) -> float:
+    """FLOPs of one ma_mfma_probe launch: 8 waves x 8 MFMAs of 32 x 32 x 16 per round."""
+    return float(blocks) * 8 * iters * 8 * 2 * 32 * 32 * 16
+
+
+def mfma_probe(operands, out, iters: int, *, clocks=None, stream=None) -> None:
+    """The matrix-core reference loop of ma_mfma_probe: `operands` a contiguous bf16 GPU
+    tensor of at least 8192 values (16 fragments of 64 lanes x 8), `out` a contiguous fp32
+    GPU tensor of blocks x 512 values (its size sets the block count), `clocks` None or a
+    contiguous int64 GPU tensor of 2 x blocks values."""
+    import torch
+
+    if not (operands.is_cuda and operands.dtype == torch.bfloat16 and operands.is_contiguous()):
+        raise ValueError("operands must be a contiguous bf16 GPU tensor")
+    if operands.numel() < MFMA_PROBE_OPERAND_VALUES:
+        raise ValueError(f"operands needs {MFMA_PROBE_OPERAND_VALUES} values")
+    _require_f32_cuda("out", out)
+    if out.numel() % MFMA_PROBE_THREADS:
+        raise ValueError("out must hold a multiple of 512 values")
+    blocks = out.numel() // MFMA_PROBE_THREADS
+    if clocks is not None:
+        if not (clocks.is_cuda and clocks.dtype == torch.int64 and clocks.is_contiguous()
+                and clocks.numel() == 2 * blocks):
+            raise ValueError("clocks must be a contiguous int64 GPU tensor of 2 x blocks values")
+    _check(load().ma_mfma_probe(_ptr(operands), blocks, int(iters), _ptr(out),
+                                _ptr(clocks) if clocks is not None else None,
+                                _stream_handle(stream, out.device)))
 
 
 def stream_probe(inputs, outputs, *, stream=None) -> None:

@@ -18,7 +18,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libmuonadamw.so")
-SOURCES = ["adamw.hip", "muon_elementwise.hip", "ns_gemm.hip", "capi.hip"]
+SOURCES = ["adamw.hip", "muon_elementwise.hip", "ns_gemm.hip", "mfma_probe.hip", "capi.hip"]
 ARCH = os.environ.get("MA_OFFLOAD_ARCH", "gfx950")
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")

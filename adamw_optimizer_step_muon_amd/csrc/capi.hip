@@ -1353,6 +1353,24 @@ ma_status ma_stream_probe(const float* const* in, int32_t reads, float* const* o
   return MA_OK;
 }
 
+ma_status ma_mfma_probe(const void* operands, int32_t blocks, int32_t iters, float* out,
+                        uint64_t* clocks, void* stream) {
+  g_last_error.clear();
+  if (!operands || (reinterpret_cast<uintptr_t>(operands) & 15u))
+    return fail(MA_ERR_INVALID_ARG, "operands NULL or not 16-byte aligned");
+  if (!out || (reinterpret_cast<uintptr_t>(out) & 3u))
+    return fail(MA_ERR_INVALID_ARG, "out NULL or not 4-byte aligned");
+  if (clocks && (reinterpret_cast<uintptr_t>(clocks) & 7u))
+    return fail(MA_ERR_INVALID_ARG, "clocks not 8-byte aligned");
+  if (blocks < 1 || blocks > 65535) return fail(MA_ERR_INVALID_ARG, "blocks = %d outside 1..65535", blocks);
+  if (iters < 1 || iters > (1 << 22)) return fail(MA_ERR_INVALID_ARG, "iters = %d outside 1..2^22", iters);
+  const hipError_t e = launch_mfma_probe(operands, blocks, iters, out,
+                                         reinterpret_cast<unsigned long long*>(clocks),
+                                         static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "probe launch");
+  return MA_OK;
+}
+
 ma_status ma_adamw_step(float* param, const float* grad, float* exp_avg, float* exp_avg_sq,
                         int64_t n, const ma_adamw_hparams* hp, void* stream) {
   g_last_error.clear();

@@ -322,4 +322,11 @@ hipError_t launch_stream_probe(const float* const* in, int reads, float* const* 
                                int64_t n, hipStream_t s);
 hipError_t launch_adamw_multi(const AdamWSegTable& t, hipStream_t s);
 
+// Matrix-core reference loop (mfma_probe.hip): `blocks` blocks of 512 threads, each wave
+// running `iters` rounds of 8 v_mfma_f32_32x32x16_bf16 on 16 fragments read once from
+// `operands` (16 x 64 x 8 bf16, 16-byte aligned); out: blocks x 512 floats; clocks
+// (may be null): 2 per block, s_memtime and s_memrealtime deltas.
+hipError_t launch_mfma_probe(const void* operands, int blocks, int iters, float* out,
+                             unsigned long long* clocks, hipStream_t s);
+
 }  // namespace ma

@@ -215,6 +215,37 @@ def cpu_baseline(wl, budget_s):
                        "single-threaded)")}
 
 
+def mfma_probe(grad, dev, stream, iters=300000, reps=3):
+    """Sustained bf16 MFMA rate and shader clock of ma_mfma_probe over the whole chip: once
+    on the first 8192 values of a Muon gradient (cast to bf16; the GEMMs' operands are
+    such values scaled), once on zeros.  TFLOP/s from HIP events on the launch stream,
+    the clock from the probe's own cycle counters."""
+    import torch
+
+    import adamw_optimizer_step_muon_amd as ma
+
+    blocks = torch.cuda.get_device_properties(dev).multi_processor_count
+    out = torch.empty(blocks * ma.MFMA_PROBE_THREADS, dtype=torch.float32, device=dev)
+    clocks = torch.zeros(2 * blocks, dtype=torch.int64, device=dev)
+    vals = grad.reshape(-1)[:ma.MFMA_PROBE_OPERAND_VALUES].to(torch.bfloat16).contiguous()
+    res = {}
+    for name, ops in (("", vals), ("_zero_operands", torch.zeros_like(vals))):
+        ma.mfma_probe(ops, out, iters, clocks=clocks, stream=stream)   # warm-up
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record(stream)
+        for _ in range(reps):
+            ma.mfma_probe(ops, out, iters, clocks=clocks, stream=stream)
+        e1.record(stream)
+        e1.synchronize()
+        ms = e0.elapsed_time(e1) / reps
+        c = clocks.double().cpu()
+        res["tflops" + name] = round(ma.mfma_probe_flops(blocks, iters) / (ms * 1e-3) / 1e12, 1)
+        res["clock_ghz" + name] = round(float(c[0::2].sum() / c[1::2].sum()) * 0.1, 3)
+    res["operands"] = "first 8192 values of the first Muon bucket's gradient, as bf16"
+    return res
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -336,6 +367,9 @@ def main():
     probe_ms = timed(lambda: ma.stream_probe([ap_, ag, am, av], [ap_, am, av], stream=stream),
                      reps)
     probe_gbs = ADAMW_BYTES_PER_ELEM * n / (probe_ms * 1e-3) / 1e9
+    # the matrix cores' sustained rate on this workload's values (ma_mfma_probe: the GEMM
+    # kernel's MFMA and occupancy, operands in registers, no memory traffic), and on zeros
+    mfma_ceiling = mfma_probe(buckets[0][1], dev, stream)
 
     out = {
         "metric": "optimizer-step ms + NS TFLOP/s (%MFMA peak) + AdamW GB/s (%HBM)",
@@ -392,6 +426,10 @@ def main():
             "achieved_hbm_gbs": round(nbytes / (ns_ms * 1e-3) / 1e9, 1),
             "attainable_tflops": round(attainable, 1),
             "frac_of_attainable": round(ns_tflops / attainable, 4),
+            # what a register-only MFMA loop sustains on the part with these operand values:
+            # the clock falls under the power limit when the operands toggle
+            "mfma_ceiling": mfma_ceiling,
+            "frac_of_mfma_ceiling": round(ns_tflops / mfma_ceiling["tflops"], 4),
         },
         "adamw_roofline": {
             "kernel": "adamw_vec_kernel",

@@ -201,6 +201,25 @@ ma_status ma_adamw_step(float* param, const float* grad, float* exp_avg, float* 
 ma_status ma_stream_probe(const float* const* in, int32_t reads, float* const* out,
                           int32_t writes, int64_t n, void* stream);
 
+/* A benchmark aid: the matrix cores' sustained rate on given operand data.  Launches
+ * `blocks` blocks of 8 waves (512 threads; with one block per compute unit that is two
+ * waves per SIMD, the Newton-Schulz GEMM kernel's occupancy).  Each wave reads 8 A and 8 B
+ * operand fragments once from `operands` (device, 16 x 64 x 8 bf16 values = 16 KiB,
+ * 16-byte aligned: fragment f of lane l is the 8 values at (f * 64 + l) * 8, A fragments
+ * even f, B fragments odd f) and then runs `iters` rounds of 8 v_mfma_f32_32x32x16_bf16,
+ * round r pairing A fragment r with B fragment (r + 3) % 8, into four accumulators, with no
+ * memory access inside the loop: blocks * 8 * iters * 8 * 32768 FLOP in all.  out (device,
+ * blocks * 512 floats, 4-byte aligned) receives each thread's sum of its accumulator
+ * elements, so the summed products can be checked.  clocks (device, 2 * blocks values,
+ * 8-byte aligned, or NULL) receives per block the shader-clock counter's advance over the
+ * loop (s_memtime) and the 100 MHz real-time counter's (s_memrealtime): their ratio times
+ * 0.1 GHz is the clock the loop ran at.  The part lowers its clock under sustained MFMA load
+ * when the operands toggle, so this rate, not the 2.5 PFLOP/s rating, bounds what any
+ * bf16 GEMM reaches on such data.  Errors: MA_ERR_INVALID_ARG (NULL or misaligned
+ * pointers, blocks outside 1..65535, iters outside 1..2^22), MA_ERR_HIP. */
+ma_status ma_mfma_probe(const void* operands, int32_t blocks, int32_t iters, float* out,
+                        uint64_t* clocks, void* stream);
+
 /* One AdamW tensor of ma_adamw_step_multi: n fp32 elements at each pointer (device). */
 typedef struct {
   float* param;

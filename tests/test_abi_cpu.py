@@ -423,3 +423,16 @@ def test_stream_probe_rejects_before_launch(lib):
     assert lib.ma_stream_probe(ins, 2, part, 1, n, None) == _lib.MA_ERR_INVALID_ARG
     two = (P * 4)(base, base + 8192, 0, 0)         # two overlapping inputs
     assert lib.ma_stream_probe(two, 2, outs, 1, n, None) == _lib.MA_ERR_INVALID_ARG
+
+
+def test_mfma_probe_rejects_before_launch(lib):
+    base = 1 << 40
+    assert lib.ma_mfma_probe(None, 1, 1, base, None, None) == _lib.MA_ERR_INVALID_ARG
+    assert lib.ma_mfma_probe(base + 8, 1, 1, base + 65536, None, None) == _lib.MA_ERR_INVALID_ARG
+    assert lib.ma_mfma_probe(base, 1, 1, None, None, None) == _lib.MA_ERR_INVALID_ARG
+    assert lib.ma_mfma_probe(base, 1, 1, base + 65538, None, None) == _lib.MA_ERR_INVALID_ARG
+    assert lib.ma_mfma_probe(base, 1, 1, base + 65536, base + 4, None) == _lib.MA_ERR_INVALID_ARG
+    for blocks, iters in ((0, 1), (65536, 1), (1, 0), (1, (1 << 22) + 1), (-1, 5)):
+        assert lib.ma_mfma_probe(base, blocks, iters, base + 65536, None, None) == \
+            _lib.MA_ERR_INVALID_ARG
+    assert b"outside" in lib.ma_last_error()

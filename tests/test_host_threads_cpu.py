@@ -18,6 +18,8 @@ import pytest
 
 from conftest import ROOT
 
+import adamw_optimizer_step_muon_amd.build as _build
+
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 CSRC = os.path.join(ROOT, "adamw_optimizer_step_muon_amd", "csrc")
 
@@ -83,8 +85,7 @@ def test_host_state_under_thread_sanitizer():
         flags = ["--offload-arch=gfx950", "-O1", "-g", "-std=c++17", "-pthread",
                  "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
                  "-Xarch_host", "-fsanitize=thread", "-I", os.path.join(ROOT, "include")]
-        srcs = [os.path.join(CSRC, s) for s in ("adamw.hip", "muon_elementwise.hip",
-                                                  "ns_gemm.hip", "capi.hip")]
+        srcs = [os.path.join(CSRC, s) for s in _build.SOURCES]
         r = subprocess.run([HIPCC, *flags, *srcs, drv, "-o", exe], capture_output=True,
                            text=True, timeout=600)
         assert r.returncode == 0, r.stderr[-3000:]
