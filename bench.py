@@ -99,6 +99,9 @@ def parse():
     ap.add_argument("--calibration-copy-mib", type=int, default=0,
                     help="after timing, copy this many MiB device-to-device once (a plain "
                          "copy of known size for calibrating HBM byte counters)")
+    ap.add_argument("--comparator", action="store_true",
+                    help="also time the same Newton-Schulz chain as torch bf16 batched GEMMs "
+                         "(hipBLASLt) on the workload's gradients, after the measurement")
     return ap.parse_args()
 
 
@@ -213,6 +216,50 @@ def cpu_baseline(wl, budget_s):
                        f"matrices, each bucket scaled by K; AdamW {n_done} of {n} elements, "
                        f"scaled; numpy float64 (BLAS threads={cores}, elementwise "
                        "single-threaded)")}
+
+
+def blas_comparator(grads, coeffs, ns_steps, stream, reps=3):
+    """The Newton-Schulz chain of each bucket as plain torch bf16 batched GEMMs (hipBLASLt
+    on this image): X = G / ||G||_F per matrix in bf16, wide orientation; per step
+    R = X X^T, P = b R + c R R, X = a X + P X (bmm / baddbmm, both operands contiguous).
+    Timed with HIP events on the launch stream; the normalisation and cast stay outside."""
+    import torch
+
+    a, b, c = coeffs
+    total_ms, sym, dense, per = 0.0, 0.0, 0.0, []
+    for g in grads:
+        K, A, B = g.shape
+        m, n = min(A, B), max(A, B)
+        X0 = g if A <= B else g.mT
+        X0 = (X0 / X0.norm(dim=(1, 2), keepdim=True).clamp_min(1e-30)).to(torch.bfloat16).contiguous()
+
+        def chain():
+            X = X0
+            for _ in range(ns_steps):
+                R = torch.bmm(X, X.mT.contiguous())
+                P = torch.baddbmm(R, R, R, beta=b, alpha=c)
+                X = torch.baddbmm(X, P, X, beta=a, alpha=1.0)
+            return X
+
+        chain()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record(stream)
+        for _ in range(reps):
+            chain()
+        e1.record(stream)
+        e1.synchronize()
+        ms = e0.elapsed_time(e1) / reps
+        total_ms += ms
+        sym += K * ns_steps * (3 * m * m * n + m ** 3)
+        dense += K * ns_steps * (4 * m * m * n + 2 * m ** 3)
+        per.append(round(ms, 4))
+        del X0
+        torch.cuda.empty_cache()
+    return {"kind": "torch bf16 bmm/baddbmm chain (hipBLASLt), same buckets and data",
+            "ns_ms": round(total_ms, 4), "bucket_ms": per,
+            "tflops_symmetric_count": round(sym / (total_ms * 1e-3) / 1e12, 1),
+            "tflops_dense_count": round(dense / (total_ms * 1e-3) / 1e12, 1)}
 
 
 def mfma_probe(grad, dev, stream, iters=300000, reps=3):
@@ -454,6 +501,10 @@ def main():
         dst.copy_(src)
         torch.cuda.synchronize()
         out["calibration_copy_bytes"] = nbytes
+    if args.comparator:
+        comp = blas_comparator([b[1] for b in buckets], mh.coeffs, mh.ns_steps, stream)
+        comp["speedup_of_this_library"] = round(comp["ns_ms"] / ns_ms, 3)
+        out["comparator"] = comp
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(wl, args.cpu_budget_s)
     print(json.dumps(out), flush=True)
