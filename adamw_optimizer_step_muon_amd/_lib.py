@@ -257,8 +257,11 @@ def _as_stack(t):
 # --------------------------------------------------------------------------
 # entry points (names of the C ABI without the ma_ prefix)
 # --------------------------------------------------------------------------
-def muon_route_of(A: int, B: int, ns_steps: int = 5, ns_mode: int = 0) -> Route:
-    hp = _MuonHParams(ns_steps=int(ns_steps), ns_mode=int(ns_mode))
+def muon_route_of(A: int, B: int, ns_steps: int = 5, ns_mode: int = 0, ns_coeffs=None) -> Route:
+    """The route one A x B matrix takes (ma_muon_route_of) for these steps, mode and
+    coefficient table (None: the quintic)."""
+    hp, _keep = _muon_hparams(0.0, 0.0, 0.0, True, int(ns_steps), ns_coeffs, 1e-7, False, 0,
+                              int(ns_mode))
     out = _MuonRoute()
     _check(load().ma_muon_route_of(int(A), int(B), ctypes.byref(hp), ctypes.byref(out)))
     return Route(bool(out.transposed), out.m, out.n, out.ns_steps_run, out.m_pad, out.n_pad,
@@ -404,7 +407,8 @@ def muon_step(buckets, *, lr: float, momentum: float = 0.95, weight_decay: float
               cautious_wd: bool = False, scale_mode: int = 0, ns_mode: int = 0, workspace=None,
               stream=None):
     """One Muon step (ma_muon_step) on (param, grad, momentum) triples of (K, A, B) or
-    (A, B) fp32 GPU tensors.  ns_mode 1 runs the Gram-space iteration where n >= 2 m.
+    (A, B) fp32 GPU tensors.  ns_mode 1 runs the fp16 Gram-space iteration on buckets whose
+    long side is at least 3.5x the Gram side.
     Returns the routing report of each bucket."""
     import torch
 

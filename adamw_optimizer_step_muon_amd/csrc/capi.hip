@@ -16,6 +16,10 @@
 #include "ma_internal.h"
 
 namespace ma {
+
+// the Gram-space route's effective mode for these hyperparameters (defined below)
+bool gram_space_range_ok(const ma_muon_hparams* hp);
+int32_t gs_mode(const ma_muon_hparams* hp);
 namespace {
 
 // Workspace of ma_muon_step_static: a file-scope device array, one copy per GPU, kept
@@ -306,14 +310,28 @@ void phase_groups(const Phase& ph, char* ws, int cur, NsGroup* g) {
 ma_status run_ns_gram_space(const Phase& ph, const ma_muon_hparams* hp, char* ws,
                             hipStream_t s, const unsigned short** out, int64_t* ldo,
                             const float** oscale) {
+  // fp16 operands throughout ("DMuon", section 2.2, Gram-space recurrence): R carries
+  // the squared spectrum, whose relative precision bf16's 8-bit significand loses on
+  // wide Gram sides; fp16 keeps three more bits at the same MFMA rate, with powers of two
+  // keeping every stored value in its normal range: X0 is stored as X0 * sx (by
+  // prep_bucket), R and T = R P as R * rs, T * rs; P and Q unscaled (their eigenvalues lie
+  // in [0.7, a] and [0, a^N] for the quintic on a normalised X0)
   NsGroup g[kMaxGemmGroups];
   SymProd sp[kMaxGemmGroups];
-  const float* inv[kMaxGemmGroups];
-  for (int j = 0; j < ph.n; ++j) inv[j] = at<const float>(ws, ph.base[j] + ph.plan[j].off_inv);
   const Choices tiles = tuned_choices(ph);
-  phase_groups(ph, ws, 0, g);  // X = X_0 (bf16 U), Xn = the output, R = R_0
+  phase_groups(ph, ws, 0, g);  // X = X_0 (fp16), Xn = the output, R = R_0
   auto buf = [&](int j, size_t off) { return at<unsigned short>(ws + ph.base[j], off); };
-  hipError_t e = launch_gram(g, ph.n, inv, tiles[kProdGram], s);
+  // per-matrix factors written by the fp16 conversion (prep_bucket): the Gram's
+  // 2^7 / sx_k (squared by its epilogue) and the last product's 1 / sx_k
+  const float* gram_f[kMaxGemmGroups];
+  const float* last_f[kMaxGemmGroups];
+  for (int j = 0; j < ph.n; ++j) {
+    const float* gsc = at<const float>(ws, ph.base[j] + ph.plan[j].off_gsc);
+    gram_f[j] = gsc + ph.plan[j].K;
+    last_f[j] = gsc + 2 * ph.plan[j].K;
+  }
+  const float rs = kGramSpaceRScale;
+  hipError_t e = launch_gram(g, ph.n, gram_f, tiles[kProdGram], s, kTyF16);
   if (e != hipSuccess) return hip_fail(e, "gram launch");
   int rc = 0, qc = 0;  // current R (off_r / off_r2) and Q (off_q[qc])
   const int N = hp->ns_steps;
@@ -325,32 +343,33 @@ ma_status run_ns_gram_space(const Phase& ph, const ma_muon_hparams* hp, char* ws
       g[j].R = buf(j, rc ? p.off_r2 : p.off_r);
       g[j].P = buf(j, it == 0 ? p.off_q[0] : p.off_p);
     }
-    e = launch_poly(g, ph.n, c.a, c.b, c.c, tiles[kProdPoly], s);
+    // P = a I + b R + c R^2 from the stored rs R: b / rs and c / rs^2
+    e = launch_poly(g, ph.n, c.a, c.b / rs, c.c / (rs * rs), tiles[kProdPoly], s, kTyF16);
     if (e != hipSuccess) return hip_fail(e, "poly launch");
     if (it > 0) {  // Q <- P Q
       for (int j = 0; j < ph.n; ++j)
         sp[j] = SymProd{&ph.plan[j], g[j].P, buf(j, ph.plan[j].off_q[qc]),
                         buf(j, ph.plan[j].off_q[qc ^ 1])};
-      e = launch_sym(sp, ph.n, tiles[kProdPoly], s);
+      e = launch_sym(sp, ph.n, tiles[kProdPoly], s, kTyF16);
       if (e != hipSuccess) return hip_fail(e, "Q product launch");
       qc ^= 1;
     }
-    if (it + 1 < N) {  // T = R P, then R <- P T
+    if (it + 1 < N) {  // T = R P, then R <- P T (both carry the factor rs)
       for (int j = 0; j < ph.n; ++j)
         sp[j] = SymProd{&ph.plan[j], g[j].R, g[j].P, buf(j, ph.plan[j].off_t)};
-      e = launch_sym(sp, ph.n, tiles[kProdPoly], s);
+      e = launch_sym(sp, ph.n, tiles[kProdPoly], s, kTyF16);
       if (e != hipSuccess) return hip_fail(e, "R P product launch");
       for (int j = 0; j < ph.n; ++j)
         sp[j] = SymProd{&ph.plan[j], g[j].P, buf(j, ph.plan[j].off_t),
                         buf(j, rc ? ph.plan[j].off_r : ph.plan[j].off_r2)};
-      e = launch_sym(sp, ph.n, tiles[kProdPoly], s);
+      e = launch_sym(sp, ph.n, tiles[kProdPoly], s, kTyF16);
       if (e != hipSuccess) return hip_fail(e, "R update launch");
       rc ^= 1;
     }
   }
-  // X_N = Q_N X_0 = inv Q_N U, in the parameter's orientation
+  // X_N = Q_N X_0 = Q_N (sx_k X0) / sx_k, in bf16 and in the parameter's orientation
   for (int j = 0; j < ph.n; ++j) g[j].P = buf(j, ph.plan[j].off_q[qc]);
-  e = launch_combine(g, ph.n, inv, true, tiles[kProdCombine], s);
+  e = launch_combine(g, ph.n, last_f, true, tiles[kProdCombine], s, kTyF16ToBf16);
   if (e != hipSuccess) return hip_fail(e, "combine launch");
   for (int j = 0; j < ph.n; ++j) {
     const BucketPlan& p = ph.plan[j];
@@ -419,10 +438,18 @@ ma_status prep_bucket(const BucketPlan& p, const float* grad, float* momentum,
   hipError_t e = launch_muon_prep(p, grad, momentum, momentum ? hp->momentum : 0.0f,
                                   momentum ? hp->nesterov : 0, partials, S, T, s);
   if (e != hipSuccess) return hip_fail(e, "momentum/cast launch");
-  e = launch_norm_finalize(p, partials, hp->ns_eps, inv, shift, s);
+  const bool f16 = p.gram_space && hp->ns_steps > 0;
+  float* gsc = f16 ? at<float>(w, p.off_gsc) : nullptr;  // ||X0||, then the 2 K factors
+  e = launch_norm_finalize(p, partials, hp->ns_eps, inv, shift, s, gsc);
   if (e != hipSuccess) return hip_fail(e, "norm launch");
   e = launch_rescale(p, S, T, shift, s);
   if (e != hipSuccess) return hip_fail(e, "rescale launch");
+  if (f16) {
+    // the Gram-space route iterates on fp16 operands: X0 = U / (||U|| + eps), times a
+    // power of two that centres it in fp16's range, converted in place
+    e = launch_to_f16(p, S, T, inv, gsc, p.gs_sx, gsc + p.K, s);
+    if (e != hipSuccess) return hip_fail(e, "fp16 conversion launch");
+  }
   return MA_OK;
 }
 
@@ -581,6 +608,7 @@ class PlanChecker final : public LaunchRecorder {
         add(b + p.off_q[0], rb, t + "Q[0]");
         add(b + p.off_q[1], rb, t + "Q[1]");
         add(b + p.off_t, rb, t + "T");
+        add(b + p.off_gsc, static_cast<size_t>(p.K) * 3 * 4, t + "Gram-space norms and factors");
       }
       add(b + p.off_part, static_cast<size_t>(p.K * p.nblk) * 8, t + "partials");
       add(b + p.off_inv, static_cast<size_t>(p.K) * 4, t + "inv");
@@ -664,11 +692,12 @@ class PlanChecker final : public LaunchRecorder {
     if (T) win(T, 0, p.K * Ap * Bp, "cast T");
   }
   void norm(const BucketPlan& p, const double* partials, const float* inv,
-            const int* shift) override {
+            const int* shift, const float* x0norm) override {
     ++launches;
     winb(reinterpret_cast<uintptr_t>(partials), p.K * p.nblk * 8, "partials");
     winb(reinterpret_cast<uintptr_t>(inv), p.K * 4, "inv");
     winb(reinterpret_cast<uintptr_t>(shift), p.K * 4, "shift");
+    if (x0norm) winb(reinterpret_cast<uintptr_t>(x0norm), p.K * 4, "x0norm");
   }
   void rescale(const BucketPlan& p, const unsigned short* S, const unsigned short* T,
                const int* shift) override {
@@ -676,6 +705,16 @@ class PlanChecker final : public LaunchRecorder {
     if (S) win(S, 0, p.K * p.m_pad * p.n_pad, "rescaled S");
     if (T) win(T, 0, p.K * p.m_pad * p.n_pad, "rescaled T");
     winb(reinterpret_cast<uintptr_t>(shift), p.K * 4, "shift");
+  }
+  void to_f16(const BucketPlan& p, const unsigned short* S, const unsigned short* T,
+              const float* inv, const float* x0norm, const float* gsc) override {
+    ++launches;
+    if (!p.gram_space) fail_("fp16 conversion of a bucket outside the Gram-space route");
+    if (S) win(S, 0, p.K * p.m_pad * p.n_pad, "fp16 S");
+    if (T) win(T, 0, p.K * p.m_pad * p.n_pad, "fp16 T");
+    winb(reinterpret_cast<uintptr_t>(inv), p.K * 4, "inv");
+    winb(reinterpret_cast<uintptr_t>(x0norm), p.K * 4, "x0norm");
+    winb(reinterpret_cast<uintptr_t>(gsc), p.K * 2 * 4, "Gram-space factors");
   }
   void apply(const BucketPlan& p, const float* out, const unsigned short* O, const float* oscale,
              int64_t ldo) override {
@@ -750,7 +789,7 @@ ma_status tune_impl(const ma_muon_bucket* buckets, int32_t n_buckets, const ma_m
     const ma_status st = check_shape(buckets[i].K, buckets[i].A, buckets[i].B);
     if (st != MA_OK) return fail(st, "bucket %d: %s", i, g_last_error.c_str());
   }
-  const int32_t mode = hp ? hp->ns_mode : 0;
+  const int32_t mode = gs_mode(hp);
   if (reps == 0) {
     // pin: check every requested configuration first, then store (all default: forget)
     int phase = 0;
@@ -931,11 +970,55 @@ int forced_tile() {
 }
 
 bool wants_gram_space(int32_t ns_mode, int64_t A, int64_t B) {
-  // wide buckets (A < B: X is the matrix itself) with n >= 2 m and m <= 1024: where the
-  // route's bf16 error was measured inside the Muon tolerance on Gaussian, low-rank and
-  // row log-normal gradients; tall row-scaled gradients (any m) and low-rank ones with
-  // Gram sides from 1536 left it, so those buckets run the printed iteration
-  return ns_mode == 1 && A < B && B >= 2 * A && A <= kGramSpaceMaxM;
+  // buckets whose long side is at least 3.5x the Gram side, in either orientation: there
+  // the route does at most 27.5 m^3 of symmetric-count work per matrix against the
+  // printed iteration's 57.5 m^3 (five steps), and its fp16 error stayed within 1.3e-2
+  // of the exact iteration on conditioned gradients over many seeds (2-7e-3 at the
+  // workloads' sizes); at 3:1 conditioned gradients reached 2.0-2.5e-2 on Gram sides of
+  // 64 to 256, so squarer buckets run the printed iteration
+  const int64_t m = A < B ? A : B, n = A < B ? B : A;
+  return ns_mode == 1 && kGramSpaceAspectDen * n >= kGramSpaceAspectNum * m;
+}
+
+// Whether every value the fp16 Gram-space route stores stays inside fp16's range for
+// these coefficients and steps.  X0 is normalised, so the iterate's singular values start
+// in [0, 1]; each step maps sigma to p(sigma) = sigma q(sigma^2), q(t) = a + b t + c t^2,
+// so their bound s becomes max |p| over [0, s].  R (eigenvalues sigma^2 <= s^2) and R P
+// (sigma p(sigma)) are stored times kGramSpaceRScale; P (q) and Q (the product of the
+// steps' q) unscaled, Q bounded by the product of max |q| over [0, s^2] (reached on a
+// zero singular value, where Q grows as a^N).  Symmetric entries are bounded by the
+// largest eigenvalue modulus; sampled on a grid, with a margin of 2 below fp16's maximum.
+bool gram_space_range_ok(const ma_muon_hparams* hp) {
+  constexpr int kGrid = 4096;
+  constexpr double kLimit = 32768.0;
+  const double rs = kGramSpaceRScale;
+  if (hp->ns_steps < 0 || hp->ns_steps > MA_MAX_NS_STEPS) return false;
+  double s = 1.0, q_prod = 1.0;
+  for (int it = 0; it < hp->ns_steps; ++it) {
+    const NsCoeffs c = coeff_at(hp, it);
+    double pmax = 0.0, qmax = 0.0;
+    for (int i = 0; i <= kGrid; ++i) {
+      const double sig = s * i / kGrid, t = sig * sig;
+      const double q = c.a + c.b * t + c.c * t * t;
+      qmax = std::max(qmax, std::fabs(q));
+      pmax = std::max(pmax, std::fabs(sig * q));
+    }
+    q_prod *= qmax;
+    // (written so that a NaN coefficient fails the test too)
+    if (!(s * s * rs <= kLimit && s * pmax * rs <= kLimit && q_prod <= kLimit)) return false;
+    s = pmax;
+  }
+  return true;
+}
+
+int32_t gs_mode(const ma_muon_hparams* hp) {
+  return (hp && hp->ns_mode == 1 && gram_space_range_ok(hp)) ? 1 : 0;
+}
+
+float gram_space_sx(int64_t m, int64_t n) {
+  int e = 0;
+  while (e < 14 && (int64_t{1} << (2 * (e + 1))) <= m * n) ++e;
+  return static_cast<float>(int64_t{1} << e);
 }
 
 BucketPlan plan_bucket(int64_t K, int64_t A, int64_t B, int tile, bool gram_space) {
@@ -966,7 +1049,8 @@ BucketPlan plan_bucket(int64_t K, int64_t A, int64_t B, int tile, bool gram_spac
   p.off_p = off;
   off = align256(off + rb);
   p.gram_space = gram_space;
-  p.off_r2 = p.off_q[0] = p.off_q[1] = p.off_t = 0;
+  p.gs_sx = gram_space ? gram_space_sx(p.m, p.n) : 1.0f;
+  p.off_r2 = p.off_q[0] = p.off_q[1] = p.off_t = p.off_gsc = 0;
   if (gram_space) {
     p.off_r2 = off;
     off = align256(off + rb);
@@ -976,6 +1060,8 @@ BucketPlan plan_bucket(int64_t K, int64_t A, int64_t B, int tile, bool gram_spac
     }
     p.off_t = off;
     off = align256(off + rb);
+    p.off_gsc = off;
+    off = align256(off + static_cast<size_t>(K) * 3 * 4);
   }
   p.off_part = off;
   off = align256(off + static_cast<size_t>(K * p.nblk) * 8);
@@ -1015,7 +1101,7 @@ ma_status ma_muon_route_of(int64_t A, int64_t B, const ma_muon_hparams* hp, ma_m
   if (A < 1 || B < 1) return fail(MA_ERR_INVALID_ARG, "matrix shape %lld x %lld", (long long)A, (long long)B);
   const int steps = hp ? hp->ns_steps : 5;
   if (steps < 0 || steps > MA_MAX_NS_STEPS) return fail(MA_ERR_INVALID_ARG, "ns_steps %d", steps);
-  *out = route_of(plan_bucket(1, A, B, 0, wants_gram_space(hp ? hp->ns_mode : 0, A, B)), steps);
+  *out = route_of(plan_bucket(1, A, B, 0, wants_gram_space(gs_mode(hp), A, B)), steps);
   return MA_OK;
 }
 
@@ -1025,7 +1111,7 @@ size_t ma_muon_workspace_bytes(const ma_muon_bucket* buckets, int32_t n_buckets,
   for (int32_t i = 0; i < n_buckets; ++i)
     if (buckets[i].K > 0 && (buckets[i].A < 1 || buckets[i].B < 1)) return 0;
   size_t need = 0;
-  for_each_phase(buckets, n_buckets, hp ? hp->ns_mode : 0, [&](const Phase& ph) {
+  for_each_phase(buckets, n_buckets, gs_mode(hp), [&](const Phase& ph) {
     if (ph.bytes > need) need = ph.bytes;
     return MA_OK;
   });
@@ -1043,7 +1129,7 @@ int32_t ma_muon_phases(const ma_muon_bucket* buckets, int32_t n_buckets,
     if (phase_of) phase_of[i] = -1;
   }
   int32_t count = 0;
-  for_each_phase(buckets, n_buckets, hp ? hp->ns_mode : 0, [&](const Phase& ph) {
+  for_each_phase(buckets, n_buckets, gs_mode(hp), [&](const Phase& ph) {
     if (phase_of)
       for (int j = 0; j < ph.n; ++j) phase_of[ph.bucket[j]] = count;
     ++count;
@@ -1069,14 +1155,14 @@ ma_status ma_muon_step(const ma_muon_bucket* buckets, int32_t n_buckets,
   if (route_out) {
     // from the plans the phases run (a phase may re-plan its buckets' tile)
     for (int32_t i = 0; i < n_buckets; ++i) route_out[i] = ma_muon_route{0, 0, 0, 0, 0, 0, 0};
-    for_each_phase(buckets, n_buckets, hp->ns_mode, [&](const Phase& ph) {
+    for_each_phase(buckets, n_buckets, gs_mode(hp), [&](const Phase& ph) {
       for (int j = 0; j < ph.n; ++j) route_out[ph.bucket[j]] = route_of(ph.plan[j], hp->ns_steps);
       return MA_OK;
     });
   }
   hipStream_t s = static_cast<hipStream_t>(stream);
   char* ws = static_cast<char*>(workspace);
-  return for_each_phase(buckets, n_buckets, hp->ns_mode, [&](const Phase& ph) {
+  return for_each_phase(buckets, n_buckets, gs_mode(hp), [&](const Phase& ph) {
     return run_phase(ph, buckets, hp, ws, s);
   });
 }
@@ -1104,7 +1190,7 @@ ma_status ma_newton_schulz(const float* in, float* out, int64_t K, int64_t A, in
   const int64_t bytes = K * A * B * 4;
   if (overlap(range_of(in, bytes), range_of(out, bytes)))
     return fail(MA_ERR_INVALID_ARG, "in and out overlap");
-  const BucketPlan p = plan_bucket(K, A, B, 0, wants_gram_space(hp->ns_mode, A, B));
+  const BucketPlan p = plan_bucket(K, A, B, 0, wants_gram_space(gs_mode(hp), A, B));
   if (!workspace) return fail(MA_ERR_WORKSPACE, "workspace is NULL, %zu bytes needed", p.bytes);
   if (reinterpret_cast<uintptr_t>(workspace) & 255u)
     return fail(MA_ERR_WORKSPACE, "workspace must be 256-byte aligned");
@@ -1234,7 +1320,7 @@ ma_status ma_muon_check_plan(const ma_muon_bucket* buckets, int32_t n_buckets,
   const uintptr_t ws = take(0);
   if (what == 0) {
     const size_t need = ma_muon_workspace_bytes(bk.data(), n_buckets, hp);
-    st = for_each_phase(bk.data(), n_buckets, hp->ns_mode, [&](const Phase& ph) -> ma_status {
+    st = for_each_phase(bk.data(), n_buckets, gs_mode(hp), [&](const Phase& ph) -> ma_status {
       chk.set_phase(ph, ws, need, bk.data(), true);
       if (chk.error.empty()) {
         const ma_status s2 = run_phase(ph, bk.data(), hp, reinterpret_cast<char*>(ws), nullptr);
@@ -1244,7 +1330,7 @@ ma_status ma_muon_check_plan(const ma_muon_bucket* buckets, int32_t n_buckets,
     });
   } else if (bk[0].K > 0) {
     const ma_muon_bucket& b = bk[0];
-    const BucketPlan p = plan_bucket(b.K, b.A, b.B, 0, wants_gram_space(hp->ns_mode, b.A, b.B));
+    const BucketPlan p = plan_bucket(b.K, b.A, b.B, 0, wants_gram_space(gs_mode(hp), b.A, b.B));
     Phase ph;
     phase_add(ph, p, 0);
     chk.set_phase(ph, ws, p.bytes, bk.data(), false);
@@ -1296,7 +1382,7 @@ ma_status ma_muon_ns_time(const ma_muon_bucket* buckets, int32_t n_buckets,
     return hip_fail(he, "event create");
   }
   int phase = 0;
-  st = for_each_phase(buckets, n_buckets, hp->ns_mode, [&](const Phase& ph) -> ma_status {
+  st = for_each_phase(buckets, n_buckets, gs_mode(hp), [&](const Phase& ph) -> ma_status {
     double total = 0.0;
     for (int r = 0; r < reps; ++r) {
       for (int j = 0; j < ph.n; ++j) {

@@ -22,6 +22,13 @@ typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
 __device__ __forceinline__ unsigned short f2bf(float f) {
   return __builtin_bit_cast(unsigned short, static_cast<__bf16>(f));
 }
+// fp32 -> fp16 (IEEE binary16), round to nearest even; fp16 -> fp32 (exact).
+__device__ __forceinline__ unsigned short f2h(float f) {
+  return __builtin_bit_cast(unsigned short, static_cast<_Float16>(f));
+}
+__device__ __forceinline__ float h2f(unsigned short h) {
+  return static_cast<float>(__builtin_bit_cast(_Float16, h));
+}
 __device__ __forceinline__ float bf2f(unsigned short h) {
   return __builtin_bit_cast(float, static_cast<unsigned int>(h) << 16);
 }
@@ -44,19 +51,30 @@ struct BucketPlan {
   // which their combine reads
   bool keeps_xt;
   size_t off_xt[2];
-  // Gram-space iteration (n >= 2 m, when asked for): R ping-pong in off_r / off_r2, the
-  // accumulated polynomial Q in off_q[2], the product R P in off_t (m_pad x m_pad bf16)
+  // Gram-space iteration (long side >= 3.5 x the Gram side, when asked for), on fp16
+  // operands: X0 is converted in place to fp16 X0 * sx_k (sx_k = gs_sx but for norms
+  // near eps); R ping-pong (stored as R * kGramSpaceRScale) in off_r / off_r2, the
+  // accumulated polynomial Q in off_q[2], the product R P in off_t (m_pad x m_pad fp16
+  // each); per matrix ||X0||, then the Gram's and the last product's factors, in off_gsc
+  // (3 K floats)
   bool gram_space;
-  size_t off_r2, off_q[2], off_t;
+  float gs_sx;
+  size_t off_r2, off_q[2], off_t, off_gsc;
 };
 
 // Plan of one bucket on the given GEMM tile (128 or 256), or on pick_tile's choice
 // (tile 0); MA_NS_TILE, when set to 128 or 256, overrides either.
 BucketPlan plan_bucket(int64_t K, int64_t A, int64_t B, int tile = 0, bool gram_space = false);
-// Whether a bucket runs the Gram-space iteration under ns_mode: 1 asks for it on wide
-// buckets (A < B) with B >= 2 A and A <= kGramSpaceMaxM.
-constexpr int64_t kGramSpaceMaxM = 1024;
+// Whether a bucket runs the Gram-space iteration under ns_mode: 1 asks for it on buckets
+// whose long side is at least 3.5 times the Gram side (either orientation), when the
+// coefficients keep the route inside fp16's range (gs_mode).
+constexpr int64_t kGramSpaceAspectNum = 7, kGramSpaceAspectDen = 2;
 bool wants_gram_space(int32_t ns_mode, int64_t A, int64_t B);
+// Gram-space scales: R is stored times kGramSpaceRScale; X0 times gram_space_sx(m, n),
+// the power of two nearest below sqrt(m n) (at most 2^14), so that the normalised
+// X0 entries (|x| <= 1, about 1 / sqrt(m n) typically) sit in fp16's normal range.
+constexpr float kGramSpaceRScale = 16384.0f;
+float gram_space_sx(int64_t m, int64_t n);
 // Whether GEMM launches holding `tri` lower-triangle and `comb` combine tiles of
 // 256 x 256 fill the chip well enough for 256-tiles.
 bool fills_256(int64_t tri, int64_t comb);
@@ -86,12 +104,21 @@ hipError_t launch_muon_prep(const BucketPlan& p, const float* G, float* M, float
                             unsigned short* T, hipStream_t s);
 // inv[k] = 1 / (sqrt(sum of partials of matrix k) + eps), shift[k] = 0; for a norm
 // outside [2^-32, 2^32], shift[k] = -e and inv[k] = 2^e / (norm + eps) (e its exponent)
+// (x0norm, when given: ||X0|| = ||U|| / (||U|| + eps) per matrix)
 hipError_t launch_norm_finalize(const BucketPlan& p, const double* partials, float eps,
-                                float* inv, int* shift, hipStream_t s);
+                                float* inv, int* shift, hipStream_t s, float* x0norm = nullptr);
 // S and T (m_pad x n_pad bf16 per matrix, either may be null) *= 2^shift[k] where
 // shift[k] != 0, so that inv[k] * X is still X0 = U / (||U|| + eps)
 hipError_t launch_rescale(const BucketPlan& p, unsigned short* S, unsigned short* T,
                           const int* shift, hipStream_t s);
+// Gram-space route: S and T (bf16 U, m_pad x n_pad per matrix, either may be null) are
+// replaced in place by fp16(U * inv[k] * sx_k), i.e. X0 * sx_k in fp16, sx_k = sx unless
+// ||X0|| (x0norm) < 1/2, then sx times the power of two that brings it to [1/2, 1);
+// gsc (2 K floats) receives the Gram's per-matrix factor 2^7 / sx_k and the last
+// product's 1 / sx_k
+hipError_t launch_to_f16(const BucketPlan& p, unsigned short* S, unsigned short* T,
+                         const float* inv, const float* x0norm, float sx, float* gsc,
+                         hipStream_t s);
 // Newton-Schulz products over a group of up to kMaxGemmGroups buckets with the same
 // tile, one launch per product for the whole group.
 constexpr int kMaxGemmGroups = 4;
@@ -108,6 +135,10 @@ struct NsGroup {
 // One Newton-Schulz GEMM launch: its arguments are read by the kernel in place from the
 // kernel-argument segment (see ns_gemm.hip), so the table must fit there.
 enum Epi { kGram = 0, kPoly = 1, kCombine = 2 };
+// Element types of a GEMM launch: bf16 operands and result (the printed iteration);
+// fp16 operands and result (the Gram-space products); fp16 operands and a bf16 result
+// (the Gram-space route's last product, which the update reads).
+enum GemmTypes { kTyBf16 = 0, kTyF16 = 1, kTyF16ToBf16 = 2 };
 
 struct GemmArgs {
   const unsigned short* A;
@@ -129,6 +160,7 @@ struct GemmArgs {
   int xcd_remap;        // 1: renumber blocks XCD by XCD
   int spread;           // 1: spread the next stage's DMAs over the first half-stage
   int symmetrize;       // gram with A != B: copy each diagonal tile's lower triangle up
+  float post;           // gram / combine: constant factor on the result (0: none)
 };
 
 // Up to kMaxGroups buckets (same tile shape) share one launch: block b belongs to the
@@ -251,9 +283,11 @@ struct LaunchRecorder {
   virtual void prep(const BucketPlan& p, const float* G, const float* M, const double* partials,
                     const unsigned short* S, const unsigned short* T) = 0;
   virtual void norm(const BucketPlan& p, const double* partials, const float* inv,
-                    const int* shift) = 0;
+                    const int* shift, const float* x0norm) = 0;
   virtual void rescale(const BucketPlan& p, const unsigned short* S, const unsigned short* T,
                        const int* shift) = 0;
+  virtual void to_f16(const BucketPlan& p, const unsigned short* S, const unsigned short* T,
+                      const float* inv, const float* x0norm, const float* gsc) = 0;
   virtual void apply(const BucketPlan& p, const float* out, const unsigned short* O,
                      const float* oscale, int64_t ldo) = 0;
 };
@@ -265,16 +299,18 @@ LaunchRecorder*& launch_recorder();
 // (192 x 256 tiles) where combine_192_ok holds for every bucket.
 bool combine_192_ok(const BucketPlan& p);
 // R = X X^T (lower-triangle tiles, mirrored); R *= scale[i][k]^2 where scale[i] is given
+// (ty: GemmTypes; post: a constant factor on the result, 0 for none)
 hipError_t launch_gram(const NsGroup* g, int n, const float* const* scale,
-                       const GemmChoice& ch, hipStream_t s);
+                       const GemmChoice& ch, hipStream_t s, int ty = kTyBf16, float post = 0.0f);
 // P = a I + b R + c R R^T (lower-triangle tiles, mirrored)
 hipError_t launch_poly(const NsGroup* g, int n, float a, float b, float c,
-                       const GemmChoice& ch, hipStream_t s);
+                       const GemmChoice& ch, hipStream_t s, int ty = kTyBf16);
 // Xn = P X (times scale[i][k] where given), written row-major (and as X^T into
 // XTn for keeps_xt buckets); with `last`, only in the orientation of the parameter
 // (X^T when A > B: n_pad x m_pad, into XTn, or into Xn for one-orientation buckets)
 hipError_t launch_combine(const NsGroup* g, int n, const float* const* scale, bool last,
-                          const GemmChoice& ch, hipStream_t s);
+                          const GemmChoice& ch, hipStream_t s, int ty = kTyBf16,
+                          float post = 0.0f);
 // One symmetric product per bucket: C = A B^T (= A B for symmetric B) on lower-triangle
 // tiles, mirrored, all m_pad x m_pad; exact only when A B is symmetric (A and B
 // polynomials in one matrix, as in the Gram-space iteration).  Tile as launch_poly's.
@@ -284,7 +320,8 @@ struct SymProd {
   const unsigned short* B;
   unsigned short* C;
 };
-hipError_t launch_sym(const SymProd* p, int n, const GemmChoice& ch, hipStream_t s);
+hipError_t launch_sym(const SymProd* p, int n, const GemmChoice& ch, hipStream_t s,
+                      int ty = kTyBf16);
 // param <- param - lr*wd*mask*param - lr*scale*O with O = oscale[k] * (bf16 O) (oscale
 // may be null: 1), row stride ldo
 hipError_t launch_muon_apply(const BucketPlan& p, float* param, const unsigned short* O,

@@ -139,7 +139,7 @@ __global__ __launch_bounds__(kThreads) void muon_prep_kernel(
 // 1 <= f < 2), inv[k] = 2^e / (norm + eps) and shift[k] = -e
 __global__ __launch_bounds__(kThreads) void norm_finalize_kernel(
     const double* __restrict__ partials, int64_t nblk, float eps, float* __restrict__ inv,
-    int* __restrict__ shift) {
+    int* __restrict__ shift, float* __restrict__ x0norm) {
   const int64_t k = blockIdx.x;
   double acc = 0.0;
   for (int64_t i = threadIdx.x; i < nblk; i += kThreads) acc += partials[k * nblk + i];
@@ -162,6 +162,8 @@ __global__ __launch_bounds__(kThreads) void norm_finalize_kernel(
     }
     inv[k] = static_cast<float>(iv);
     shift[k] = sh;
+    // ||X0|| = ||U|| / (||U|| + eps): 1 up to eps / ||U||, smaller only for norms near eps
+    if (x0norm) x0norm[k] = static_cast<float>(norm / (norm + static_cast<double>(eps)));
   }
 }
 
@@ -185,6 +187,49 @@ __global__ __launch_bounds__(kThreads) void rescale_kernel(unsigned short* __res
       for (int e = 0; e < 4; ++e) {
         const unsigned lo = f2bf(__builtin_ldexpf(bf2f(static_cast<unsigned short>(v[e] & 0xffffu)), sh));
         const unsigned hi = f2bf(__builtin_ldexpf(bf2f(static_cast<unsigned short>(v[e] >> 16)), sh));
+        v[e] = lo | (hi << 16);
+      }
+      q[i] = v;
+    }
+  }
+}
+
+// grid (nb, K): the `per` bf16 values of matrix k in X and in Y (either may be null) are
+// replaced in place by fp16(value * inv[k] * sx_k): the normalised X0 of the Gram-space
+// route times sx_k = sx * 2^-e, a power of two that puts its entries in fp16's range.
+// e <= 0 is the exponent of ||X0|| (x0norm[k]) when that norm is below 1/2, which
+// happens only when ||U|| is near eps; then X0 itself is small and its fp16 copy would
+// otherwise lose its digits or flush to zero.  Block (0, k) also writes the factors the
+// route's products apply: gsc[k] = 2^7 / sx_k (the Gram: R * 2^14 = (X0 sx_k)(X0 sx_k)^T
+// gsc^2) and gsc[K + k] = 1 / sx_k (the last product: X = Q (X0 sx_k) / sx_k).
+// per % 8 == 0
+__global__ __launch_bounds__(kThreads) void to_f16_kernel(unsigned short* __restrict__ X,
+                                                          unsigned short* __restrict__ Y,
+                                                          int64_t per, const float* __restrict__ inv,
+                                                          const float* __restrict__ x0norm,
+                                                          float sx, float* __restrict__ gsc) {
+  const int64_t k = blockIdx.y;
+  float xn = x0norm[k], sxk = sx;
+  for (int e = 0; xn > 0.0f && xn < 0.5f && e < 100; ++e) {
+    xn *= 2.0f;
+    sxk *= 2.0f;
+  }
+  if (blockIdx.x == 0 && threadIdx.x == 0) {
+    gsc[k] = 128.0f / sxk;
+    gsc[gridDim.y + k] = 1.0f / sxk;
+  }
+  const float f = inv[k] * sxk;
+  for (int b = 0; b < 2; ++b) {
+    unsigned short* base = b == 0 ? X : Y;
+    if (!base) continue;
+    u32x4* q = reinterpret_cast<u32x4*>(base + k * per);
+    for (int64_t i = static_cast<int64_t>(blockIdx.x) * kThreads + threadIdx.x; i < per / 8;
+         i += static_cast<int64_t>(gridDim.x) * kThreads) {
+      u32x4 v = q[i];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const unsigned lo = f2h(bf2f(static_cast<unsigned short>(v[e] & 0xffffu)) * f);
+        const unsigned hi = f2h(bf2f(static_cast<unsigned short>(v[e] >> 16)) * f);
         v[e] = lo | (hi << 16);
       }
       q[i] = v;
@@ -274,13 +319,29 @@ hipError_t launch_muon_prep(const BucketPlan& p, const float* G, float* M, float
 }
 
 hipError_t launch_norm_finalize(const BucketPlan& p, const double* partials, float eps,
-                                float* inv, int* shift, hipStream_t s) {
+                                float* inv, int* shift, hipStream_t s, float* x0norm) {
   if (LaunchRecorder* r = launch_recorder()) {
-    r->norm(p, partials, inv, shift);
+    r->norm(p, partials, inv, shift, x0norm);
     return hipSuccess;
   }
   hipLaunchKernelGGL(norm_finalize_kernel, dim3(static_cast<unsigned>(p.K)), dim3(kThreads), 0,
-                     s, partials, p.nblk, eps, inv, shift);
+                     s, partials, p.nblk, eps, inv, shift, x0norm);
+  return hipGetLastError();
+}
+
+hipError_t launch_to_f16(const BucketPlan& p, unsigned short* S, unsigned short* T,
+                         const float* inv, const float* x0norm, float sx, float* gsc,
+                         hipStream_t s) {
+  if (LaunchRecorder* r = launch_recorder()) {
+    r->to_f16(p, S, T, inv, x0norm, gsc);
+    return hipSuccess;
+  }
+  // streams both copies once: enough blocks per matrix to fill the chip
+  const int64_t per = p.m_pad * p.n_pad;
+  const int64_t want = std::max<int64_t>(1, 2048 / std::max<int64_t>(p.K, 1));
+  const int64_t nb = std::max<int64_t>(1, std::min<int64_t>(want, (per / 8 + kThreads - 1) / kThreads));
+  hipLaunchKernelGGL(to_f16_kernel, dim3(static_cast<unsigned>(nb), static_cast<unsigned>(p.K)),
+                     dim3(kThreads), 0, s, S, T, per, inv, x0norm, sx, gsc);
   return hipGetLastError();
 }
 

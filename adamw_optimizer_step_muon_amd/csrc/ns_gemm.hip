@@ -129,6 +129,30 @@ __device__ __forceinline__ int tswz(int c, int j) {
 
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef short s16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+
+// One 32 x 32 x 16 MFMA on 16-bit operands (kTy: GemmTypes): bf16, or fp16 (the
+// Gram-space products; same rate).  The fragments are loaded as raw 16-bit values.
+template <int kTy>
+__device__ __forceinline__ f32x16 mfma_32x32x16(bf16x8 a, bf16x8 b, f32x16 c) {
+  if constexpr (kTy == kTyBf16) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+  } else {
+    return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, a),
+                                                  __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
+  }
+}
+// fp32 result -> the 16-bit type a launch writes, and a 16-bit operand -> fp32
+template <int kTy>
+__device__ __forceinline__ unsigned short to16(float f) {
+  if constexpr (kTy == kTyF16) return f2h(f);
+  else return f2bf(f);
+}
+template <int kTy>
+__device__ __forceinline__ float from16(unsigned short h) {
+  if constexpr (kTy == kTyBf16) return bf2f(h);
+  else return h2f(h);
+}
 
 // 4 bf16 of a column block: lane i of each 16-lane group receives element i % 4 of the
 // 8 bytes addressed by lane 4 e + i / 4 of its group, as element e (e = 0..3).
@@ -186,7 +210,7 @@ __device__ __forceinline__ void dma16(const unsigned short* base, int voff, unsi
   }
 }
 
-template <class C, int kEpi>
+template <class C, int kEpi, int kTy = kTyBf16>
 __global__ __launch_bounds__(C::kThreads) void ns_gemm_kernel(GemmTable table) {
   __shared__ __attribute__((aligned(16))) unsigned short smem[C::kLdsElems];
   // The table is read in place from the kernel-argument segment with the (uniform)
@@ -399,8 +423,8 @@ __global__ __launch_bounds__(C::kThreads) void ns_gemm_kernel(GemmTable table) {
       for (int i = 0; i < C::WTM; ++i)
 #pragma unroll
         for (int j = 0; j < C::WTN; ++j)
-          acc[i][j] = kSwap ? __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[cur][j], fa[cur][i], acc[i][j], 0, 0, 0)
-                            : __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[cur][i], fb[cur][j], acc[i][j], 0, 0, 0);
+          acc[i][j] = kSwap ? mfma_32x32x16<kTy>(fb[cur][j], fa[cur][i], acc[i][j])
+                            : mfma_32x32x16<kTy>(fa[cur][i], fb[cur][j], acc[i][j]);
     }
     if constexpr ((KK & 1) == 1) {
       // odd slice count: the next stage's first fragments landed in buffer 1
@@ -461,7 +485,7 @@ __global__ __launch_bounds__(C::kThreads) void ns_gemm_kernel(GemmTable table) {
             for (int e = 0; e < 4; ++e) {
               const int il = wm * (C::WTM * 32) + i * 32 + 8 * q + 4 * fkh + e;
               const unsigned int w = ax[ii][j][q][e >> 1];
-              const float t = bf2f(static_cast<unsigned short>((e & 1) ? (w >> 16) : (w & 0xffffu)));
+              const float t = from16<kTy>(static_cast<unsigned short>((e & 1) ? (w >> 16) : (w & 0xffffu)));
               float v = args.alpha * t + args.beta * acc[i][j][q * 4 + e];
               if (diag_tile && il == jl) v += args.diag;
               acc[i][j][q * 4 + e] = v;
@@ -469,10 +493,11 @@ __global__ __launch_bounds__(C::kThreads) void ns_gemm_kernel(GemmTable table) {
         }
       }
     }
-  } else if (args.scale) {
-    // first iteration: R = (inv U)(inv U)^T = inv^2 U U^T, X1 = P (inv U) = inv P U
-    const float sc = args.scale[batch];
-    const float f = (kEpi == kGram) ? sc * sc : sc;
+  } else if (args.scale || args.post != 0.0f) {
+    // first iteration: R = (inv U)(inv U)^T = inv^2 U U^T, X1 = P (inv U) = inv P U;
+    // and the Gram-space route's constant factors of its fp16 scaling
+    const float sc = args.scale ? args.scale[batch] : 1.0f;
+    const float f = ((kEpi == kGram) ? sc * sc : sc) * (args.post != 0.0f ? args.post : 1.0f);
 #pragma unroll
     for (int i = 0; i < C::WTM; ++i)
 #pragma unroll
@@ -481,7 +506,7 @@ __global__ __launch_bounds__(C::kThreads) void ns_gemm_kernel(GemmTable table) {
         for (int r = 0; r < 16; ++r) acc[i][j][r] *= f;
   }
 
-  // 2. each orientation goes through LDS (bf16) and out with 16-byte row stores
+  // 2. each orientation goes through LDS (16-bit) and out with 16-byte row stores
   __syncthreads();  // every wave is done reading the operand stages
   if (need_c) {
     // row-major tile [BM][BN]: 2-byte writes, chunk c of row r at c ^ (r % kCChunks)
@@ -499,10 +524,10 @@ __global__ __launch_bounds__(C::kThreads) void ns_gemm_kernel(GemmTable table) {
           for (int q = 0; q < 4; ++q) {
             const int cl0 = wn * (C::WTN * 32) + j * 32 + 8 * q + 4 * fkh;
             u32x2 packed;
-            packed[0] = static_cast<unsigned>(f2bf(acc[i][j][q * 4 + 0])) |
-                        (static_cast<unsigned>(f2bf(acc[i][j][q * 4 + 1])) << 16);
-            packed[1] = static_cast<unsigned>(f2bf(acc[i][j][q * 4 + 2])) |
-                        (static_cast<unsigned>(f2bf(acc[i][j][q * 4 + 3])) << 16);
+            packed[0] = static_cast<unsigned>(to16<kTy>(acc[i][j][q * 4 + 0])) |
+                        (static_cast<unsigned>(to16<kTy>(acc[i][j][q * 4 + 1])) << 16);
+            packed[1] = static_cast<unsigned>(to16<kTy>(acc[i][j][q * 4 + 2])) |
+                        (static_cast<unsigned>(to16<kTy>(acc[i][j][q * 4 + 3])) << 16);
             *reinterpret_cast<u32x2*>(
                 Cs + rl * C::BN + ((((cl0 >> 3) ^ (rl % kCChunks)) << 3) | (cl0 & 7))) = packed;
           }
@@ -513,7 +538,7 @@ __global__ __launch_bounds__(C::kThreads) void ns_gemm_kernel(GemmTable table) {
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
               const int r = wm * (C::WTM * 32) + i * 32 + 8 * q + 4 * fkh + e;
-              Cs[r * C::BN + ((((jl >> 3) ^ (r % kCChunks)) << 3) | (jl & 7))] = f2bf(acc[i][j][q * 4 + e]);
+              Cs[r * C::BN + ((((jl >> 3) ^ (r % kCChunks)) << 3) | (jl & 7))] = to16<kTy>(acc[i][j][q * 4 + e]);
             }
         }
       }
@@ -563,7 +588,7 @@ __global__ __launch_bounds__(C::kThreads) void ns_gemm_kernel(GemmTable table) {
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
             const int cl = wn * (C::WTN * 32) + j * 32 + 8 * q + 4 * fkh + e;
-            Ts[cl * C::BM + tswz<kTChunks>(rl >> 3, cl) * 8 + (rl & 7)] = f2bf(acc[i][j][q * 4 + e]);
+            Ts[cl * C::BM + tswz<kTChunks>(rl >> 3, cl) * 8 + (rl & 7)] = to16<kTy>(acc[i][j][q * 4 + e]);
           }
         continue;
       }
@@ -572,10 +597,10 @@ __global__ __launch_bounds__(C::kThreads) void ns_gemm_kernel(GemmTable table) {
       for (int q = 0; q < 4; ++q) {
         const int il0 = wm * (C::WTM * 32) + i * 32 + 8 * q + 4 * fkh;
         u32x2 packed;
-        packed[0] = static_cast<unsigned>(f2bf(acc[i][j][q * 4 + 0])) |
-                    (static_cast<unsigned>(f2bf(acc[i][j][q * 4 + 1])) << 16);
-        packed[1] = static_cast<unsigned>(f2bf(acc[i][j][q * 4 + 2])) |
-                    (static_cast<unsigned>(f2bf(acc[i][j][q * 4 + 3])) << 16);
+        packed[0] = static_cast<unsigned>(to16<kTy>(acc[i][j][q * 4 + 0])) |
+                    (static_cast<unsigned>(to16<kTy>(acc[i][j][q * 4 + 1])) << 16);
+        packed[1] = static_cast<unsigned>(to16<kTy>(acc[i][j][q * 4 + 2])) |
+                    (static_cast<unsigned>(to16<kTy>(acc[i][j][q * 4 + 3])) << 16);
         const int c = il0 >> 3, half = (il0 >> 2) & 1;
         *reinterpret_cast<u32x2*>(Ts + jl * C::BM + tswz<kTChunks>(c, jl) * 8 + half * 4) = packed;
       }
@@ -622,15 +647,28 @@ using SmallCfg = Cfg<128, 128, 64, 4, 2, 2, true>;
 // left over (the 12-layer GPT: 1296 256-tiles are 5.06 rounds, 1728 192-row tiles 6.75).
 using Mid8X = Cfg<192, 256, 64, 2, 4, 3, true, 2>;
 
-template <class C>
+template <class C, int kTy = kTyBf16>
 hipError_t launch_cfg(int epi, const GemmTable& t, hipStream_t s) {
   const int blocks = t.start[t.ngroups];
   if (blocks <= 0) return hipSuccess;
   const dim3 grid(static_cast<unsigned>(blocks));
-  switch (epi) {
-    case kGram: hipLaunchKernelGGL((ns_gemm_kernel<C, kGram>), grid, dim3(C::kThreads), 0, s, t); break;
-    case kPoly: hipLaunchKernelGGL((ns_gemm_kernel<C, kPoly>), grid, dim3(C::kThreads), 0, s, t); break;
-    default: hipLaunchKernelGGL((ns_gemm_kernel<C, kCombine>), grid, dim3(C::kThreads), 0, s, t); break;
+  if constexpr (kTy == kTyF16ToBf16) {
+    // the Gram-space route's last product only
+    if (epi != kCombine) return hipErrorInvalidValue;
+    hipLaunchKernelGGL((ns_gemm_kernel<C, kCombine, kTy>), grid, dim3(C::kThreads), 0, s, t);
+  } else if constexpr (kTy == kTyF16) {
+    // the Gram-space route's symmetric products (gram epilogue) and polynomials
+    if (epi == kCombine) return hipErrorInvalidValue;
+    if (epi == kPoly)
+      hipLaunchKernelGGL((ns_gemm_kernel<C, kPoly, kTy>), grid, dim3(C::kThreads), 0, s, t);
+    else
+      hipLaunchKernelGGL((ns_gemm_kernel<C, kGram, kTy>), grid, dim3(C::kThreads), 0, s, t);
+  } else {
+    switch (epi) {
+      case kGram: hipLaunchKernelGGL((ns_gemm_kernel<C, kGram>), grid, dim3(C::kThreads), 0, s, t); break;
+      case kPoly: hipLaunchKernelGGL((ns_gemm_kernel<C, kPoly>), grid, dim3(C::kThreads), 0, s, t); break;
+      default: hipLaunchKernelGGL((ns_gemm_kernel<C, kCombine>), grid, dim3(C::kThreads), 0, s, t); break;
+    }
   }
   return hipGetLastError();
 }
@@ -689,7 +727,13 @@ TileShape shape_of(TileCfg cfg, int pipeline) {
   }
 }
 
-hipError_t launch_table(int epi, GemmTable& t, TileCfg cfg, int pipeline, hipStream_t s) {
+hipError_t launch_table(int epi, GemmTable& t, TileCfg cfg, int pipeline, int ty, hipStream_t s) {
+  // the fp16 kernels exist for the default pipeline and the 256 and 128 tiles (the
+  // configuration search may still name the others: they run as these)
+  if (ty != kTyBf16) {
+    if (cfg == kTileMidX) cfg = kTileBigX;
+    pipeline = 1;
+  }
   // longest contraction first, so the blocks with the most work are dispatched first
   for (int i = 1; i < t.ngroups; ++i)
     for (int j = i; j > 0 && t.g[j].kdim > t.g[j - 1].kdim; --j) {
@@ -704,6 +748,16 @@ hipError_t launch_table(int epi, GemmTable& t, TileCfg cfg, int pipeline, hipStr
   if (LaunchRecorder* r = launch_recorder()) {
     r->gemm(epi, shape_of(cfg, pipeline), t);
     return hipSuccess;
+  }
+  if (ty == kTyF16) {
+    if (cfg == kTileBig) return launch_cfg<Big8K64, kTyF16>(epi, t, s);
+    if (cfg == kTileSmall) return launch_cfg<SmallCfg, kTyF16>(epi, t, s);
+    return hipErrorInvalidValue;
+  }
+  if (ty == kTyF16ToBf16) {
+    if (cfg == kTileBig) return launch_cfg<Big8K64, kTyF16ToBf16>(epi, t, s);
+    if (cfg == kTileBigX) return launch_cfg<Big8K64X, kTyF16ToBf16>(epi, t, s);
+    return launch_cfg<SmallCfg, kTyF16ToBf16>(epi, t, s);
   }
   if (cfg == kTileBig)
     return use_big8(pipeline) ? launch_cfg<Big8>(epi, t, s) : launch_cfg<Big8K64>(epi, t, s);
@@ -756,7 +810,7 @@ int pick_tile(int64_t K, int64_t m, int64_t n) {
 }
 
 hipError_t launch_gram(const NsGroup* g, int n, const float* const* scale,
-                       const GemmChoice& ch, hipStream_t s) {
+                       const GemmChoice& ch, hipStream_t s, int ty, float post) {
   const int tile = chosen_tile(*g[0].plan, ch.tile);
   GemmTable t{};
   t.ngroups = n;
@@ -771,14 +825,15 @@ hipError_t launch_gram(const NsGroup* g, int n, const float* const* scale,
     a.ldc = a.ldc2 = p.m_pad;
     a.strideC = a.strideC2 = p.m_pad * p.m_pad;
     a.scale = scale ? scale[i] : nullptr;
+    a.post = post;
     a.tiles_k = static_cast<int>(p.K);
     set_tiles(kGram, a, p, tile, tile, ch);
   }
-  return launch_table(kGram, t, tile == 256 ? kTileBig : kTileSmall, ch.pipeline, s);
+  return launch_table(kGram, t, tile == 256 ? kTileBig : kTileSmall, ch.pipeline, ty, s);
 }
 
 hipError_t launch_poly(const NsGroup* g, int n, float a_coef, float b, float c,
-                       const GemmChoice& ch, hipStream_t s) {
+                       const GemmChoice& ch, hipStream_t s, int ty) {
   const int tile_choice = ch.tile;
   // The polynomial contracts over the Gram side alone.  Where a 256-tile phase's
   // triangles fill less than two rounds of the chip, it runs on 128-tiles (two blocks
@@ -809,10 +864,10 @@ hipError_t launch_poly(const NsGroup* g, int n, float a_coef, float b, float c,
     a.tiles_k = static_cast<int>(p.K);
     set_tiles(kPoly, a, p, tile, tile, ch);
   }
-  return launch_table(kPoly, t, tile == 256 ? kTileBig : kTileSmall, ch.pipeline, s);
+  return launch_table(kPoly, t, tile == 256 ? kTileBig : kTileSmall, ch.pipeline, ty, s);
 }
 
-hipError_t launch_sym(const SymProd* pr, int n, const GemmChoice& ch, hipStream_t s) {
+hipError_t launch_sym(const SymProd* pr, int n, const GemmChoice& ch, hipStream_t s, int ty) {
   const int tile_choice = ch.tile;
   // contracts over the Gram side like the polynomial: same tile rule
   int tile = chosen_tile(*pr[0].plan, tile_choice);
@@ -837,14 +892,14 @@ hipError_t launch_sym(const SymProd* pr, int n, const GemmChoice& ch, hipStream_
     a.tiles_k = static_cast<int>(p.K);
     set_tiles(kGram, a, p, tile, tile, ch);
   }
-  return launch_table(kGram, t, tile == 256 ? kTileBig : kTileSmall, ch.pipeline, s);
+  return launch_table(kGram, t, tile == 256 ? kTileBig : kTileSmall, ch.pipeline, ty, s);
 }
 
 hipError_t launch_combine(const NsGroup* g, int n, const float* const* scale, bool last,
-                          const GemmChoice& ch, hipStream_t s) {
+                          const GemmChoice& ch, hipStream_t s, int ty, float post) {
   // a phase's buckets agree on the tile and on keeping X^T; a 256-tile phase that reads
-  // X (no X^T) may also run its combine on 128-tiles
-  bool mid = ch.tile == 192 && !forced_tile();
+  // X (no X^T) may also run its combine on 128-tiles (and on 192 x 256 tiles in bf16)
+  bool mid = ch.tile == 192 && !forced_tile() && ty == kTyBf16;
   for (int i = 0; i < n && mid; ++i) mid = combine_192_ok(*g[i].plan);
   const int tile = g[0].plan->keeps_xt ? g[0].plan->tile : chosen_tile(*g[0].plan, ch.tile);
   const TileCfg cfg = g[0].plan->keeps_xt ? kTileBig
@@ -880,10 +935,11 @@ hipError_t launch_combine(const NsGroup* g, int n, const float* const* scale, bo
       a.C2 = (last && !p.transposed) ? nullptr : g[i].XTn;
     }
     a.scale = scale ? scale[i] : nullptr;
+    a.post = post;
     a.tiles_k = static_cast<int>(p.K);
     set_tiles(kCombine, a, p, mid ? Mid8X::BM : tile, mid ? Mid8X::BN : tile, ch);
   }
-  return launch_table(kCombine, t, cfg, ch.pipeline, s);
+  return launch_table(kCombine, t, cfg, ch.pipeline, ty, s);
 }
 
 }  // namespace ma

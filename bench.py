@@ -33,7 +33,7 @@ ADAMW_BYTES_PER_ELEM = 28        # read p, g, m, v; write p, m, v (fp32)
 
 def gram_space(b, ns_mode):
     """Whether the library runs this bucket's Newton-Schulz in Gram space (its own
-    routing report: wide buckets with n >= 2 m and m <= 2048 under ns_mode 1)."""
+    routing report: buckets whose long side is at least 3x the Gram side, under ns_mode 1)."""
     if ns_mode != 1:
         return False
     import adamw_optimizer_step_muon_amd as ma
@@ -44,7 +44,7 @@ def gram_space(b, ns_mode):
 def ns_flops(wl, steps=None, symmetric=True, ns_mode=0):
     """Algorithmic Newton-Schulz FLOP of one optimizer step.  Printed iteration, per matrix
     and iteration: 3 m^2 n + m^3 with the symmetric Gram and R R^T on one triangle (dense:
-    4 m^2 n + 2 m^3).  Gram-space route (ns_mode 1, n >= 2 m), per matrix for N steps:
+    4 m^2 n + 2 m^3).  Gram-space route (ns_mode 1, n >= 3 m), per matrix for N steps:
     the Gram m^2 n, N polynomials, N - 1 products P Q, 2 (N - 1) products for R <- P R P
     (m^3 each on one triangle), and the final Q X0, 2 m^2 n: 3 m^2 n + (4 N - 3) m^3
     (dense: 4 m^2 n + (8 N - 6) m^3)."""
@@ -62,7 +62,7 @@ def ns_flops(wl, steps=None, symmetric=True, ns_mode=0):
 
 
 def ns_bytes(wl, ns_mode=0):
-    """Algorithmic HBM bytes of the Newton-Schulz launches of one step (bf16 operands and
+    """Algorithmic HBM bytes of the Newton-Schulz launches of one step (16-bit operands and
     results, each read or written once, padding ignored).  Printed iteration, per matrix
     and iteration: the Gram reads X and writes R (m n + m^2), the polynomial reads R and
     writes P (2 m^2), the combine reads P and X and writes X' (m^2 + 2 m n): 2 (3 m n +
@@ -89,8 +89,9 @@ def parse():
     ap.add_argument("--workload", type=int, default=4)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--ns-mode", type=int, default=0, choices=(0, 1),
-                    help="1: Gram-space Newton-Schulz for buckets with n >= 2 m (opt-in; its "
-                         "bf16 error is input-dependent)")
+                    help="1: the fp16 Gram-space Newton-Schulz for buckets whose long side is "
+                         "at least 3.5x the Gram side (opt-in; by default it is timed beside "
+                         "the printed iteration and reported as gram_space_route)")
     ap.add_argument("--no-tune", action="store_true",
                     help="keep the default GEMM rules instead of searching each Newton-Schulz "
                          "product's configuration once before the warm-up "
@@ -99,6 +100,9 @@ def parse():
     ap.add_argument("--calibration-copy-mib", type=int, default=0,
                     help="after timing, copy this many MiB device-to-device once (a plain "
                          "copy of known size for calibrating HBM byte counters)")
+    ap.add_argument("--no-alt-route", action="store_true",
+                    help="skip timing the opt-in fp16 Gram-space route (ns_mode 1) beside the "
+                         "printed iteration")
     ap.add_argument("--comparator", action="store_true",
                     help="also time the same Newton-Schulz chain as torch bf16 batched GEMMs "
                          "(hipBLASLt) on the workload's gradients, after the measurement")
@@ -216,6 +220,53 @@ def cpu_baseline(wl, budget_s):
                        f"matrices, each bucket scaled by K; AdamW {n_done} of {n} elements, "
                        f"scaled; numpy float64 (BLAS threads={cores}, elementwise "
                        "single-threaded)")}
+
+
+def alt_route(wl, buckets, state, adamw, stream, dev, args):
+    """The same step with the opt-in fp16 Gram-space route (ns_mode 1) for the buckets it
+    takes, timed after the headline measurement on the same state: its configuration
+    search, one warm-up step, then min(steps, 5) steps between HIP events, and its
+    Newton-Schulz launches per phase (ma_muon_ns_time)."""
+    import torch
+
+    import adamw_optimizer_step_muon_amd as ma
+
+    mh = wl.muon_hp
+    shapes = [(b.K, b.A, b.B) for b in wl.muon]
+    ws = torch.empty(max(ma.muon_workspace_bytes(shapes, 1), 1), dtype=torch.uint8, device=dev)
+    if not args.no_tune:
+        ma.muon_tune_configs(shapes, reps=3, workspace=ws, stream=stream, ns_mode=1,
+                             grads=[b[1] for b in buckets])
+    routes = []
+
+    def step():
+        state["t"] += 1
+        adamw()
+        routes[:] = ma.muon_step(buckets, lr=mh.lr, momentum=mh.momentum,
+                                 weight_decay=mh.weight_decay, nesterov=mh.nesterov,
+                                 ns_steps=mh.ns_steps, ns_eps=mh.ns_eps,
+                                 cautious_wd=mh.cautious_wd, scale_mode=mh.scale_mode,
+                                 ns_mode=1, workspace=ws, stream=stream)
+
+    step()
+    k = max(1, min(args.steps, 5))
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record(stream)
+    for _ in range(k):
+        step()
+    e1.record(stream)
+    e1.synchronize()
+    step_ms = e0.elapsed_time(e1) / k
+    phase_ms = ma.muon_ns_time([b[1] for b in buckets], reps=3, ns_steps=mh.ns_steps,
+                               ns_eps=mh.ns_eps, ns_mode=1, workspace=ws, stream=stream)
+    del ws
+    torch.cuda.empty_cache()
+    return {"ns_mode": 1, "operands": "fp16 (Gram-space products), bf16 result",
+            "buckets_on_route": [int(r.ns_mode_run) for r in routes], "steps": k,
+            "step_ms": round(step_ms, 4), "ns_ms": round(sum(phase_ms), 4),
+            "ns_phase_ms": [round(x, 4) for x in phase_ms],
+            "ns_tflops_algorithmic": round(ns_flops(wl, ns_mode=1) / (sum(phase_ms) * 1e-3) / 1e12, 1)}
 
 
 def blas_comparator(grads, coeffs, ns_steps, stream, reps=3):
@@ -501,6 +552,8 @@ def main():
         dst.copy_(src)
         torch.cuda.synchronize()
         out["calibration_copy_bytes"] = nbytes
+    if args.ns_mode == 0 and not args.no_alt_route and any(gram_space(b, 1) for b in wl.muon):
+        out["gram_space_route"] = alt_route(wl, buckets, state, adamw, stream, dev, args)
     if args.comparator:
         comp = blas_comparator([b[1] for b in buckets], mh.coeffs, mh.ns_steps, stream)
         comp["speedup_of_this_library"] = round(comp["ns_ms"] / ns_ms, 3)

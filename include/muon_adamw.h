@@ -81,21 +81,25 @@ typedef struct {
   const float* ns_coeffs; /* host, ns_steps x 3 (a, b, c) per iteration; NULL selects
                              the quintic (3.4445, -4.7750, 2.0315) for every iteration */
   int32_t ns_mode;        /* 0: the iteration as printed [HB] (default).
-                             1: Gram-space iteration ([DMuon] section 2.2) for wide buckets
-                             (A < B) with B >= 2 A and A <= 1024 (others as 0, reported in
+                             1: Gram-space iteration ([DMuon] section 2.2) for buckets
+                             whose long side is at least 3.5x the Gram side, in either
+                             orientation (others as 0, reported in
                              ma_muon_route.ns_mode_run): R0 = X0 X0^T once, then per step
-                             P = a I + b R + c R^2, Q <- P Q, R <- P R P on A x A matrices,
-                             and X = Q X0 at the end: 3 m^2 n + ~4 N m^3 instead of
-                             N (3 m^2 n + m^3) FLOP for N steps (symmetric counts).  Exact
-                             in real arithmetic; in bf16 its error depends on the input:
-                             R holds squared singular values, whose small end bf16 loses,
-                             and the recurrence carries that loss on.  Inside the domain
-                             it was measured within 2e-2 of the printed iteration on
-                             Gaussian, low-rank and row-scaled gradients, but NOT on
-                             gradients with condition numbers near 1e4 (6e-2 to 1.5e-1 at
-                             every Gram side); tall row-scaled gradients and low-rank ones
-                             with Gram sides from 1536 (2e-2 to 5e-2) are why the domain
-                             stops where it does.  Opt-in, for well-conditioned inputs. */
+                             P = a I + b R + c R^2, Q <- P Q, R <- P R P on m x m matrices
+                             (m the Gram side), and X = Q X0 at the end: 3 m^2 n +
+                             (4 N - 3) m^3 instead of N (3 m^2 n + m^3) FLOP for N steps
+                             (symmetric counts; 2.1x fewer at n = 3.5 m and N = 5).  Exact
+                             in real arithmetic; R holds squared singular values, so the
+                             route runs on fp16 operands (three more significand bits
+                             than bf16, same MFMA rate, fp32 accumulation) scaled by
+                             powers of two into fp16's range, and returns bf16.  Its error
+                             was measured at 2-7e-3 against the exact iteration on
+                             Gaussian, low-rank, row-scaled and condition-1e4 gradients at
+                             the workloads' sizes, at most 1.3e-2 on small conditioned
+                             ones (the printed iteration's bf16 path: 7-10e-3).  Taken only
+                             when the coefficients keep every stored value inside fp16
+                             (the quintic: up to 8 steps, since Q grows as a^N on a zero
+                             singular value); else the bucket runs as under 0. */
 } ma_muon_hparams;
 
 #define MA_MAX_NS_STEPS 64

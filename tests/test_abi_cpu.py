@@ -149,7 +149,7 @@ FAKE = 0x10000000  # never dereferenced: every call below fails validation first
 ])
 def test_muon_step_rejects_before_launch(lib, case, status):
     K, A, B = 2, 64, 96
-    size = K * A * B * 4
+    size = K * A * 256 * 4  # room for the wider bucket of the Gram-space case
     bucket = _lib._MuonBucket(K, A, B, FAKE, FAKE + 2 * size, FAKE + 4 * size)
     hp = _hp()
     hp_ptr = ctypes.byref(hp)
@@ -166,8 +166,8 @@ def test_muon_step_rejects_before_launch(lib, case, status):
     elif case == "bad_ns_mode":
         hp.ns_mode = 2
     elif case == "small_gram_space_workspace":
-        # 64 x 96 is not 2:1, so 64 x 160 is used: its Gram-space plan needs more
-        bucket.B = 160
+        # 64 x 96 is not 3.5:1, so 64 x 224 is used: its Gram-space plan needs more
+        bucket.B = 224
         hp.ns_mode = 1
         ws_bytes = lib.ma_muon_workspace_bytes(ctypes.byref(bucket), 1, None)
     elif case == "nan_lr":
@@ -181,7 +181,7 @@ def test_muon_step_rejects_before_launch(lib, case, status):
     elif case == "misaligned":
         bucket.grad = FAKE + 2 * size + 2
     elif case == "overlap":
-        bucket.grad = FAKE + size // 2
+        bucket.grad = FAKE + 256   # inside the parameters
     elif case == "no_workspace":
         ws = None
     elif case == "small_workspace":
@@ -310,22 +310,30 @@ def test_tune_rejects_bad_arguments_before_launch(lib):
 
 
 def test_gram_space_routing_and_workspace(lib):
-    """ns_mode 1 routes wide buckets (A < B) with B >= 2 A and A <= 1024 through the
-    Gram-space iteration, in phases of their own, with four more m x m buffers; tall
-    buckets and wider Gram sides keep the printed iteration."""
-    mlp, sq = (12, 768, 3072), (48, 768, 768)
-    assert ma.muon_phases([sq, mlp, (12, 3072, 768)]) == (1, [0, 0, 0])
-    assert ma.muon_phases([sq, mlp, (12, 3072, 768)], ns_mode=1) == (3, [0, 1, 2])
-    for (A, B), gs in [((768, 3072), 1), ((3072, 768), 0), ((1024, 2048), 1), ((1024, 2047), 0),
-                       ((1025, 4096), 0), ((2048, 4096), 0), ((2560, 5120), 0), ((64, 128), 1),
-                       ((1, 7), 1), ((512, 2048), 1), ((2048, 512), 0), ((768, 768), 0)]:
+    """ns_mode 1 routes buckets whose long side is at least 3.5x the Gram side (either
+    orientation, any Gram side) through the Gram-space iteration, in phases of their own
+    (shared by Gram-space buckets of one tile), with four more m x m buffers; squarer
+    buckets keep the printed iteration."""
+    mlp, sq, down = (12, 768, 3072), (48, 768, 768), (12, 3072, 768)
+    assert ma.muon_phases([sq, mlp, down]) == (1, [0, 0, 0])
+    assert ma.muon_phases([sq, mlp, down], ns_mode=1) == (2, [0, 1, 1])
+    # Gram-space buckets of one tile share a phase whatever their fp16 scales (the
+    # products apply them per matrix)
+    assert ma.muon_phases([mlp, (4, 512, 2048), (12, 1024, 4096)], ns_mode=1)[0] == 1
+    for (A, B), gs in [((768, 3072), 1), ((3072, 768), 1), ((1024, 2048), 0), ((1024, 3072), 0),
+                       ((1024, 3584), 1), ((1024, 3583), 0), ((3584, 1024), 1),
+                       ((2048, 4096), 0), ((2048, 8192), 1), ((8192, 28672), 1),
+                       ((28672, 8192), 1), ((2560, 5120), 0), ((64, 128), 0), ((64, 224), 1),
+                       ((64, 223), 0), ((1, 7), 1), ((2, 7), 1), ((2, 6), 0), ((512, 2048), 1),
+                       ((2048, 512), 1), ((768, 768), 0)]:
         assert ma.muon_route_of(A, B, 5, ns_mode=1).ns_mode_run == gs, (A, B)
         assert ma.muon_route_of(A, B, 5, ns_mode=0).ns_mode_run == 0
         assert ma.muon_route_of(A, B, 0, ns_mode=1).ns_mode_run == 0
     m_pad = 768 if not os.environ.get("MA_NS_TILE") else None
     extra = ma.muon_workspace_bytes([mlp], ns_mode=1) - ma.muon_workspace_bytes([mlp])
     if m_pad:
-        assert extra == 4 * 12 * m_pad * m_pad * 2
+        # R2, Q[0], Q[1], T, and 3 K floats of per-matrix norms and factors (256-aligned)
+        assert extra == 4 * 12 * m_pad * m_pad * 2 + 256
     assert ma.muon_workspace_bytes([sq], ns_mode=1) == ma.muon_workspace_bytes([sq])
     assert ma.muon_workspace_bytes([(3, 100, 199)], ns_mode=1) == ma.muon_workspace_bytes(
         [(3, 100, 199)])
