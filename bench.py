@@ -118,6 +118,9 @@ def source_hash(name):
         return hashlib.sha256(f.read()).hexdigest()[:16]
 
 
+ns_mode_of_run = 0  # set by main: the committed summaries profile the printed iteration
+
+
 def counted_traffic(summary, source, key="traffic_bytes_per_launch"):
     """A figure (HBM bytes per launch by default) from a committed rocprofv3 counter
     summary, or None when the summary is missing or the kernel source changed since."""
@@ -125,6 +128,8 @@ def counted_traffic(summary, source, key="traffic_bytes_per_launch"):
     if not os.path.exists(path):
         return None
     vals = {}
+    if ns_mode_of_run != 0:
+        return None  # the summaries describe the default route's launches
     with open(path) as f:
         for line in f:
             parts = line.split()
@@ -356,6 +361,8 @@ def main():
     import workloads
     from workloads import gen
 
+    global ns_mode_of_run
+    ns_mode_of_run = args.ns_mode
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     wl = workloads.workload(args.workload)
