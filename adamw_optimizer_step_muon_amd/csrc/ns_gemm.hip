@@ -142,11 +142,19 @@ __device__ __forceinline__ f32x16 mfma_32x32x16(bf16x8 a, bf16x8 b, f32x16 c) {
                                                   __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
   }
 }
-// fp32 result -> the 16-bit type a launch writes, and a 16-bit operand -> fp32
+// fp32 result -> the 16-bit type a launch writes, and a 16-bit operand -> fp32.  The
+// fp16 conversion takes the finished fp32 value: the compiler would otherwise fold it
+// into the epilogue's last multiply-add (v_fma_mixlo_f16, one rounding instead of two)
+// in some instantiations and not in others, so tile shapes would differ in the last
+// bit (the empty asm only pins the value in a register; it emits nothing).
 template <int kTy>
 __device__ __forceinline__ unsigned short to16(float f) {
-  if constexpr (kTy == kTyF16) return f2h(f);
-  else return f2bf(f);
+  if constexpr (kTy == kTyF16) {
+    asm volatile("" : "+v"(f));
+    return f2h(f);
+  } else {
+    return f2bf(f);
+  }
 }
 template <int kTy>
 __device__ __forceinline__ float from16(unsigned short h) {

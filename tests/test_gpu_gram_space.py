@@ -157,3 +157,37 @@ def test_gram_space_input_range(scale, eps):
     ref = oracle.newton_schulz(G[0], 5, eps=eps)
     err = rel_fro(go.cpu().numpy()[0], ref)
     assert err <= MUON_RTOL, (scale, eps, err)
+
+
+def test_optimizer_group_takes_the_gram_space_route():
+    """MuonAdamW with ns_mode 1 in its group, over a model's separate MLP matrices
+    (768 x 3072 and 3072 x 768, 4:1) and attention matrices (768 x 768): the MLP buckets
+    run the Gram-space route in one phase, the square one the printed iteration; two
+    steps bit for bit the stacked ma_muon_step with ns_mode 1."""
+    shapes = [(768, 768), (768, 3072), (3072, 768)]
+    gen_ = torch.Generator(device=DEV).manual_seed(5)
+    params = [torch.nn.Parameter(torch.randn(s, generator=gen_, device=DEV))
+              for _ in range(4) for s in shapes]
+    grads = [[0.02 * torch.randn(p.shape, generator=gen_, device=DEV) for p in params]
+             for _ in range(2)]
+    stacks = [torch.stack([p.detach().clone() for p in params if tuple(p.shape) == s])
+              for s in shapes]
+    opt = ma.MuonAdamW([{"params": params, "kind": "muon", "lr": LR, "momentum": MU,
+                         "weight_decay": WD, "ns_mode": 1}])
+    assert opt.muon_buckets() == [(4, 768, 768), (4, 768, 3072), (4, 3072, 768)]
+    assert ma.muon_phases(opt.muon_buckets(), ns_mode=1) == (2, [0, 1, 1])
+    moms = [torch.zeros_like(s) for s in stacks]
+    for t in range(2):
+        for p, g in zip(params, grads[t]):
+            p.grad = g.clone()
+        opt.step()
+        gst = [torch.stack([g for p, g in zip(params, grads[t]) if tuple(p.shape) == s])
+               for s in shapes]
+        routes = ma.muon_step(list(zip(stacks, gst, moms)), lr=LR, momentum=MU,
+                              weight_decay=WD, ns_mode=1)
+        assert [r.ns_mode_run for r in routes] == [0, 1, 1]
+        torch.cuda.synchronize()
+        for s, st in zip(shapes, stacks):
+            mine = [p.detach() for p in params if tuple(p.shape) == s]
+            assert all(torch.equal(a, b) for a, b in zip(mine, st)), (t, s)
+        opt.zero_grad()

@@ -10,7 +10,7 @@ ma = pytest.importorskip("adamw_optimizer_step_muon_amd")
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda:0"
-SHAPES = [(3, 200, 330), (2, 390, 130), (2, 130, 390), (4, 256, 256)]
+SHAPES = [(3, 200, 330), (2, 455, 130), (2, 130, 455), (4, 256, 256)]
 
 
 def _state(seed):
@@ -24,7 +24,10 @@ def _state(seed):
 
 @pytest.mark.parametrize("ns_mode", [0, 1])
 def test_muon_step_graph_replays_match_eager(ns_mode):
-    """ns_mode 1 routes the wide 130 x 390 bucket through the Gram-space launches."""
+    """ns_mode 1 routes the 3.5:1 buckets (130 x 455 and its transpose) through the fp16
+    Gram-space launches."""
+    assert [ma.muon_route_of(A, B, 5, ns_mode=ns_mode).ns_mode_run for _, A, B in SHAPES] == \
+        [0, ns_mode, ns_mode, 0]
     ps, gs, ms = _state(5)
     ps_e, ms_e = [p.clone() for p in ps], [m.clone() for m in ms]
     ws = torch.empty(ma.muon_workspace_bytes(SHAPES, ns_mode), dtype=torch.uint8, device=DEV)

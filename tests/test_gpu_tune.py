@@ -143,3 +143,39 @@ def test_pinned_configurations_are_bitwise_identical(config):
         assert _same(got, ref), config
     finally:
         ma.muon_tune_reset()
+
+
+GS_SHAPES = [(8, 2048, 8192), (8, 8192, 2048)]  # one 256-tile Gram-space phase
+
+
+def _step_gs(state, ws):
+    bks = [(p.clone(), g, m.clone()) for p, g, m in state]
+    routes = ma.muon_step(bks, lr=0.02, momentum=0.95, weight_decay=0.1, ns_mode=1, workspace=ws)
+    assert [r.ns_mode_run for r in routes] == [1, 1]
+    torch.cuda.synchronize()
+    return bks
+
+
+@pytest.mark.parametrize("config", [{"tile": 128}, {"tile": 256, "pipeline": 2},
+                                    {"band": 2}, {"band": 8}, {"spread": 0}, {"xcd": 2}])
+def test_gram_space_configurations_are_bitwise_identical(config):
+    """The fp16 Gram-space launches under each pinned configuration (the fp16 kernels run
+    the default pipeline, so a pinned second pipeline runs as the default) and under the
+    searched one: bitwise the default's."""
+    shapes = GS_SHAPES
+    assert ma.muon_phases(shapes, ns_mode=1) == (1, [0, 0])
+    state = _state(shapes, 11)
+    ws = torch.empty(ma.muon_workspace_bytes(shapes, ns_mode=1), dtype=torch.uint8, device="cuda")
+    ma.muon_tune_reset()
+    try:
+        ref = _step_gs(state, ws)
+        # (the combine of a phase that reads X has no pipeline choice)
+        comb = {"tile": 256} if "pipeline" in config else config
+        ma.muon_tune_configs(shapes, reps=0, configs=[[config, config, comb]], ns_mode=1)
+        assert _same(_step_gs(state, ws), ref), config
+        ma.muon_tune_reset()
+        cfg = ma.muon_tune_configs(shapes, reps=2, workspace=ws, ns_mode=1)
+        print(f"gram-space: searched {cfg}", flush=True)
+        assert _same(_step_gs(state, ws), ref)
+    finally:
+        ma.muon_tune_reset()
