@@ -271,7 +271,10 @@ def alt_route(wl, buckets, state, adamw, stream, dev, args):
             "buckets_on_route": [int(r.ns_mode_run) for r in routes], "steps": k,
             "step_ms": round(step_ms, 4), "ns_ms": round(sum(phase_ms), 4),
             "ns_phase_ms": [round(x, 4) for x in phase_ms],
-            "ns_tflops_algorithmic": round(ns_flops(wl, ns_mode=1) / (sum(phase_ms) * 1e-3) / 1e12, 1)}
+            "ns_tflops_algorithmic": round(ns_flops(wl, ns_mode=1) / (sum(phase_ms) * 1e-3) / 1e12, 1),
+            # the printed iteration's FLOP count over this route's time: the rate a printed
+            # iteration would need to match it (context for the saving, not a kernel rate)
+            "ns_tflops_printed_equivalent": round(ns_flops(wl, ns_mode=0) / (sum(phase_ms) * 1e-3) / 1e12, 1)}
 
 
 def blas_comparator(grads, coeffs, ns_steps, stream, reps=3):
