@@ -191,3 +191,50 @@ def test_optimizer_group_takes_the_gram_space_route():
             mine = [p.detach() for p in params if tuple(p.shape) == s]
             assert all(torch.equal(a, b) for a, b in zip(mine, st)), (t, s)
         opt.zero_grad()
+
+
+@pytest.mark.parametrize("index", [1, 2, 3])
+def test_gram_space_full_size_workloads(index, capsys):
+    """Each GPT workload at full size under ns_mode 1, in one ma_muon_step over all its
+    buckets, for three steps: its 4:1 buckets (MLP up and down projections; the 24-layer
+    model's 2048 x 512 key/value projections too) take the fp16 Gram-space route, the
+    square ones the printed iteration; the first and last matrix of every Gram-space
+    bucket against the oracle at every step, stepped from the GPU's previous parameters
+    and the oracle's own momentum."""
+    import workloads
+    from test_gpu_muon import _oracle_check_step
+    from workloads import gen
+
+    wl = workloads.workload(index)
+    hp = wl.muon_hp
+    ps, gs, ms = [], [], []
+    for bi, b in enumerate(wl.muon):
+        p = torch.empty((b.K, b.A, b.B), dtype=torch.float32, device=DEV)
+        gen.torch_muon_bucket(torch, wl, bi, 0, p)
+        ps.append(p)
+        gs.append(torch.empty_like(p))
+        ms.append(torch.zeros_like(p))
+    on_route = [2 * max(b.A, b.B) >= 7 * min(b.A, b.B) for b in wl.muon]
+    picks = [(bi, k) for bi, b in enumerate(wl.muon) if on_route[bi] for k in sorted({0, b.K - 1})]
+    prev = {pk: ps[pk[0]][pk[1]].cpu().numpy().astype(np.float64) for pk in picks}
+    mom = {pk: np.zeros((wl.muon[pk[0]].A, wl.muon[pk[0]].B)) for pk in picks}
+    worst = 0.0
+    for t in range(1, 4):
+        for bi in range(len(wl.muon)):
+            gen.torch_muon_bucket(torch, wl, bi, t, gs[bi])
+        grads = {pk: gs[pk[0]][pk[1]].cpu().numpy() for pk in picks}
+        routes = ma.muon_step(list(zip(ps, gs, ms)), lr=hp.lr, momentum=hp.momentum,
+                              weight_decay=hp.weight_decay, cautious_wd=hp.cautious_wd,
+                              ns_mode=1)
+        torch.cuda.synchronize()
+        assert [r.ns_mode_run for r in routes] == [int(x) for x in on_route]
+        for bi, k in picks:
+            b = wl.muon[bi]
+            got_p = ps[bi][k].cpu().numpy()
+            mom[(bi, k)], err = _oracle_check_step(prev[(bi, k)], grads[(bi, k)], mom[(bi, k)],
+                                                   got_p, ms[bi][k].cpu().numpy(), b.A, b.B, hp)
+            prev[(bi, k)] = got_p.astype(np.float64)
+            worst = max(worst, err)
+        with capsys.disabled():
+            print(f"gram-space workload {index} step {t}: worst update error {worst:.3e}",
+                  flush=True)
