@@ -53,7 +53,7 @@ int main() {
   };
   for (const auto& l : lists) {
     for (int mode = 0; mode < 2; ++mode)
-      for (int steps : {0, 1, 5}) {
+      for (int steps : {0, 1, 5, 9}) {
         ma_muon_hparams hp = hp_of(mode, steps);
         ma_plan_report rep;
         EXPECT(ma_muon_check_plan(l.data(), (int)l.size(), &hp, 0, &rep) == MA_OK);
