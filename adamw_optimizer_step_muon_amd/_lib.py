@@ -31,6 +31,7 @@ EXPORTED = (
     "ma_muon_step_static", "ma_muon_tune_configs", "ma_stream_probe", "ma_mfma_probe",
 )
 MA_STATIC_WORKSPACE_BYTES = 512 << 20
+ABI_VERSION = 4  # include/muon_adamw.h MA_ABI_VERSION
 
 
 class MuonAdamWError(RuntimeError):
@@ -108,6 +109,11 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
             "(python -c 'import __graft_entry__ as g; g.build()')")
     lib = ctypes.CDLL(path)
     lib.ma_abi_version.restype = ctypes.c_int
+    # the structures below are laid out for this ABI; a library built from other sources
+    # would read them wrongly
+    if lib.ma_abi_version() != ABI_VERSION:
+        raise RuntimeError(f"{path} has ABI version {lib.ma_abi_version()}, this binding "
+                           f"expects {ABI_VERSION}: rebuild the library")
     lib.ma_status_string.restype = ctypes.c_char_p
     lib.ma_status_string.argtypes = [ctypes.c_int]
     lib.ma_last_error.restype = ctypes.c_char_p

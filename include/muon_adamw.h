@@ -48,7 +48,7 @@
 extern "C" {
 #endif
 
-#define MA_ABI_VERSION 3
+#define MA_ABI_VERSION 4
 
 typedef enum {
   MA_OK = 0,

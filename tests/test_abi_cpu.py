@@ -40,7 +40,7 @@ def test_exports_every_declared_symbol(lib):
 
 def test_abi_version_matches_header(lib):
     m = re.search(r"#define MA_ABI_VERSION (\d+)", open(HEADER).read())
-    assert lib.ma_abi_version() == int(m.group(1))
+    assert lib.ma_abi_version() == int(m.group(1)) == _lib.ABI_VERSION
     assert lib.ma_status_string(0) == b"ok"
     assert lib.ma_status_string(-3).startswith(b"workspace")
 
