@@ -24,6 +24,10 @@ them), and a single ma_muon_step runs all buckets, so buckets that share a GEMM
 configuration share its launches.  Parameters without a gradient are not stepped.
 State is fp32 and zero-initialised: ``momentum_buffer`` (4 bytes per Muon parameter),
 ``exp_avg`` and ``exp_avg_sq`` (8 bytes per AdamW parameter).
+
+A Muon group's ``ns_mode`` (0 by default) selects the Newton-Schulz route: 1 runs the
+Gram-space iteration ("DMuon", section 2.2) on fp16 operands for the buckets whose long
+side is at least 3.5x the other (MLP projections), the printed iteration elsewhere.
 """
 from __future__ import annotations
 
