@@ -44,6 +44,7 @@
 // Sizes are padded to the tile by the caller and the padding is zero (preserved by
 // the iteration), so there are no bounds checks inside.
 #include <cstdlib>
+#include <type_traits>
 
 #include "ma_internal.h"
 
@@ -176,6 +177,20 @@ __device__ __forceinline__ void wait_vmcnt() {
   __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
 }
 
+// The block-wide step between two operand stages: this wave's LDS reads have completed
+// (lgkmcnt(0)), then s_barrier.  After it other waves load the next stages into the
+// slots just read, so no read of those slots may be left behind it.  The s_barrier
+// builtin does not order memory accesses for the compiler: in the polynomial kernels
+// with 128-row tiles it moved a stage's last fragment reads (whose only uses, the
+// stage's last MFMAs, follow the barrier) into the block after it, and the results
+// changed from run to run.  As one asm statement with a memory clobber neither the
+// reads nor the DMAs can cross it.  The builtin lgkmcnt(0) before it is the same wait,
+// visible to the compiler's own wait counting.
+__device__ __forceinline__ void stage_barrier() {
+  __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0), vmcnt and expcnt untouched
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
 
 // Resource of a buffer of `bytes` bytes at the wave-uniform `base` (reads past `bytes`
 // return zero: the hardware range check).
@@ -228,7 +243,11 @@ __global__ __launch_bounds__(C::kThreads) void ns_gemm_kernel(GemmTable table) {
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  // the wave index is uniform across the wave: as a scalar it keeps the per-wave LDS
+  // destinations of the operand DMAs (the m0 operand) and the fragment bases in scalar
+  // registers, which halved the main loop's vector ALU instructions (76 -> 38 per
+  // stage of the 256-tile kernels) and measured 0.4 % faster on 8192-wide Gram sides
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave / C::WN;
   const int wn = wave % C::WN;
 
@@ -395,35 +414,60 @@ __global__ __launch_bounds__(C::kThreads) void ns_gemm_kernel(GemmTable table) {
   };
   bf16x8 fa[2][C::WTM], fb[2][C::WTN];
   wait_stage(0);
-  __builtin_amdgcn_s_barrier();
+  stage_barrier();
   load_frags(0, 0, fa[0], fb[0]);
   capture(0);
-  for (int kt = 0; kt < nk; ++kt) {
-    // issue group kt: its slots were last read before the barrier that ended stage kt - 1
-    const bool load_next = kt + (C::LA < C::LB ? C::LA : C::LB) < nk;  // group kt not empty
-    if (load_next && !args.spread) {
+  // The wait for stage kt + 1 once every DMA after it is still in flight (the steady
+  // state of wait_stage, with no branch on the stage index).
+  auto wait_next_steady = [&]() {
+    if constexpr (C::SB != C::SA) {
+      constexpr int kDeep = C::kBFirst ? C::kDmaA : C::kDmaB;
+      wait_vmcnt<kDeep>();
+    } else if constexpr (C::STAGES >= 3) {
+      wait_vmcnt<(C::STAGES - 2) * L>();
+    } else {
+      wait_vmcnt<0>();
+    }
+  };
+  // One stage.  kSteady: every DMA group of the ring still has a stage to load and a
+  // next stage exists, so the stage is straight-line code (no branch on kt): the
+  // compiler's wait counts are then exact and the next stage's first fragment reads
+  // overlap the last k-slice's MFMAs as intended, where a branch around them made it
+  // wait for every LDS read before that slice's second MFMA.  kSpread: the DMA issue
+  // pattern (chosen once per block).
+  auto run_stage = [&](int kt, auto steady_tag, auto spread_tag) {
+    constexpr bool kSteady = decltype(steady_tag)::value;
+    constexpr bool kSpread = decltype(spread_tag)::value;
+    auto issue = [&](int d) {
+      if constexpr (kSteady) issue_one(kt + (is_a(d) ? C::LA : C::LB), d);
+      else issue_group_one(kt, d);
+    };
+    const bool load_next = kSteady || kt + (C::LA < C::LB ? C::LA : C::LB) < nk;
+    if constexpr (!kSpread) {
+      if (load_next) {
 #pragma unroll
-      for (int d = 0; d < L; ++d) issue_group_one(kt, d);
+        for (int d = 0; d < L; ++d) issue(d);
+      }
     }
 #pragma unroll
     for (int kk = 0; kk < KK; ++kk) {
       const int cur = kk & 1;
-      // spread: the next stage's DMAs go out over the first half of this stage's
-      // k-slices, between MFMA groups, instead of as one burst after the barrier
       constexpr int kHalf = KK / 2 > 0 ? KK / 2 : 1;
       constexpr int kPer = (C::kDmaPerStage + kHalf - 1) / kHalf;
-      if (load_next && args.spread && kk < kHalf) {
+      if constexpr (kSpread) {
+        if (load_next && kk < kHalf) {
 #pragma unroll
-        for (int e = 0; e < kPer; ++e)
-          if (kk * kPer + e < C::kDmaPerStage) issue_group_one(kt, kk * kPer + e);
+          for (int e = 0; e < kPer; ++e)
+            if (kk * kPer + e < C::kDmaPerStage) issue(kk * kPer + e);
+        }
       }
       if (kk + 1 < KK) {
         load_frags(kt, kk + 1, fa[cur ^ 1], fb[cur ^ 1]);
-      } else if (kt + 1 < nk) {
-        // every wave's reads of this stage are done and stage kt+1 has landed
-        __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0), vmcnt and expcnt untouched
-        wait_stage(kt + 1);
-        __builtin_amdgcn_s_barrier();
+      } else if (kSteady || kt + 1 < nk) {
+        // stage kt+1 has landed and every wave's reads of this stage are done
+        if constexpr (kSteady) wait_next_steady();
+        else wait_stage(kt + 1);
+        stage_barrier();
         load_frags(kt + 1, 0, fa[cur ^ 1], fb[cur ^ 1]);
         capture(kt + 1);
       }
@@ -441,6 +485,19 @@ __global__ __launch_bounds__(C::kThreads) void ns_gemm_kernel(GemmTable table) {
 #pragma unroll
       for (int j = 0; j < C::WTN; ++j) fb[0][j] = fb[1][j];
     }
+  };
+  // steady stages while every DMA group and the next stage exist, then the last ones
+  constexpr int kTail = C::kLead > C::STAGES ? C::kLead : C::STAGES;
+  auto run_all = [&](auto spread_tag) {
+    int kt = 0;
+    for (; kt < nk - kTail; ++kt) run_stage(kt, std::true_type{}, spread_tag);
+    for (; kt < nk; ++kt) run_stage(kt, std::false_type{}, spread_tag);
+  };
+  if constexpr (C::BM < 192) {
+    run_all(std::false_type{});  // 128-tiles never spread their DMAs
+  } else {
+    if (args.spread) run_all(std::true_type{});
+    else run_all(std::false_type{});
   }
 
   // ---------------- epilogue ----------------
@@ -494,7 +551,10 @@ __global__ __launch_bounds__(C::kThreads) void ns_gemm_kernel(GemmTable table) {
               const int il = wm * (C::WTM * 32) + i * 32 + 8 * q + 4 * fkh + e;
               const unsigned int w = ax[ii][j][q][e >> 1];
               const float t = from16<kTy>(static_cast<unsigned short>((e & 1) ? (w >> 16) : (w & 0xffffu)));
-              float v = args.alpha * t + args.beta * acc[i][j][q * 4 + e];
+              // one rounding order for every tile shape: left to the compiler, the
+              // sum of two products was fused either way round depending on the
+              // instantiation, and tile shapes differed in the last bit
+              float v = __builtin_fmaf(args.beta, acc[i][j][q * 4 + e], args.alpha * t);
               if (diag_tile && il == jl) v += args.diag;
               acc[i][j][q * 4 + e] = v;
             }

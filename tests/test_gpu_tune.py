@@ -179,3 +179,25 @@ def test_gram_space_configurations_are_bitwise_identical(config):
         assert _same(_step_gs(state, ws), ref)
     finally:
         ma.muon_tune_reset()
+
+
+@pytest.mark.parametrize("shape", [(43, 768, 1024), (8, 2048, 2048)])
+@pytest.mark.parametrize("config", [{"tile": 128}, {"tile": 256, "spread": 0},
+                                    {"tile": 256, "spread": 1}])
+def test_repeated_steps_are_bitwise_identical(shape, config):
+    """The same step three times on the same inputs, every product on one tile shape:
+    bitwise identical results.  Each wave finishes its LDS reads of an operand stage
+    before the barrier after which the other waves load later stages into those slots;
+    a read left behind that barrier makes the results change from run to run (where the
+    reference comparisons, with their tolerance, may not notice)."""
+    shapes = [shape]
+    state = _state(shapes, 12)
+    ws = torch.empty(ma.muon_workspace_bytes(shapes), dtype=torch.uint8, device="cuda")
+    ma.muon_tune_reset()
+    try:
+        ma.muon_tune_configs(shapes, reps=0, configs=[[config, config, config]])
+        ref = _step(state, ws)
+        for rep in range(2):
+            assert _same(_step(state, ws), ref), (config, rep)
+    finally:
+        ma.muon_tune_reset()
