@@ -201,3 +201,22 @@ def test_repeated_steps_are_bitwise_identical(shape, config):
             assert _same(_step(state, ws), ref), (config, rep)
     finally:
         ma.muon_tune_reset()
+
+
+@pytest.mark.parametrize("config", [{"tile": 128}, {"tile": 256, "spread": 0},
+                                    {"tile": 256, "spread": 1}])
+def test_repeated_gram_space_steps_are_bitwise_identical(config):
+    """The same repetition on the fp16 Gram-space route (ns_mode 1), whose symmetric
+    products and polynomials run the same main loop on fp16 operands."""
+    shapes = GS_SHAPES
+    state = _state(shapes, 13)
+    ws = torch.empty(ma.muon_workspace_bytes(shapes, ns_mode=1), dtype=torch.uint8, device="cuda")
+    ma.muon_tune_reset()
+    try:
+        comb = {"tile": 256} if config["tile"] == 256 else config
+        ma.muon_tune_configs(shapes, reps=0, configs=[[config, config, comb]], ns_mode=1)
+        ref = _step_gs(state, ws)
+        for rep in range(2):
+            assert _same(_step_gs(state, ws), ref), (config, rep)
+    finally:
+        ma.muon_tune_reset()
