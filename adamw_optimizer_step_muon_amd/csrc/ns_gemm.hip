@@ -38,9 +38,10 @@
 //     on a contiguous run of tiles, and those runs are grouped by row panels, so
 //     the blocks resident on one XCD share operand panels in its L2;
 //   * epilogue: b/c terms (and a on the diagonal) or the first iteration's
-//     normalisation in fp32 in registers, round to bf16; each orientation
-//     (row-major, and the transposed / mirrored copy) is staged through an
-//     XOR-swizzled LDS tile and written with 16-byte row stores.
+//     normalisation in fp32 in registers, round to bf16; the tile is staged once in an
+//     XOR-swizzled LDS tile and both orientations (row-major, and the transposed /
+//     mirrored copy) leave with 16-byte row stores, the second through transposing
+//     LDS reads.
 // Sizes are padded to the tile by the caller and the padding is zero (preserved by
 // the iteration), so there are no bounds checks inside.
 #include <cstdlib>
@@ -574,116 +575,108 @@ __global__ __launch_bounds__(C::kThreads) void ns_gemm_kernel(GemmTable table) {
         for (int r = 0; r < 16; ++r) acc[i][j][r] *= f;
   }
 
-  // 2. each orientation goes through LDS (16-bit) and out with 16-byte row stores
+  // 2. the tile goes through LDS (16-bit) once, staged in the orientation the
+  // accumulator layout writes 8 bytes at a time: the transposed tile [BN][BM] for the
+  // plain layout (a lane's 4 consecutive rows), the row-major tile [BM][BN] for the
+  // swapped one (its 4 consecutive columns).  Rows of the staged tile leave with
+  // 16-byte stores as the orientation they hold; the other orientation is read out of
+  // the same staging with the transposing LDS loads (ds_read_b64_tr_b16), 16 bytes of
+  // one of its rows per lane from two of them.  Staging both orientations in turn
+  // instead took a second pass of 2-byte LDS writes and two more barriers.
+  if (!need_c && !need_t) return;
   __syncthreads();  // every wave is done reading the operand stages
-  if (need_c) {
-    // row-major tile [BM][BN]: 2-byte writes, chunk c of row r at c ^ (r % kCChunks)
-    // (the two half-waves write rows 4 apart, which land on different 64-byte groups)
-    constexpr int kCChunks = C::BN / 8;
-    unsigned short* Cs = smem;
-#pragma unroll
-    for (int i = 0; i < C::WTM; ++i)
-#pragma unroll
-      for (int j = 0; j < C::WTN; ++j) {
-        if constexpr (kSwap) {
-          // row rl, columns cl0 .. cl0 + 3: one 8-byte write
-          const int rl = wm * (C::WTM * 32) + i * 32 + (lane & 31);
-#pragma unroll
-          for (int q = 0; q < 4; ++q) {
-            const int cl0 = wn * (C::WTN * 32) + j * 32 + 8 * q + 4 * fkh;
-            u32x2 packed;
-            packed[0] = static_cast<unsigned>(to16<kTy>(acc[i][j][q * 4 + 0])) |
-                        (static_cast<unsigned>(to16<kTy>(acc[i][j][q * 4 + 1])) << 16);
-            packed[1] = static_cast<unsigned>(to16<kTy>(acc[i][j][q * 4 + 2])) |
-                        (static_cast<unsigned>(to16<kTy>(acc[i][j][q * 4 + 3])) << 16);
-            *reinterpret_cast<u32x2*>(
-                Cs + rl * C::BN + ((((cl0 >> 3) ^ (rl % kCChunks)) << 3) | (cl0 & 7))) = packed;
-          }
-        } else {
-          const int jl = wn * (C::WTN * 32) + j * 32 + (lane & 31);
-#pragma unroll
-          for (int q = 0; q < 4; ++q)
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-              const int r = wm * (C::WTM * 32) + i * 32 + 8 * q + 4 * fkh + e;
-              Cs[r * C::BN + ((((jl >> 3) ^ (r % kCChunks)) << 3) | (jl & 7))] = to16<kTy>(acc[i][j][q * 4 + e]);
-            }
-        }
-      }
-    __syncthreads();
-    if constexpr (kEpi == kGram && C::BM == C::BN) {
-      if (args.symmetrize && ti == tj) {
-        // A B^T with A != B (a product of two commuting symmetric matrices) is symmetric
-        // only up to rounding; the off-diagonal tiles are mirrored whole, and a diagonal
-        // tile takes its upper triangle from its lower one, so the stored matrix is
-        // exactly symmetric (reads below the diagonal, writes above it: no overlap)
-        for (int idx = tid; idx < C::BM * C::BN; idx += C::kThreads) {
-          const int r = idx / C::BN, c = idx - r * C::BN;
-          if (c > r)
-            Cs[r * C::BN + ((((c >> 3) ^ (r % kCChunks)) << 3) | (c & 7))] =
-                Cs[c * C::BN + ((((r >> 3) ^ (c % kCChunks)) << 3) | (r & 7))];
-        }
-        __syncthreads();
-      }
-    }
-    unsigned short* Cp = args.C + batch * args.strideC;
-    constexpr int kAll = C::BM * kCChunks;
-    static_assert(kAll % C::kThreads == 0, "epilogue copy");
-#pragma unroll
-    for (int it = 0; it < kAll / C::kThreads; ++it) {
-      const int idx = tid + it * C::kThreads;
-      const int row = idx / kCChunks;
-      const int c = idx - row * kCChunks;
-      const u32x4 v = *reinterpret_cast<const u32x4*>(Cs + row * C::BN + ((c ^ (row % kCChunks)) * 8));
-      *reinterpret_cast<u32x4*>(Cp + (m0 + row) * args.ldc + n0 + c * 8) = v;
-    }
-    if (need_t) __syncthreads();  // the transposed tile reuses the buffer
-  }
-  if (!need_t) return;
-  // transposed tile [BN][BM]: a lane's 4 consecutive rows are one 8-byte write,
-  // chunk c of row j at tswz(c, j)
-  constexpr int kTChunks = C::BM / 8;
-  unsigned short* Ts = smem;
+  // staged tile: kSR rows of kSW elements; chunk c of row r at sphys(c, r)
+  constexpr int kSR = kSwap ? C::BM : C::BN;
+  constexpr int kSW = kSwap ? C::BN : C::BM;
+  constexpr int kSChunks = kSW / 8;
+  auto sphys = [](int c, int r) {
+    if constexpr (kSwap) return c ^ (r % kSChunks);
+    else return tswz<kSChunks>(c, r);
+  };
+  unsigned short* St = smem;
 #pragma unroll
   for (int i = 0; i < C::WTM; ++i)
 #pragma unroll
     for (int j = 0; j < C::WTN; ++j) {
-      if constexpr (kSwap) {
-        // row rl of the product is column rl of the transposed tile: 2-byte writes
-        const int rl = wm * (C::WTM * 32) + i * 32 + (lane & 31);
-#pragma unroll
-        for (int q = 0; q < 4; ++q)
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const int cl = wn * (C::WTN * 32) + j * 32 + 8 * q + 4 * fkh + e;
-            Ts[cl * C::BM + tswz<kTChunks>(rl >> 3, cl) * 8 + (rl & 7)] = to16<kTy>(acc[i][j][q * 4 + e]);
-          }
-        continue;
-      }
-      const int jl = wn * (C::WTN * 32) + j * 32 + (lane & 31);
+      // kSwap: row rl of the product, columns c0 .. c0 + 3; plain: column jl of the
+      // product (a row of the staged transpose), rows c0 .. c0 + 3
+      const int r = kSwap ? wm * (C::WTM * 32) + i * 32 + (lane & 31)
+                          : wn * (C::WTN * 32) + j * 32 + (lane & 31);
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
-        const int il0 = wm * (C::WTM * 32) + i * 32 + 8 * q + 4 * fkh;
+        const int c0 = kSwap ? wn * (C::WTN * 32) + j * 32 + 8 * q + 4 * fkh
+                             : wm * (C::WTM * 32) + i * 32 + 8 * q + 4 * fkh;
         u32x2 packed;
         packed[0] = static_cast<unsigned>(to16<kTy>(acc[i][j][q * 4 + 0])) |
                     (static_cast<unsigned>(to16<kTy>(acc[i][j][q * 4 + 1])) << 16);
         packed[1] = static_cast<unsigned>(to16<kTy>(acc[i][j][q * 4 + 2])) |
                     (static_cast<unsigned>(to16<kTy>(acc[i][j][q * 4 + 3])) << 16);
-        const int c = il0 >> 3, half = (il0 >> 2) & 1;
-        *reinterpret_cast<u32x2*>(Ts + jl * C::BM + tswz<kTChunks>(c, jl) * 8 + half * 4) = packed;
+        *reinterpret_cast<u32x2*>(St + r * kSW + sphys(c0 >> 3, r) * 8 + (c0 & 4)) = packed;
       }
     }
   __syncthreads();
-  unsigned short* C2 = args.C2 + batch * args.strideC2;
-  constexpr int kAll = C::BN * kTChunks;
-  static_assert(kAll % C::kThreads == 0, "epilogue copy");
+  if constexpr (kEpi == kGram && C::BM == C::BN && !kSwap) {
+    if (args.symmetrize && ti == tj) {
+      // A B^T with A != B (a product of two commuting symmetric matrices) is symmetric
+      // only up to rounding; the off-diagonal tiles are mirrored whole, and a diagonal
+      // tile takes its upper triangle from its lower one, so the stored matrix is
+      // exactly symmetric.  Staged transposed: C[o][x] is St[x][o], so for x > o
+      // St[x][o] takes St[o][x] (reads above the staged diagonal, writes below it).
+      for (int idx = tid; idx < C::BM * C::BN; idx += C::kThreads) {
+        const int x = idx / kSW, o = idx - x * kSW;
+        if (x > o)
+          St[x * kSW + sphys(o >> 3, x) * 8 + (o & 7)] = St[o * kSW + sphys(x >> 3, o) * 8 + (x & 7)];
+      }
+      __syncthreads();
+    }
+  }
+  // the orientation the staging holds: its rows, 16 bytes per lane
+  const bool direct = kSwap ? need_c : need_t;
+  if (direct) {
+    unsigned short* D = kSwap ? args.C + batch * args.strideC : args.C2 + batch * args.strideC2;
+    const int64_t ld = kSwap ? args.ldc : args.ldc2;
+    const int64_t r0 = kSwap ? m0 : n0, col0 = kSwap ? n0 : m0;
+    constexpr int kAll = kSR * kSChunks;
+    static_assert(kAll % C::kThreads == 0, "epilogue copy");
 #pragma unroll
-  for (int it = 0; it < kAll / C::kThreads; ++it) {
-    const int idx = tid + it * C::kThreads;
-    const int row = idx / kTChunks;  // local column j of the product
-    const int c = idx - row * kTChunks;
-    const u32x4 v = *reinterpret_cast<const u32x4*>(Ts + row * C::BM + tswz<kTChunks>(c, row) * 8);
-    *reinterpret_cast<u32x4*>(C2 + (n0 + row) * args.ldc2 + m0 + c * 8) = v;
+    for (int it = 0; it < kAll / C::kThreads; ++it) {
+      const int idx = tid + it * C::kThreads;
+      const int row = idx / kSChunks;
+      const int c = idx - row * kSChunks;
+      const u32x4 v = *reinterpret_cast<const u32x4*>(St + row * kSW + sphys(c, row) * 8);
+      *reinterpret_cast<u32x4*>(D + (r0 + row) * ld + col0 + c * 8) = v;
+    }
+  }
+  // the other orientation: out[o][x] = St[x][o], o < kSW, x < kSR.  A 16-lane group
+  // takes 4 rows o = 4 oq + b of it and 4 chunks x0 = 8 (4 xq + a) (lane 4 a + b) per
+  // pair of transposing reads: source lane 4 e + a addresses St[x0 + e][4 oq .. + 3]
+  // (then St[x0 + 4 + e]), and lane 4 a + b receives element b of those 4 lanes' runs,
+  // i.e. out[4 oq + b][x0 + e] (then x0 + 4 + e).
+  const bool other = kSwap ? need_t : need_c;
+  if (other) {
+    unsigned short* D = kSwap ? args.C2 + batch * args.strideC2 : args.C + batch * args.strideC;
+    const int64_t ld = kSwap ? args.ldc2 : args.ldc;
+    const int64_t r0 = kSwap ? n0 : m0, col0 = kSwap ? m0 : n0;
+    constexpr int kXQ = kSR / 32;          // chunk quads per output row
+    constexpr int kTasks = (kSW / 4) * kXQ;  // (row quad, chunk quad) per 16-lane group
+    constexpr int kGroups = C::kThreads / 16;
+    static_assert(kSR % 32 == 0 && kSW % 4 == 0 && kTasks % kGroups == 0, "transposed copy");
+    // as a source this lane is 4 e + a (e = gl >> 2, a = gl & 3); as a receiver it is
+    // 4 a + b (a = gl >> 2, b = gl & 3)
+    const int gl = lane & 15, ga = gl >> 2, gb = gl & 3;
+#pragma unroll
+    for (int it = 0; it < kTasks / kGroups; ++it) {
+      const int task = (tid >> 4) + it * kGroups;
+      const int oq = task / kXQ, xq = task - oq * kXQ;
+      const int ocol = 4 * oq;                   // the source runs: St[..][ocol .. + 3]
+      const int xs = 8 * (4 * xq + gb) + ga;     // this lane's source row, first read
+      const s16x4 lo = lds_read_tr(St + xs * kSW + sphys(ocol >> 3, xs) * 8 + (ocol & 4));
+      const s16x4 hi =
+          lds_read_tr(St + (xs + 4) * kSW + sphys(ocol >> 3, xs + 4) * 8 + (ocol & 4));
+      const s16x8 both = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+      // this lane's output: row 4 oq + gb, chunk 4 xq + ga
+      *reinterpret_cast<s16x8*>(D + (r0 + ocol + gb) * ld + col0 + 8 * (4 * xq + ga)) = both;
+    }
   }
 }
 
