@@ -326,10 +326,12 @@ __global__ __launch_bounds__(C::kThreads) void ns_gemm_kernel(GemmTable table) {
   // A combine that reads X (one orientation kept, row-major output every iteration but
   // the last of a transposed bucket) passes its operands to the MFMA the other way
   // round, so its accumulators hold the transposed layout: a lane keeps one row of the
-  // tile and runs of 4 columns, which leave for the row-major output as 8-byte LDS writes
-  // (the products are the same, summed over k in the same order).  Measured 0.8-1.5 %
-  // less Newton-Schulz time on the 12-, 20- and 24-layer workloads; the combine that
-  // keeps X^T writes both orientations every iteration and keeps the plain layout.
+  // tile and runs of 4 columns, so the epilogue stages the row-major tile and its
+  // output leaves straight from the staged rows, without transposing LDS reads (the
+  // products are the same, summed over k in the same order).  Measured 2-2.4 % less
+  // Newton-Schulz time on the 12-, 20- and 24-layer workloads than the plain layout;
+  // the combine that keeps X^T writes both orientations every iteration and keeps the
+  // plain layout.
   constexpr bool kSwap = (kEpi == kCombine) && C::kCombineReadsX;
   const int fkh = lane >> 5;   // which 8-wide half of a 16-wide k slice
 
