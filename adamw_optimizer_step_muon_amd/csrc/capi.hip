@@ -263,13 +263,13 @@ bool has_pipeline_choice(const Phase& ph, int prod, int tile) {
 }
 
 // A pinned configuration the phase can run: tile available (or 0), pipeline 0..2 (1, 2
-// only where has_pipeline_choice), band 0..64, spread -1..1, xcd 0..2.
+// only where has_pipeline_choice), band 0..64, spread -1..1, xcd 0..3.
 bool choice_valid(const Phase& ph, int prod, const GemmChoice& c) {
   if (c.tile != 0 && !tile_available(ph, prod, c.tile)) return false;
   if (c.pipeline < 0 || c.pipeline > 2) return false;
   if (c.pipeline != 0 && !has_pipeline_choice(ph, prod, c.tile)) return false;
   return c.band >= 0 && c.band <= 64 && c.spread >= -1 && c.spread <= 1 && c.xcd >= 0 &&
-         c.xcd <= 2;
+         c.xcd <= 3;
 }
 
 template <class T>
@@ -931,7 +931,7 @@ ma_status tune_impl(const ma_muon_bucket* buckets, int32_t n_buckets, const ma_m
           }
         // 5. block order across the XCDs
         const GemmChoice base4 = cur;
-        for (int x : {1, 2}) {
+        for (int x : {1, 2, 3}) {
           GemmChoice t = base4;
           t.xcd = x;
           const hipError_t e = consider(t);

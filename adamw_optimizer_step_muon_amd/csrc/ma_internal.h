@@ -157,7 +157,7 @@ struct GemmArgs {
   int tiles_per_batch;
   int tiles_k;          // matrices in the group (host side: block count = tiles_k x tiles_per_batch)
   int band;             // tile rows per L2 band (tile order; 0: plain row-major triangle)
-  int xcd_remap;        // 1: renumber blocks XCD by XCD
+  int xcd_remap;        // block order across the XCDs (XcdOrder)
   int spread;           // 1: spread the next stage's DMAs over the first half-stage
   int symmetrize;       // gram with A != B: copy each diagonal tile's lower triangle up
   float post;           // gram / combine: constant factor on the result (0: none)
@@ -173,7 +173,27 @@ struct GemmTable {
 static_assert(sizeof(GemmTable) <= 2048, "GemmTable is passed whole as the kernel argument");
 static_assert(offsetof(GemmTable, g) == 0, "the kernel reads the table at the segment start");
 
-// Block id -> logical id so that each XCD's blocks (bid % 8) are a contiguous run.
+// Block order across the 8 XCDs (blocks go to them round-robin: bid % 8).
+//   kXcdRoundRobin: logical id = block id;
+//   kXcdRuns: each XCD takes a contiguous run of the logical ids, so the blocks one XCD
+//     runs together are neighbouring tiles whose operand panels its L2 serves;
+//   kXcdShared: the XCDs share each matrix: XCD x takes the x-th eighth of every
+//     matrix's tiles (in the band order), matrix after matrix, so at any time all eight
+//     work on the same matrix and the panels one XCD's L2 misses are likely in the
+//     memory-side cache (MALL) from another's.  For matrices of many tiles (the
+//     8192-wide Gram sides: 528 triangle tiles, 3584 combine tiles) that measured 5 %
+//     less Newton-Schulz time than kXcdRuns; for matrices of a few dozen tiles, where
+//     one XCD's run covers whole matrices, 5-7 % more.  A group then takes
+//     8 * K * ceil(tiles_per_batch / 8) blocks (XCDs with one tile fewer per matrix
+//     get padding blocks).
+enum XcdOrder { kXcdRoundRobin = 0, kXcdRuns = 1, kXcdShared = 2 };
+
+// blocks a group of K matrices of `tpb` tiles takes in the grid (a multiple of 8)
+__host__ __device__ __forceinline__ int gemm_group_blocks(int tpb, int K, int xcd_order) {
+  return xcd_order == kXcdShared ? 8 * K * ((tpb + 7) / 8) : (tpb * K + 7) & ~7;
+}
+
+// kXcdRuns: block id -> logical id so that each XCD's blocks are a contiguous run.
 __host__ __device__ __forceinline__ int xcd_linear(int bid, int nblocks) {
   constexpr int kXcd = 8;
   const int q = nblocks / kXcd, r = nblocks % kXcd;
@@ -186,7 +206,8 @@ __host__ __device__ __forceinline__ int xcd_linear(int bid, int nblocks) {
 // on multiples of 8 blocks, so a group's blocks keep the round-robin XCD pattern; inside
 // a group the blocks are renumbered so each XCD owns a contiguous run of tiles, in bands
 // of `band` row panels (the combine: column by column inside a band; the symmetric
-// products: the lower triangle band by band).  Used by the kernel and by the host-side
+// products: the lower triangle band by band); or, kXcdShared, each matrix's run is
+// split among the eight XCDs.  Used by the kernel and by the host-side
 // plan check, which enumerates every block of every launch.
 __host__ __device__ __forceinline__ bool gemm_block_tile(const GemmTable& t, int epi, int bid,
                                                          int& gi, int64_t& batch, int& ti,
@@ -199,8 +220,21 @@ __host__ __device__ __forceinline__ bool gemm_block_tile(const GemmTable& t, int
   const int g0 = t.start[gi];
   const int gcount = args.tiles_per_batch * args.tiles_k;
   const int raw = bid - g0;
-  const int lid = args.xcd_remap ? xcd_linear(raw, (gcount + 7) & ~7) : raw;
-  if (lid >= gcount) return false;
+  int lid;
+  if (args.xcd_remap == kXcdShared) {
+    // XCD x: tiles [x q + min(x, r), ... + per) of matrix 0, then of matrix 1, ...
+    const int tpb = args.tiles_per_batch;
+    const int q = tpb / 8, r = tpb % 8;
+    const int x = raw % 8, local = raw / 8;
+    const int per = q + (x < r ? 1 : 0);
+    if (per == 0) return false;
+    const int b = local / per;
+    if (b >= args.tiles_k) return false;
+    lid = b * tpb + x * q + (x < r ? x : r) + (local - b * per);
+  } else {
+    lid = args.xcd_remap == kXcdRuns ? xcd_linear(raw, (gcount + 7) & ~7) : raw;
+    if (lid >= gcount) return false;
+  }
   batch = lid / args.tiles_per_batch;
   const int tile = lid - static_cast<int>(batch) * args.tiles_per_batch;
   if (epi == kCombine) {
@@ -266,7 +300,8 @@ struct GemmChoice {
   int pipeline = 0;  // 256-tiles of the Gram, polynomial and X^T-reading combine:
                      // 1 = stages of k = 64 in a 3 + 2 ring, 2 = 4 stages of k = 32
                      // (default 1)
-  int xcd = 0;       // 1 = blocks renumbered XCD by XCD, 2 = round-robin order (default 1)
+  int xcd = 0;       // 1 = contiguous runs per XCD, 2 = round-robin order, 3 = matrices
+                     // shared by the XCDs (default: 3 for matrices of >= 512 tiles, else 1)
   bool operator==(const GemmChoice& o) const {
     return tile == o.tile && band == o.band && spread == o.spread && pipeline == o.pipeline &&
            xcd == o.xcd;

@@ -752,15 +752,17 @@ int env_int(const char* name, int dflt) {
 // Fill the tile-grid and tile-order fields of one group's arguments (bm x bn tiles).
 void set_tiles(int epi, GemmArgs& a, const BucketPlan& p, int bm, int bn, const GemmChoice& ch) {
   // Defaults measured on the MI355X (env knobs for tuning, a tuned choice above both):
-  // bands of 4 row panels for both tile orders, XCD renumbering on, spread DMA issue
-  // for 256-tiles only.
+  // bands of 4 row panels for both tile orders; the eight XCDs sharing each matrix
+  // when it has at least kSharedMinTiles tiles (each XCD's share then spans two rounds
+  // of the blocks it runs at once), else contiguous runs per XCD; spread DMA issue for
+  // 256-tiles only.
+  constexpr int kSharedMinTiles = 512;
   static const int band_combine = env_int("MA_NS_BAND_COMBINE", 4);
   static const int band_tri = env_int("MA_NS_BAND_TRI", 4);
-  static const int xcd = env_int("MA_NS_XCD", 1);
+  static const int xcd = env_int("MA_NS_XCD", -1);  // XcdOrder, -1: the rule
   static const int spread = env_int("MA_NS_SPREAD", -1);
   if (ch.band > 0) a.band = ch.band;
   else a.band = epi == kCombine ? (band_combine > 0 ? band_combine : 1) : band_tri;
-  a.xcd_remap = ch.xcd == 1 ? 1 : ch.xcd == 2 ? 0 : xcd;
   if (bm < 192) a.spread = 0;  // measured slower on 128-tiles
   else if (ch.spread >= 0) a.spread = ch.spread ? 1 : 0;
   else a.spread = spread >= 0 ? spread : 1;
@@ -772,6 +774,12 @@ void set_tiles(int epi, GemmArgs& a, const BucketPlan& p, int bm, int bn, const 
     a.tiles_m = a.tiles_n = static_cast<int>(p.m_pad / bm);
     a.tiles_per_batch = a.tiles_m * (a.tiles_m + 1) / 2;
   }
+  // configuration value (1 runs, 2 round-robin, 3 shared) -> XcdOrder
+  if (ch.xcd == 1) a.xcd_remap = kXcdRuns;
+  else if (ch.xcd == 2) a.xcd_remap = kXcdRoundRobin;
+  else if (ch.xcd == 3) a.xcd_remap = kXcdShared;
+  else if (xcd >= kXcdRoundRobin && xcd <= kXcdShared) a.xcd_remap = xcd;
+  else a.xcd_remap = a.tiles_per_batch >= kSharedMinTiles ? kXcdShared : kXcdRuns;
 }
 
 // 256-tile kernel of the Gram-side products and of the X^T-reading combine: the 4-stage
@@ -806,7 +814,8 @@ hipError_t launch_table(int epi, GemmTable& t, TileCfg cfg, int pipeline, int ty
     }
   t.start[0] = 0;
   for (int i = 0; i < t.ngroups; ++i)
-    t.start[i + 1] = t.start[i] + ((t.g[i].tiles_per_batch * t.g[i].tiles_k + 7) & ~7);
+    t.start[i + 1] =
+        t.start[i] + gemm_group_blocks(t.g[i].tiles_per_batch, t.g[i].tiles_k, t.g[i].xcd_remap);
   for (int i = t.ngroups + 1; i <= kMaxGemmGroups; ++i) t.start[i] = t.start[t.ngroups];
   if (LaunchRecorder* r = launch_recorder()) {
     r->gemm(epi, shape_of(cfg, pipeline), t);

@@ -295,12 +295,15 @@ typedef struct {
                         stages, 2 = four stages of k = 32; 0: 1 */
   int32_t xcd;       /* block order across the 8 XCDs: 1 = each XCD takes a contiguous run
                         of tiles (so its L2 serves neighbouring tiles), 2 = the hardware's
-                        round-robin order; 0: 1 */
+                        round-robin order, 3 = the XCDs share each matrix (XCD x takes the
+                        x-th eighth of every matrix's tiles, so the operand panels one
+                        XCD misses in its L2 are likely in the memory-side cache from
+                        another); 0: 3 for matrices of at least 512 tiles, else 1 */
 } ma_gemm_config;
 
 /* ma_muon_tune over whole configurations.  reps > 0: for each product of each phase,
  * search one dimension at a time from the defaults -- tile, then pipeline (where the
- * tile has a choice), then band width (2, 4, 8), then spreading, then the XCD order --
+ * tile has a choice), then band width (2, 4, 8), then spreading, then the XCD order (1, 2, 3) --
  * timing each candidate
  * as ma_muon_tune does; a candidate replaces the kept one only when at least 3 % faster.
  * The result is reported in configs (host, 3 entries per phase: Gram, polynomial,

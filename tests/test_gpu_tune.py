@@ -128,7 +128,7 @@ def test_searched_configurations_keep_results(case):
 
 
 @pytest.mark.parametrize("config", [{"tile": 256, "pipeline": 2}, {"band": 2}, {"band": 8},
-                                    {"spread": 0}, {"xcd": 2}])
+                                    {"spread": 0}, {"xcd": 1}, {"xcd": 2}, {"xcd": 3}])
 def test_pinned_configurations_are_bitwise_identical(config):
     """Each dimension pinned on its own for every product that accepts it (the 4096-wide
     phase keeps X^T, so its combine has a pipeline choice too)."""
@@ -157,7 +157,8 @@ def _step_gs(state, ws):
 
 
 @pytest.mark.parametrize("config", [{"tile": 128}, {"tile": 256, "pipeline": 2},
-                                    {"band": 2}, {"band": 8}, {"spread": 0}, {"xcd": 2}])
+                                    {"band": 2}, {"band": 8}, {"spread": 0}, {"xcd": 2},
+                                    {"xcd": 3}])
 def test_gram_space_configurations_are_bitwise_identical(config):
     """The fp16 Gram-space launches under each pinned configuration (the fp16 kernels run
     the default pipeline, so a pinned second pipeline runs as the default) and under the
@@ -218,5 +219,26 @@ def test_repeated_gram_space_steps_are_bitwise_identical(config):
         ref = _step_gs(state, ws)
         for rep in range(2):
             assert _same(_step_gs(state, ws), ref), (config, rep)
+    finally:
+        ma.muon_tune_reset()
+
+
+@pytest.mark.parametrize("case", ["gpt12", "gpt20", "promoted"])
+def test_shared_xcd_order_is_bitwise_identical(case):
+    """Every product pinned to the order in which the eight XCDs share each matrix (the
+    default only for matrices of at least 512 tiles), on phases whose per-matrix tile
+    counts are not multiples of 8, so some XCDs run padding blocks: bitwise the default's
+    result, and within tolerance of the oracle."""
+    shapes = CASES[case]
+    state = _state(shapes, 14)
+    ws = torch.empty(ma.muon_workspace_bytes(shapes), dtype=torch.uint8, device="cuda")
+    ma.muon_tune_reset()
+    try:
+        ref = _step(state, ws)
+        shared = {"xcd": 3}
+        ma.muon_tune_configs(shapes, reps=0, configs=[[shared, shared, shared]])
+        got = _step(state, ws)
+        assert _same(got, ref)
+        assert max(_oracle_errors(state[:1], got[:1])) <= MUON_RTOL
     finally:
         ma.muon_tune_reset()

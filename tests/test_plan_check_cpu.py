@@ -131,6 +131,7 @@ CONFIGS = [
     {"tile": 256, "pipeline": 2}, {"tile": 256, "pipeline": 1, "band": 2},
     {"tile": 256, "band": 8, "spread": 0}, {"tile": 128, "band": 1}, {"band": 16},
     {"spread": 1}, {"tile": 192, "band": 3, "spread": 0}, {"xcd": 2}, {"xcd": 1, "band": 2},
+    {"xcd": 3}, {"xcd": 3, "band": 2, "tile": 128},
 ]
 
 
@@ -162,7 +163,7 @@ def test_workload_plans_under_pinned_configurations(index):
 def test_configuration_pins_are_validated():
     shapes = [(48, 768, 768), (12, 768, 3072), (12, 3072, 768)]
     bad = [{"tile": 128, "pipeline": 2}, {"pipeline": 3}, {"band": 65}, {"spread": 2},
-           {"tile": 512}, {"xcd": 3}]
+           {"tile": 512}, {"xcd": 4}, {"xcd": -1}]
     for c in bad:
         with pytest.raises(_lib.MuonAdamWError):
             ma.muon_tune_configs(shapes, reps=0, configs=[[c, {}, {}]])
