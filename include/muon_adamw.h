@@ -287,7 +287,8 @@ ma_status ma_muon_tune(const ma_muon_bucket* buckets, int32_t n_buckets,
 typedef struct {
   int32_t tile;      /* 128 or 256 (on a 256-padded phase); 192 (combine, Gram sides padded
                         to a multiple of 192); 0: the phase's rule */
-  int32_t band;      /* row panels per L2 band of the tile order, 1..64; 0: 4 */
+  int32_t band;      /* row panels per L2 band of the tile order, 1..64; 0: 4 (8 for a
+                        combine whose matrices the XCDs share, xcd 3) */
   int32_t spread;    /* 256- and 192-tiles: 1 spreads the next stage's operand loads over
                         half a stage, 0 issues them at once; -1: 1 */
   int32_t pipeline;  /* 256-tiles of the Gram, the polynomial and the combine of a phase
