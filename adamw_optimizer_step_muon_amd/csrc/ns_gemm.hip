@@ -34,9 +34,11 @@
 //     distinct banks;
 //     the swizzle is applied on the global side, since LDS-DMA writes each wave's
 //     64 chunks contiguously;
-//   * blocks are renumbered so each XCD (blocks go round-robin to the 8 XCDs) works
-//     on a contiguous run of tiles, and those runs are grouped by row panels, so
-//     the blocks resident on one XCD share operand panels in its L2;
+//   * blocks are renumbered (they go round-robin to the 8 XCDs): for matrices of a
+//     few hundred tiles or fewer each XCD works on a contiguous run of tiles, grouped
+//     by row panels, so the blocks resident on one XCD share operand panels in its L2;
+//     larger matrices are shared by the eight XCDs, so the panels one XCD's L2 misses
+//     are likely in the memory-side cache from another;
 //   * epilogue: b/c terms (and a on the diagonal) or the first iteration's
 //     normalisation in fp32 in registers, round to bf16; the tile is staged once in an
 //     XOR-swizzled LDS tile and both orientations (row-major, and the transposed /
