@@ -119,9 +119,12 @@ print("ok")
 
 @pytest.mark.parametrize("env", [{"MA_NS_TILE": "128"}, {"MA_NS_TILE": "256"}, {"MA_NS_BIG": "1"},
                                  {"MA_NS_BAND_COMBINE": "3", "MA_NS_BAND_TRI": "0"},
-                                 {"MA_NS_XCD": "0", "MA_NS_BAND_TRI": "7"}])
+                                 {"MA_NS_XCD": "0", "MA_NS_BAND_TRI": "7"},
+                                 {"MA_NS_XCD": "1"}, {"MA_NS_XCD": "2", "MA_NS_BAND_COMBINE": "5"}])
 def test_environment_tile_overrides(env):
-    """The tuning overrides are read once per process: each runs in a child process."""
+    """The tuning overrides are read once per process: each runs in a child process
+    (MA_NS_XCD 2 puts every launch, of any tile count, in the order where the XCDs share
+    each matrix)."""
     r = subprocess.run([sys.executable, "-c", _ENV_SCRIPT], cwd=ROOT, capture_output=True,
                        text=True, env={**os.environ, **env}, timeout=120)
     assert r.returncode == 0 and r.stdout.strip().endswith("ok"), r.stderr[-2000:]
