@@ -106,6 +106,10 @@ def parse():
     ap.add_argument("--comparator", action="store_true",
                     help="also time the same Newton-Schulz chain as torch bf16 batched GEMMs "
                          "(hipBLASLt) on the workload's gradients, after the measurement")
+    ap.add_argument("--zero-operands", action="store_true",
+                    help="also time the Newton-Schulz launches on zero gradients: operands "
+                         "that do not toggle take the power limit out, so the rate shows "
+                         "what the kernels' structure allows at the full clock")
     return ap.parse_args()
 
 
@@ -564,6 +568,15 @@ def main():
         out["calibration_copy_bytes"] = nbytes
     if args.ns_mode == 0 and not args.no_alt_route and any(gram_space(b, 1) for b in wl.muon):
         out["gram_space_route"] = alt_route(wl, buckets, state, adamw, stream, dev, args)
+    if args.zero_operands:
+        zeros = [torch.zeros_like(b[1]) for b in buckets]
+        zphase = ma.muon_ns_time(zeros, reps=reps, ns_steps=mh.ns_steps, ns_eps=mh.ns_eps,
+                                 ns_mode=args.ns_mode, workspace=ws, stream=stream)
+        del zeros
+        zms = sum(zphase)
+        out["zero_operands"] = {"ns_ms": round(zms, 4), "ns_tflops": round(flops / (zms * 1e-3) / 1e12, 1),
+                                "ns_mfma_frac": round(flops / (zms * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4),
+                                "ns_phase_ms": [round(x, 4) for x in zphase]}
     if args.comparator:
         comp = blas_comparator([b[1] for b in buckets], mh.coeffs, mh.ns_steps, stream)
         comp["speedup_of_this_library"] = round(comp["ns_ms"] / ns_ms, 3)
