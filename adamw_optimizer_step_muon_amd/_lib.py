@@ -355,12 +355,12 @@ def muon_tune_configs(shapes: Sequence[Sequence[int]], *, reps: int = 3, configs
                       workspace=None, stream=None, device=None, ns_mode: int = 0, grads=None):
     """Per-shape Newton-Schulz GEMM configurations (ma_muon_tune_configs) for buckets of
     these (K, A, B) shapes.  reps > 0: search tile, pipeline, band width, spreading and
-    XCD order on
-    the workspace (scratch; allocated for the call when None) and keep the fastest;
-    reps == 0: pin `configs` (per phase, three dicts with keys tile, band, spread,
-    pipeline, xcd; missing keys take their defaults).  grads: the buckets' (K, A, B) gradients,
-    cast into the workspace before the timing so the candidates run on real operands.
-    Returns the configurations in force."""
+    XCD order on the workspace (scratch; allocated for the call when None) and keep the
+    fastest; reps == 0: pin `configs` (per phase, three dicts with keys tile, band,
+    spread, pipeline, xcd; missing keys take their defaults; xcd 1 = a contiguous run of
+    tiles per XCD, 2 = round-robin, 3 = the XCDs share each matrix).  grads: the buckets'
+    (K, A, B) gradients, cast into the workspace before the timing so the candidates run
+    on real operands.  Returns the configurations in force."""
     import torch
 
     n = len(shapes)
