@@ -104,6 +104,30 @@ def test_random_shapes():
             ma.muon_check_plan(shapes, ns_mode=ns_mode, ns_steps=int(rng.integers(0, 4)))
 
 
+_SHARED_SCRIPT = """
+import numpy as np
+import adamw_optimizer_step_muon_amd as ma
+rng = np.random.default_rng(11)
+for _ in range(80):
+    n = int(rng.integers(1, 5))
+    shapes = [(int(rng.integers(1, 12)), int(rng.integers(1, 2600)), int(rng.integers(1, 2600)))
+              for _ in range(n)]
+    for mode in (0, 1):
+        ma.muon_check_plan(shapes, ns_mode=mode, ns_steps=int(rng.integers(1, 3)))
+print("ok")
+"""
+
+
+def test_random_shapes_under_the_shared_xcd_order():
+    """Random bucket lists with every launch in the order where the eight XCDs share
+    each matrix (MA_NS_XCD 2; by default only matrices of 512 tiles or more take it):
+    tile counts per matrix that are not multiples of 8, and batches that do not fill the
+    last round, each output tile still computed by exactly one block."""
+    r = subprocess.run([sys.executable, "-c", _SHARED_SCRIPT], cwd=ROOT, capture_output=True,
+                       text=True, env={**os.environ, "MA_NS_XCD": "2"}, timeout=300)
+    assert r.returncode == 0 and r.stdout.strip().endswith("ok"), r.stderr[-2000:]
+
+
 _ENV_SCRIPT = """
 import sys, workloads
 import adamw_optimizer_step_muon_amd as ma
