@@ -7,7 +7,8 @@ block must stay inside the buffer its argument addresses, with each output tile 
 launch computed exactly once.  Covered: the five workloads' bucket lists in both
 iteration modes, every tile a phase can be pinned to, the environment tile overrides,
 and a spread of ragged shapes.  A CPU mutation check (a wrong row stride, overlapping
-workspace offsets) showed the check fails on such mistakes.
+workspace offsets, a wrong block offset in the shared XCD order) showed the check fails
+on such mistakes.
 """
 import itertools
 import os
